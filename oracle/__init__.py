@@ -1,0 +1,164 @@
+"""fp64 CPU oracle for exact scaled-dot-product attention (forward + backward).
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the
+bench's CPU-baseline leg, never by the GPU library or its Python binding.
+
+The arithmetic lives in attn_oracle.c (plain C, double precision, sequential
+sums); this module only marshals numpy arrays through ctypes.  Definitions
+follow the FlashAttention-4 pages: the three per-tile phases in "The
+Asymmetric Hardware Scaling Wall" (S = QK^T/sqrt(d), P = exp(S - m)/l,
+O = PV) and the simulator's validation harness, which equates the tiled result
+with softmax(QK^T * scale) V; the causal mask keeps key j for query i iff
+j <= i (the simulator's in-tile causal mask).  The backward is the analytic
+gradient of that definition (the pages give no backward formulas).
+
+Inputs are bf16 bit patterns held in numpy uint16 arrays, laid out
+[B, H, N, d].  Outputs are float64.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        from . import build as _b
+        _b.build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    u16p = ctypes.POINTER(ctypes.c_uint16)
+    f64p = ctypes.POINTER(ctypes.c_double)
+    i64p = ctypes.POINTER(ctypes.c_int64)
+    c_int, c_float, c_i64 = ctypes.c_int, ctypes.c_float, ctypes.c_int64
+    lib.oracle_fwd_rows.argtypes = [u16p, u16p, u16p, c_int, c_int, c_int, c_int, c_int,
+                                    c_float, c_int, i64p, c_i64, f64p, f64p, c_int]
+    lib.oracle_fwd_rows.restype = c_int
+    lib.oracle_fwd.argtypes = [u16p, u16p, u16p, f64p, f64p, c_int, c_int, c_int, c_int,
+                               c_int, c_float, c_int, c_int]
+    lib.oracle_fwd.restype = c_int
+    lib.oracle_bwd_groups.argtypes = [u16p, u16p, u16p, u16p, c_int, c_int, c_int, c_int,
+                                      c_int, c_float, c_int, i64p, c_i64, f64p, f64p, f64p,
+                                      f64p, f64p, c_int]
+    lib.oracle_bwd_groups.restype = c_int
+    _lib = lib
+    return lib
+
+
+def default_threads() -> int:
+    """Threads the oracle uses: the cores this process may run on (capped by
+    OMP_NUM_THREADS when that is set)."""
+    n = len(os.sched_getaffinity(0))
+    env = os.environ.get("OMP_NUM_THREADS")
+    if env and env.isdigit() and int(env) > 0:
+        n = min(n, int(env))
+    return max(1, n)
+
+
+def _u16(a, name):
+    a = np.ascontiguousarray(a)
+    if a.dtype != np.uint16:
+        raise TypeError(f"{name} must hold bf16 bit patterns as uint16, got {a.dtype}")
+    return a
+
+
+def _ptr(a, ctype):
+    return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+def _shape(q, k, v):
+    if q.ndim != 4 or k.ndim != 4 or v.ndim != 4:
+        raise ValueError("q, k, v must be [B, H, N, d]")
+    B, Hq, N, d = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[2] != N or k.shape[3] != d:
+        raise ValueError(f"shape mismatch q{q.shape} k{k.shape} v{v.shape}")
+    Hkv = k.shape[1]
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    return B, Hq, Hkv, N, d
+
+
+def fwd(q, k, v, scale, causal, threads=None):
+    """Exact attention forward.  Returns (O [B,Hq,N,d] f64, LSE [B,Hq,N] f64)."""
+    lib = _load()
+    q, k, v = _u16(q, "q"), _u16(k, "k"), _u16(v, "v")
+    B, Hq, Hkv, N, d = _shape(q, k, v)
+    o = np.empty((B, Hq, N, d), np.float64)
+    lse = np.empty((B, Hq, N), np.float64)
+    st = lib.oracle_fwd(_ptr(q, ctypes.c_uint16), _ptr(k, ctypes.c_uint16),
+                        _ptr(v, ctypes.c_uint16), _ptr(o, ctypes.c_double),
+                        _ptr(lse, ctypes.c_double), B, Hq, Hkv, N, d, float(scale),
+                        int(bool(causal)), threads or default_threads())
+    if st:
+        raise RuntimeError(f"oracle_fwd failed with status {st}")
+    return o, lse
+
+
+def fwd_rows(q, k, v, scale, causal, rows, threads=None):
+    """Forward for selected query rows.  rows: flat indices (b*Hq + h)*N + i.
+    Returns (O [n, d] f64, LSE [n] f64)."""
+    lib = _load()
+    q, k, v = _u16(q, "q"), _u16(k, "k"), _u16(v, "v")
+    B, Hq, Hkv, N, d = _shape(q, k, v)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    o = np.empty((rows.size, d), np.float64)
+    lse = np.empty((rows.size,), np.float64)
+    st = lib.oracle_fwd_rows(_ptr(q, ctypes.c_uint16), _ptr(k, ctypes.c_uint16),
+                             _ptr(v, ctypes.c_uint16), B, Hq, Hkv, N, d, float(scale),
+                             int(bool(causal)), _ptr(rows, ctypes.c_int64), rows.size,
+                             _ptr(o, ctypes.c_double), _ptr(lse, ctypes.c_double),
+                             threads or default_threads())
+    if st:
+        raise RuntimeError(f"oracle_fwd_rows failed with status {st}")
+    return o, lse
+
+
+def bwd_groups(q, k, v, dout, scale, causal, groups, threads=None):
+    """Backward for selected key/value groups (flat index b*Hkv + g).
+
+    Returns dict with dq [G, Hq/Hkv, N, d], dk [G, N, d], dv [G, N, d],
+    o [G, Hq/Hkv, N, d], lse [G, Hq/Hkv, N], all float64."""
+    lib = _load()
+    q, k, v, dout = _u16(q, "q"), _u16(k, "k"), _u16(v, "v"), _u16(dout, "dout")
+    B, Hq, Hkv, N, d = _shape(q, k, v)
+    if dout.shape != q.shape:
+        raise ValueError("dout must have q's shape")
+    groups = np.ascontiguousarray(groups, dtype=np.int64)
+    G, grp = groups.size, Hq // Hkv
+    out = {
+        "dq": np.empty((G, grp, N, d), np.float64),
+        "dk": np.empty((G, N, d), np.float64),
+        "dv": np.empty((G, N, d), np.float64),
+        "o": np.empty((G, grp, N, d), np.float64),
+        "lse": np.empty((G, grp, N), np.float64),
+    }
+    st = lib.oracle_bwd_groups(
+        _ptr(q, ctypes.c_uint16), _ptr(k, ctypes.c_uint16), _ptr(v, ctypes.c_uint16),
+        _ptr(dout, ctypes.c_uint16), B, Hq, Hkv, N, d, float(scale), int(bool(causal)),
+        _ptr(groups, ctypes.c_int64), G, _ptr(out["dq"], ctypes.c_double),
+        _ptr(out["dk"], ctypes.c_double), _ptr(out["dv"], ctypes.c_double),
+        _ptr(out["o"], ctypes.c_double), _ptr(out["lse"], ctypes.c_double),
+        threads or default_threads())
+    if st:
+        raise RuntimeError(f"oracle_bwd_groups failed with status {st}")
+    return out
+
+
+def bwd(q, k, v, dout, scale, causal, threads=None):
+    """Whole backward.  Returns dict dq [B,Hq,N,d], dk/dv [B,Hkv,N,d], o, lse."""
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    r = bwd_groups(q, k, v, dout, scale, causal, np.arange(B * Hkv), threads)
+    return {
+        "dq": r["dq"].reshape(B, Hq, N, d),
+        "dk": r["dk"].reshape(B, Hkv, N, d),
+        "dv": r["dv"].reshape(B, Hkv, N, d),
+        "o": r["o"].reshape(B, Hq, N, d),
+        "lse": r["lse"].reshape(B, Hq, N),
+    }

@@ -1,0 +1,371 @@
+"""Pins for the fp64 CPU oracle (no GPU).
+
+The oracle (oracle/attn_oracle.c) is pinned to things other than itself:
+  * brute force in pure Python (math.fsum / math.exp) on tiny inputs;
+  * torch's own scaled_dot_product_attention, logsumexp and autograd in
+    float64 on the CPU (independent library routines);
+  * closed forms (zero keys, a single key, the first causal row, a hand-worked
+    example in tests/golden/);
+  * invariants (probability rows sum to one and follow exp-score ratios,
+    constant V, key permutation, LSE bounds, per-row score shift);
+  * central finite differences on a bf16-exact grid for the gradients, and the
+    exact gradient identities sum_j dK_j = 0 and sum_j dV_j = sum_i dO_i.
+A plausible slip in the oracle (dropped term, wrong sign, wrong index,
+transposed operand, wrong mask edge, wrong GQA mapping) fails at least one.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth import bf16_bits_to_f32, f32_to_bf16_bits, random_bf16
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def f64(bits):
+    return bf16_bits_to_f32(bits).astype(np.float64)
+
+
+# ---------------------------------------------------------------- brute force
+
+def brute_fwd(q, k, v, scale, causal):
+    """Pure-Python attention, one row at a time, math.fsum sums."""
+    qf, kf, vf = f64(q), f64(k), f64(v)
+    B, Hq, N, d = qf.shape
+    grp = Hq // kf.shape[1]
+    o = np.zeros((B, Hq, N, d))
+    lse = np.zeros((B, Hq, N))
+    sc = float(np.float32(scale))
+    for b in range(B):
+        for h in range(Hq):
+            g = h // grp
+            for i in range(N):
+                keys = range(i + 1) if causal else range(N)
+                s = [sc * math.fsum(qf[b, h, i, c] * kf[b, g, j, c] for c in range(d)) for j in keys]
+                m = max(s)
+                p = [math.exp(x - m) for x in s]
+                l = math.fsum(p)
+                for c in range(d):
+                    o[b, h, i, c] = math.fsum(p[t] * vf[b, g, j, c] for t, j in enumerate(keys)) / l
+                lse[b, h, i] = m + math.log(l)
+    return o, lse
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("B,Hq,Hkv,N,d", [(1, 1, 1, 1, 1), (1, 1, 1, 5, 3), (1, 2, 2, 7, 8),
+                                          (1, 2, 1, 9, 4), (2, 4, 2, 6, 5)])
+def test_fwd_brute_force(B, Hq, Hkv, N, d, causal):
+    q = random_bf16((B, Hq, N, d), 1)
+    k = random_bf16((B, Hkv, N, d), 2)
+    v = random_bf16((B, Hkv, N, d), 3)
+    scale = 1.0 / math.sqrt(d)
+    o, lse = oracle.fwd(q, k, v, scale, causal)
+    o_ref, lse_ref = brute_fwd(q, k, v, scale, causal)
+    np.testing.assert_allclose(o, o_ref, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lse, lse_ref, rtol=1e-12, atol=1e-13)
+
+
+# ------------------------------------------------------- torch library routine
+
+def torch_fwd(q, k, v, scale, causal):
+    qt, kt, vt = (torch.from_numpy(f64(x)) for x in (q, k, v))
+    grp = qt.shape[1] // kt.shape[1]
+    kt = kt.repeat_interleave(grp, dim=1)
+    vt = vt.repeat_interleave(grp, dim=1)
+    sc = float(np.float32(scale))
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=causal, scale=sc)
+    s = (qt @ kt.transpose(-1, -2)) * sc
+    if causal:
+        n = s.shape[-1]
+        s = s.masked_fill(torch.ones(n, n, dtype=torch.bool).triu(1), float("-inf"))
+    return o.numpy(), torch.logsumexp(s, dim=-1).numpy()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("B,Hq,Hkv,N,d", [(1, 2, 2, 64, 64), (2, 4, 1, 37, 32), (1, 8, 2, 130, 16)])
+def test_fwd_vs_torch_sdpa(B, Hq, Hkv, N, d, causal):
+    q = random_bf16((B, Hq, N, d), 11)
+    k = random_bf16((B, Hkv, N, d), 12)
+    v = random_bf16((B, Hkv, N, d), 13)
+    scale = 1.0 / math.sqrt(d)
+    o, lse = oracle.fwd(q, k, v, scale, causal)
+    o_ref, lse_ref = torch_fwd(q, k, v, scale, causal)
+    np.testing.assert_allclose(o, o_ref, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(lse, lse_ref, rtol=1e-11, atol=1e-12)
+
+
+def test_fwd_rows_matches_full():
+    B, Hq, Hkv, N, d = 2, 4, 2, 33, 16
+    q, k, v = random_bf16((B, Hq, N, d), 5), random_bf16((B, Hkv, N, d), 6), random_bf16((B, Hkv, N, d), 7)
+    for causal in (False, True):
+        o, lse = oracle.fwd(q, k, v, 0.25, causal)
+        rows = np.array([0, 5, 32, 33 * 4 + 7, B * Hq * N - 1])
+        o_r, lse_r = oracle.fwd_rows(q, k, v, 0.25, causal, rows)
+        np.testing.assert_array_equal(o_r, o.reshape(-1, d)[rows])
+        np.testing.assert_array_equal(lse_r, lse.reshape(-1)[rows])
+
+
+# ----------------------------------------------------------------- closed forms
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_zero_keys_give_running_mean(causal):
+    """K = 0: every valid score is 0, so O_i is the mean of the valid V rows and
+    LSE_i = ln(n_i) with n_i = i + 1 (causal) or N."""
+    B, Hq, Hkv, N, d = 1, 2, 1, 12, 8
+    q = random_bf16((B, Hq, N, d), 21)
+    k = np.zeros((B, Hkv, N, d), np.uint16)
+    v = random_bf16((B, Hkv, N, d), 22)
+    o, lse = oracle.fwd(q, k, v, 0.5, causal)
+    vf = f64(v)[0, 0]
+    for i in range(N):
+        n = i + 1 if causal else N
+        np.testing.assert_allclose(o[0, :, i], np.broadcast_to(vf[:n].mean(0), (Hq, d)), rtol=1e-13, atol=1e-14)
+        np.testing.assert_allclose(lse[0, :, i], math.log(n), rtol=1e-14)
+
+
+def test_single_key_and_first_causal_row():
+    """N = 1: O = V and LSE = s_00.  Causal row 0 sees only key 0: O_0 = V_0."""
+    d = 16
+    q, k, v = random_bf16((1, 1, 1, d), 31), random_bf16((1, 1, 1, d), 32), random_bf16((1, 1, 1, d), 33)
+    for causal in (False, True):
+        o, lse = oracle.fwd(q, k, v, 0.25, causal)
+        np.testing.assert_array_equal(o, f64(v))
+        assert lse[0, 0, 0] == pytest.approx(0.25 * float(f64(q)[0, 0, 0] @ f64(k)[0, 0, 0]), rel=1e-14)
+    q, k, v = random_bf16((2, 3, 20, d), 34), random_bf16((2, 3, 20, d), 35), random_bf16((2, 3, 20, d), 36)
+    o, lse = oracle.fwd(q, k, v, 0.25, True)
+    np.testing.assert_array_equal(o[:, :, 0], f64(v)[:, :, 0])
+    s00 = 0.25 * np.einsum("bhc,bhc->bh", f64(q)[:, :, 0], f64(k)[:, :, 0])
+    np.testing.assert_allclose(lse[:, :, 0], s00, rtol=1e-14, atol=1e-15)
+
+
+def test_golden_hand_worked():
+    """Hand-derived closed forms stored in tests/golden/hand_worked.json."""
+    with open(os.path.join(GOLDEN, "hand_worked.json")) as f:
+        cases = json.load(f)["cases"]
+    for case in cases:
+        q = f32_to_bf16_bits(np.array(case["q"], np.float32))[None, None]
+        k = f32_to_bf16_bits(np.array(case["k"], np.float32))[None, None]
+        v = f32_to_bf16_bits(np.array(case["v"], np.float32))[None, None]
+        o, lse = oracle.fwd(q, k, v, case["scale"], case["causal"])
+        ev = np.vectorize(lambda e: eval(e, {"__builtins__": {}}, {"exp": math.exp, "log": math.log}),
+                          otypes=[np.float64])
+        np.testing.assert_allclose(o[0, 0], ev(np.array(case["o"])), rtol=1e-14, atol=1e-15,
+                                   err_msg=case["name"])
+        np.testing.assert_allclose(lse[0, 0], ev(np.array(case["lse"])), rtol=1e-14, atol=1e-15,
+                                   err_msg=case["name"])
+
+
+# ------------------------------------------------------------------- invariants
+
+def test_probability_rows():
+    """With V rows the unit vectors (d = N), O_i is the probability row P_i:
+    it sums to 1, is zero above the causal diagonal, and P_ij / P_ik equals
+    exp(s_ij - s_ik) with s computed here by numpy."""
+    N = d = 10
+    q = random_bf16((1, 1, N, d), 41)
+    k = random_bf16((1, 1, N, d), 42)
+    v = f32_to_bf16_bits(np.eye(N, dtype=np.float32))[None, None]
+    sc = 0.3
+    s = float(np.float32(sc)) * (f64(q)[0, 0] @ f64(k)[0, 0].T)
+    for causal in (False, True):
+        o, _ = oracle.fwd(q, k, v, sc, causal)
+        P = o[0, 0]
+        np.testing.assert_allclose(P.sum(1), 1.0, rtol=1e-14)
+        for i in range(N):
+            n = i + 1 if causal else N
+            if causal:
+                assert np.all(P[i, n:] == 0)
+            np.testing.assert_allclose(P[i, :n] / P[i, 0], np.exp(s[i, :n] - s[i, 0]), rtol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_constant_v(causal):
+    q, k = random_bf16((1, 2, 17, 8), 51), random_bf16((1, 2, 17, 8), 52)
+    row = f32_to_bf16_bits(np.linspace(-2, 3, 8, dtype=np.float32))
+    v = np.broadcast_to(row, (1, 2, 17, 8)).copy()
+    o, _ = oracle.fwd(q, k, v, 0.4, causal)
+    np.testing.assert_allclose(o, np.broadcast_to(f64(row), o.shape), rtol=1e-14, atol=1e-15)
+
+
+def test_key_permutation_noncausal():
+    q, k, v = random_bf16((1, 1, 23, 8), 61), random_bf16((1, 1, 23, 8), 62), random_bf16((1, 1, 23, 8), 63)
+    perm = np.random.default_rng(0).permutation(23)
+    o, lse = oracle.fwd(q, k, v, 0.35, False)
+    o2, lse2 = oracle.fwd(q, k[:, :, perm], v[:, :, perm], 0.35, False)
+    np.testing.assert_allclose(o2, o, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(lse2, lse, rtol=1e-14)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_lse_bounds(causal):
+    """max_j s_ij <= LSE_i <= max_j s_ij + ln n_i."""
+    N, d = 31, 16
+    q, k, v = random_bf16((1, 1, N, d), 71, 2.0), random_bf16((1, 1, N, d), 72), random_bf16((1, 1, N, d), 73)
+    sc = 0.25
+    s = sc * (f64(q)[0, 0] @ f64(k)[0, 0].T)
+    _, lse = oracle.fwd(q, k, v, sc, causal)
+    for i in range(N):
+        n = i + 1 if causal else N
+        mx = s[i, :n].max()
+        assert mx - 1e-12 <= lse[0, 0, i] <= mx + math.log(n) + 1e-12
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_row_shift(causal):
+    """K' = K + u (u = 1 in every channel) adds scale * (q_i . u) to every
+    score of row i: O is unchanged, LSE_i moves by exactly that amount.
+    K sits on multiples of 1/16 in [-4, 4] so K + 1 is exact in bf16."""
+    N, d = 19, 8
+    rng = np.random.default_rng(81)
+    kg = (rng.integers(-64, 65, size=(1, 1, N, d)) / 16.0).astype(np.float32)
+    k = f32_to_bf16_bits(kg)
+    k2 = f32_to_bf16_bits(kg + 1.0)
+    assert np.array_equal(f64(k2), f64(k) + 1.0)
+    q, v = random_bf16((1, 1, N, d), 82), random_bf16((1, 1, N, d), 83)
+    sc = 0.25
+    o, lse = oracle.fwd(q, k, v, sc, causal)
+    o2, lse2 = oracle.fwd(q, k2, v, sc, causal)
+    np.testing.assert_allclose(o2, o, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lse2 - lse, sc * f64(q)[0, 0].sum(-1)[None, None], rtol=1e-11, atol=1e-12)
+
+
+def test_causal_ignores_future_keys():
+    """Changing keys/values after position t leaves causal rows <= t untouched."""
+    N, d, t = 16, 8, 9
+    q, k, v = random_bf16((1, 1, N, d), 91), random_bf16((1, 1, N, d), 92), random_bf16((1, 1, N, d), 93)
+    k2, v2 = k.copy(), v.copy()
+    k2[..., t + 1:, :] = random_bf16((1, 1, N - t - 1, d), 94)
+    v2[..., t + 1:, :] = random_bf16((1, 1, N - t - 1, d), 95)
+    o, lse = oracle.fwd(q, k, v, 0.3, True)
+    o2, lse2 = oracle.fwd(q, k2, v2, 0.3, True)
+    np.testing.assert_array_equal(o2[..., :t + 1, :], o[..., :t + 1, :])
+    np.testing.assert_array_equal(lse2[..., :t + 1], lse[..., :t + 1])
+    assert not np.allclose(o2[..., t + 1:, :], o[..., t + 1:, :])
+
+
+def test_gqa_mapping():
+    """Query head h reads key/value head h // (Hq/Hkv): the GQA result equals
+    the per-head result with K/V repeated per group."""
+    B, Hq, Hkv, N, d = 1, 6, 2, 13, 8
+    q, k, v = random_bf16((B, Hq, N, d), 101), random_bf16((B, Hkv, N, d), 102), random_bf16((B, Hkv, N, d), 103)
+    o, lse = oracle.fwd(q, k, v, 0.3, True)
+    o2, lse2 = oracle.fwd(q, np.repeat(k, 3, axis=1), np.repeat(v, 3, axis=1), 0.3, True)
+    np.testing.assert_array_equal(o, o2)
+    np.testing.assert_array_equal(lse, lse2)
+
+
+# --------------------------------------------------------------------- backward
+
+def torch_grads(q, k, v, dout, scale, causal):
+    """float64 autograd of torch's SDPA (an independent derivation)."""
+    qt, kt, vt = (torch.from_numpy(f64(x)).requires_grad_() for x in (q, k, v))
+    grp = qt.shape[1] // kt.shape[1]
+    o = torch.nn.functional.scaled_dot_product_attention(
+        qt, kt.repeat_interleave(grp, 1), vt.repeat_interleave(grp, 1), is_causal=causal,
+        scale=float(np.float32(scale)))
+    o.backward(torch.from_numpy(f64(dout)))
+    return qt.grad.numpy(), kt.grad.numpy(), vt.grad.numpy()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("B,Hq,Hkv,N,d", [(1, 1, 1, 1, 4), (1, 2, 2, 24, 16), (2, 4, 2, 19, 8), (1, 4, 1, 40, 32)])
+def test_bwd_vs_torch_autograd(B, Hq, Hkv, N, d, causal):
+    q, k, v = random_bf16((B, Hq, N, d), 111), random_bf16((B, Hkv, N, d), 112), random_bf16((B, Hkv, N, d), 113)
+    dout = random_bf16((B, Hq, N, d), 114)
+    scale = 1.0 / math.sqrt(d)
+    r = oracle.bwd(q, k, v, dout, scale, causal)
+    dq, dk, dv = torch_grads(q, k, v, dout, scale, causal)
+    np.testing.assert_allclose(r["dq"], dq, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(r["dk"], dk, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(r["dv"], dv, rtol=1e-10, atol=1e-12)
+    o, lse = oracle.fwd(q, k, v, scale, causal)
+    np.testing.assert_array_equal(r["o"], o)
+    np.testing.assert_allclose(r["lse"], lse, rtol=1e-15, atol=1e-15)
+
+
+def _grid(shape, rng):
+    """Values on multiples of 1/32 in [-1, 1]: x +- m/128 (|m| <= 4) stays exact in bf16."""
+    return (rng.integers(-32, 33, size=shape) / 32.0).astype(np.float32)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("Hq,Hkv", [(1, 1), (2, 1)])
+def test_bwd_finite_differences(causal, Hq, Hkv):
+    """L = sum(dO * O).  Richardson-extrapolated central differences along a
+    random {-1, 0, 1} direction (step 2^-7, exact in bf16) match
+    sum(grad * direction) for each of Q, K, V."""
+    B, N, d = 1, 7, 4
+    rng = np.random.default_rng(121)
+    base = {"q": _grid((B, Hq, N, d), rng), "k": _grid((B, Hkv, N, d), rng), "v": _grid((B, Hkv, N, d), rng)}
+    dout = f32_to_bf16_bits(_grid((B, Hq, N, d), rng))
+    scale = 0.5
+    bits = {n: f32_to_bf16_bits(x) for n, x in base.items()}
+    grads = oracle.bwd(bits["q"], bits["k"], bits["v"], dout, scale, causal)
+
+    def loss(arrs):
+        o, _ = oracle.fwd(f32_to_bf16_bits(arrs["q"]), f32_to_bf16_bits(arrs["k"]),
+                          f32_to_bf16_bits(arrs["v"]), scale, causal)
+        return float(np.sum(f64(dout) * o))
+
+    eps = 2.0 ** -7
+    for name, gname in (("q", "dq"), ("k", "dk"), ("v", "dv")):
+        direction = rng.integers(-1, 2, size=base[name].shape).astype(np.float32)
+
+        def central(step):
+            plus, minus = dict(base), dict(base)
+            plus[name] = base[name] + np.float32(step) * direction
+            minus[name] = base[name] - np.float32(step) * direction
+            assert np.array_equal(f64(f32_to_bf16_bits(plus[name])), plus[name].astype(np.float64))
+            return (loss(plus) - loss(minus)) / (2 * step)
+
+        fd = (4 * central(eps) - central(2 * eps)) / 3
+        analytic = float(np.sum(grads[gname] * direction))
+        assert fd == pytest.approx(analytic, rel=2e-6, abs=1e-8), name
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_exact_identities(causal):
+    """sum_j dS_ij = 0 for every row, so sum_j dK_j = 0; P rows sum to 1, so
+    sum_j dV_j = sum over the group's heads and rows of dO_i."""
+    B, Hq, Hkv, N, d = 2, 4, 2, 21, 8
+    q, k, v = random_bf16((B, Hq, N, d), 131), random_bf16((B, Hkv, N, d), 132), random_bf16((B, Hkv, N, d), 133)
+    dout = random_bf16((B, Hq, N, d), 134)
+    r = oracle.bwd(q, k, v, dout, 0.35, causal)
+    np.testing.assert_allclose(r["dk"].sum(2), 0.0, atol=1e-13)
+    want = f64(dout).reshape(B, Hkv, Hq // Hkv, N, d).sum((2, 3))
+    np.testing.assert_allclose(r["dv"].sum(2), want, rtol=1e-12, atol=1e-12)
+
+
+def test_bwd_constant_v():
+    """Constant V makes dP_ij = D_i, so dS = 0 and dQ = dK = 0."""
+    q, k = random_bf16((1, 2, 15, 8), 141), random_bf16((1, 2, 15, 8), 142)
+    row = f32_to_bf16_bits(np.linspace(-1, 2, 8, dtype=np.float32))
+    v = np.broadcast_to(row, (1, 2, 15, 8)).copy()
+    dout = random_bf16((1, 2, 15, 8), 143)
+    for causal in (False, True):
+        r = oracle.bwd(q, k, v, dout, 0.4, causal)
+        np.testing.assert_allclose(r["dq"], 0.0, atol=1e-13)
+        np.testing.assert_allclose(r["dk"], 0.0, atol=1e-13)
+
+
+def test_bwd_groups_subset_matches_full():
+    B, Hq, Hkv, N, d = 2, 4, 2, 17, 8
+    q, k, v = random_bf16((B, Hq, N, d), 151), random_bf16((B, Hkv, N, d), 152), random_bf16((B, Hkv, N, d), 153)
+    dout = random_bf16((B, Hq, N, d), 154)
+    full = oracle.bwd(q, k, v, dout, 0.3, True)
+    sub = oracle.bwd_groups(q, k, v, dout, 0.3, True, [3])  # b = 1, g = 1
+    np.testing.assert_array_equal(sub["dq"][0], full["dq"][1, 2:4])
+    np.testing.assert_array_equal(sub["dk"][0], full["dk"][1, 1])
+    np.testing.assert_array_equal(sub["dv"][0], full["dv"][1, 1])
+
+
+def test_rejects_bad_shapes():
+    q = random_bf16((1, 3, 4, 4), 1)
+    k = random_bf16((1, 2, 4, 4), 2)
+    with pytest.raises(ValueError):
+        oracle.fwd(q, k, k, 0.5, False)
