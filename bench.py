@@ -1,0 +1,186 @@
+"""Throughput of exact tiled attention (forward + backward) on one MI355X.
+
+One step = the whole path over one batch: fa_fwd (O, LSE) then fa_bwd (dQ, dK,
+dV; atomic-dQ mode) on the B=4, Hq=Hkv=16, N=4096, d=128 non-causal bf16
+workload (iid N(0,1) inputs, dO drawn after V).  FLOPs are counted nominally:
+forward 4*B*Hq*N^2*d (halved when causal), backward 2.5x the forward.
+
+Prints ONE JSON line.  Inputs are resident in HBM before the timed region; the
+region is bracketed by device synchronisation.  HIP events recorded on the
+launch stream around each call give per-kernel durations for the roofline.
+The fp64 CPU oracle is timed on a bounded sample (one head's forward and
+backward) of the same workload as a reported baseline.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA peak (published)
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="fwd_n4096")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--extra", action="store_true",
+                   help="also time the deterministic backward (reported under parts)")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import exact_tiled_attention_27_amd as fa
+    from synth import WORKLOADS, make_inputs, random_bf16
+    from dataclasses import replace
+
+    w = WORKLOADS[args.workload]
+    if not w.backward:
+        w = replace(w, backward=True)  # the step runs the backward on the same shape
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    x = make_inputs(w)
+
+    def to_dev(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, k, v, do = to_dev(x["q"]), to_dev(x["k"]), to_dev(x["v"]), to_dev(x["dout"])
+    B, Hq, Hkv, N, d = w.B, w.Hq, w.Hkv, w.N, w.d
+    o = torch.empty((B, Hq, N, d), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
+    dq = torch.empty((B, Hq, N, d), dtype=torch.float32, device=dev)
+    dk = torch.empty((B, Hkv, N, d), dtype=torch.float32, device=dev)
+    dv = torch.empty_like(dk)
+    ws_bytes = max(fa.fa_bwd_workspace_bytes(B, Hq, Hkv, N, d, 1),
+                   fa.fa_bwd_workspace_bytes(B, Hq, Hkv, N, d, 0))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def fwd():
+        st = fa.fa_fwd(q, k, v, o, lse, B, Hq, Hkv, N, d, w.scale, w.causal, stream.cuda_stream)
+        if st:
+            raise fa.FAError(st, "fa_fwd")
+
+    def bwd(det):
+        st = fa.fa_bwd(q, k, v, o, lse, do, dq, dk, dv, B, Hq, Hkv, N, d, w.scale, w.causal, det,
+                       ws, ws_bytes, stream.cuda_stream)
+        if st:
+            raise fa.FAError(st, "fa_bwd")
+
+    print(f"bench: workload {w.name} ({w.note}); warmup {args.warmup}, steps {args.steps}",
+          file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        fwd()
+        bwd(0)
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        fwd()
+        ev[i][1].record(stream)
+        bwd(0)
+        ev[i][2].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    fwd_ms = [e[0].elapsed_time(e[1]) for e in ev]
+    bwd_ms = [e[1].elapsed_time(e[2]) for e in ev]
+    ms_step = total_ms / args.steps
+    f_fwd, f_bwd = w.fwd_flops(), w.bwd_flops()
+    value = (f_fwd + f_bwd) / (ms_step * 1e-3) / 1e12
+
+    parts = {
+        "fwd_ms_avg": float(np.mean(fwd_ms)),
+        "fwd_tflops": f_fwd / (np.mean(fwd_ms) * 1e-3) / 1e12,
+        "bwd_atomic_ms_avg": float(np.mean(bwd_ms)),
+        "bwd_atomic_tflops": f_bwd / (np.mean(bwd_ms) * 1e-3) / 1e12,
+    }
+    parts["fwd_frac_peak"] = parts["fwd_tflops"] / PEAK_BF16_TFLOPS
+    parts["bwd_atomic_frac_peak"] = parts["bwd_atomic_tflops"] / PEAK_BF16_TFLOPS
+
+    if args.extra:
+        reps = max(3, args.steps // 2)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        bwd(1)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            bwd(1)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        det_ms = e0.elapsed_time(e1) / reps
+        parts["bwd_deterministic_ms_avg"] = det_ms
+        parts["bwd_deterministic_tflops"] = f_bwd / (det_ms * 1e-3) / 1e12
+
+    # Roofline of the dominant launch: the forward kernel is one launch per
+    # fa_fwd; fa_bwd (atomic mode) is a short preprocess kernel plus the dK/dV
+    # kernel that carries all backward MFMA work.
+    if parts["fwd_ms_avg"] >= parts["bwd_atomic_ms_avg"]:
+        rl_name, rl_flops, rl_ms = "fa::fwd_kernel", f_fwd, parts["fwd_ms_avg"]
+    else:
+        rl_name, rl_flops, rl_ms = "fa_bwd (bwd_pre_kernel + bwd_dkdv_kernel)", f_bwd, parts["bwd_atomic_ms_avg"]
+    achieved = rl_flops / (rl_ms * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": rl_name, "achieved": achieved,
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                "traffic": None, "flops_per_launch": rl_flops, "avg_launch_ms": rl_ms}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        threads = oracle.default_threads()
+        # Sample: the forward and backward of one (batch, head) pair.
+        groups = [0]
+        t0 = time.perf_counter()
+        oracle.bwd_groups(x["q"], x["k"], x["v"], x["dout"], w.scale, w.causal, groups,
+                          threads=threads)
+        secs = time.perf_counter() - t0
+        grp = Hq // Hkv
+        frac = grp / (B * Hq)
+        sample_flops = (f_fwd + f_bwd) * frac
+        cpu = {"value": sample_flops / secs / 1e12, "unit": "TFLOP/s", "cores": threads,
+               "kind": "oracle",
+               "sample": f"fp64 forward+backward of {grp} of {B * Hq} heads "
+                         f"(N={N}, d={d}); {secs:.1f} s"}
+
+    out = {
+        "metric": "attention fwd/bwd TFLOP/s (bf16, d=128) and % of MI355X bf16 MFMA peak",
+        "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "frac_peak": value / PEAK_BF16_TFLOPS,
+        "config": {"workload": w.name, "B": B, "Hq": Hq, "Hkv": Hkv, "N": N, "d": d,
+                   "causal": w.causal, "step": "fa_fwd + fa_bwd (atomic dQ)",
+                   "flops_per_step": f_fwd + f_bwd},
+        "parts": parts,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

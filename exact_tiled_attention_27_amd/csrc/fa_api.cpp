@@ -1,0 +1,95 @@
+// fa_api.cpp -- the C ABI declared in include/fa.h: argument validation,
+// workspace layout and dispatch to the gfx950 kernels.  Nothing here touches
+// the GPU before every argument has been checked.
+#include "fa.h"
+
+#include <cmath>
+#include <cstdint>
+
+#include "fa_launch.hpp"
+
+namespace {
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Shape and scale checks shared by forward and backward.
+int check_common(int B, int Hq, int Hkv, int N, int d, float scale)
+{
+    if (B < 1 || Hq < 1 || Hkv < 1 || N < 1 || Hq % Hkv != 0) return FA_ERR_SHAPE;
+    if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_SHAPE;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    // Largest element offset must fit the kernels' 64-bit indexing and the
+    // 32-bit grid: B * Hq * ceil(N / 64) workgroups.
+    const int64_t rows = (int64_t)B * Hq * N;
+    if (rows > ((int64_t)1 << 40) || (int64_t)B * Hq * ((N + 63) / 64) > INT32_MAX) return FA_ERR_SHAPE;
+    return FA_OK;
+}
+
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char *fa_status_string(int status)
+{
+    switch (status) {
+    case FA_OK: return "FA_OK";
+    case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
+    case FA_ERR_SHAPE: return "FA_ERR_SHAPE: invalid B/Hq/Hkv/N or scale";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: head dimension must be 64 or 128";
+    case FA_ERR_ALIGN: return "FA_ERR_ALIGN: pointers must be 16-byte aligned";
+    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing or too small";
+    case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime reported an error";
+    default: return "unknown fa_status";
+    }
+}
+
+int fa_fwd(const void *q, const void *k, const void *v, float *o, float *lse, int B, int Hq,
+           int Hkv, int N, int d, float scale, int causal, void *stream)
+{
+    if (!q || !k || !v || !o) return FA_ERR_NULL;
+    int st = check_common(B, Hq, Hkv, N, d, scale);
+    if (st != FA_OK) return st;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+        (lse && !aligned16(lse)))
+        return FA_ERR_ALIGN;
+    fa::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, N, d, scale, fa::kRescaleTau, causal != 0,
+                  reinterpret_cast<hipStream_t>(stream)};
+    return hip_status(fa::launch_fwd(a));
+}
+
+size_t fa_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d, int deterministic)
+{
+    (void)deterministic;
+    if (check_common(B, Hq, Hkv, N, d, 1.0f) != FA_OK) return 0;
+    const size_t rows = (size_t)B * Hq * N;
+    return 2 * round256(rows * sizeof(float));
+}
+
+int fa_bwd(const void *q, const void *k, const void *v, const float *o, const float *lse,
+           const void *dout, float *dq, float *dk, float *dv, int B, int Hq, int Hkv, int N,
+           int d, float scale, int causal, int deterministic, void *workspace,
+           size_t workspace_bytes, void *stream)
+{
+    if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL;
+    int st = check_common(B, Hq, Hkv, N, d, scale);
+    if (st != FA_OK) return st;
+    const void *ptrs[] = {q, k, v, o, lse, dout, dq, dk, dv};
+    for (const void *p : ptrs)
+        if (!aligned16(p)) return FA_ERR_ALIGN;
+    const size_t need = fa_bwd_workspace_bytes(B, Hq, Hkv, N, d, deterministic);
+    if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return FA_ERR_ALIGN;
+    const size_t rows = (size_t)B * Hq * N;
+    float *delta = reinterpret_cast<float *>(workspace);
+    float *lse2 = reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) +
+                                            round256(rows * sizeof(float)));
+    fa::BwdArgs a{q, k, v, dout, o, lse, dq, dk, dv, delta, lse2, B, Hq, Hkv, N, d, scale,
+                  causal != 0, deterministic != 0, reinterpret_cast<hipStream_t>(stream)};
+    return hip_status(fa::launch_bwd(a));
+}
+
+}  // extern "C"

@@ -1,0 +1,115 @@
+// fa_device.hpp -- gfx950 device building blocks for the attention kernels.
+//
+// MFMA v_mfma_f32_32x32x16_bf16 (one wave of 64 lanes, lane l, half h = l/32):
+//   A (32 x 16):  lane l holds A[l % 32][k-slots of half h]      (8 bf16)
+//   B (16 x 32):  lane l holds B[k-slots of half h][l % 32]      (8 bf16)
+//   C (32 x 32):  lane l holds C[8*(r/4) + 4*h + r%4][l % 32], r = 0..15
+// A and B map (half, slot) to the contraction index identically, so any
+// consistent assignment of physical contraction indices to (half, slot)
+// computes the same product; the kernels use that freedom to feed a C result
+// straight back as a B operand (the contraction runs over C's rows).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x16 mfma32(const bf16x8 &a, const bf16x8 &b, const f32x16 &c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Hardware base-2 exponential (v_exp_f32): exp2(-inf) = 0.
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Pack 8 fp32 values into bf16 (round to nearest even).
+__device__ __forceinline__ bf16x8 pack_bf16x8(float a0, float a1, float a2, float a3, float a4,
+                                              float a5, float a6, float a7)
+{
+    bf16x8 r;
+    r[0] = (__bf16)a0; r[1] = (__bf16)a1; r[2] = (__bf16)a2; r[3] = (__bf16)a3;
+    r[4] = (__bf16)a4; r[5] = (__bf16)a5; r[6] = (__bf16)a6; r[7] = (__bf16)a7;
+    return r;
+}
+
+// Registers 8*j .. 8*j+7 of a 32x32 accumulator as a bf16 B operand.
+__device__ __forceinline__ bf16x8 pack_half(const f32x16 &c, int j)
+{
+    return pack_bf16x8(c[8 * j + 0], c[8 * j + 1], c[8 * j + 2], c[8 * j + 3], c[8 * j + 4],
+                       c[8 * j + 5], c[8 * j + 6], c[8 * j + 7]);
+}
+
+// LDS (address space 3) 16-byte and 8-byte accesses at a byte offset.
+__device__ __forceinline__ bf16x8 lds_read_bf16x8(const char *lds, uint32_t byte_off)
+{
+    return *reinterpret_cast<const bf16x8 *>(lds + byte_off);
+}
+__device__ __forceinline__ f32x4 lds_read_f32x4(const char *lds, uint32_t byte_off)
+{
+    return *reinterpret_cast<const f32x4 *>(lds + byte_off);
+}
+__device__ __forceinline__ void lds_write_u32x4(char *lds, uint32_t byte_off, u32x4 v)
+{
+    *reinterpret_cast<u32x4 *>(lds + byte_off) = v;
+}
+__device__ __forceinline__ void lds_write_u32x2(char *lds, uint32_t byte_off, u32x2 v)
+{
+    *reinterpret_cast<u32x2 *>(lds + byte_off) = v;
+}
+
+// 16-byte global load with a zero fill when the row is out of range.
+__device__ __forceinline__ u32x4 gload16(const void *base, size_t byte_off, bool ok)
+{
+    u32x4 z = {0u, 0u, 0u, 0u};
+    return ok ? *reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(base) + byte_off) : z;
+}
+
+// Value of lane l ^ 32 (the other half of the wave).
+__device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32, 64); }
+
+// Within a group of 16 keys, the key order a 32x32 C tile presents to a B
+// operand: half h, slot t holds key 8*(t/4) + 4*h + t%4.  Stored position of
+// key kk so that half h reads positions 8h .. 8h+7 as one 16-byte chunk:
+// swap quarters 1 and 2 of the group.
+__device__ __host__ __forceinline__ int key_pos16(int kk)
+{
+    return ((kk & 4) << 1) | ((kk & 8) >> 1) | (kk & 3);
+}
+
+// Round-robin dispatch puts workgroup i on XCD i % 8.  Map the hardware id to
+// (head, tile) so each XCD works through whole heads: the workgroups that
+// share one head's K/V run on the same XCD and share its L2.  With a causal
+// mask the tiles of an XCD are issued longest first.
+constexpr int kNumXcd = 8;
+__device__ __forceinline__ void xcd_tile_map(int hw, int BH, int T, bool longest_first,
+                                             int &bh, int &t)
+{
+    if (BH % kNumXcd == 0) {
+        const int per = BH / kNumXcd;
+        const int xcd = hw % kNumXcd, slot = hw / kNumXcd;
+        if (longest_first) {
+            t = T - 1 - slot / per;
+            bh = xcd * per + slot % per;
+        } else {
+            bh = xcd * per + slot / T;
+            t = slot % T;
+        }
+    } else if (longest_first) {
+        t = T - 1 - hw / BH;
+        bh = hw % BH;
+    } else {
+        bh = hw / T;
+        t = hw % T;
+    }
+}
+
+}  // namespace fa

@@ -1,0 +1,37 @@
+// fa_launch.hpp -- internal launcher interface between the C ABI (fa_api.cpp)
+// and the kernels.  Arguments reach here already validated.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace fa {
+
+struct FwdArgs {
+    const void *q, *k, *v;
+    float *o, *lse;
+    int B, Hq, Hkv, N, d;
+    float scale;   // > 0
+    float tau;     // rescale threshold in the base-2 exponent domain
+    bool causal;
+    hipStream_t stream;
+};
+
+struct BwdArgs {
+    const void *q, *k, *v, *dout;
+    const float *o, *lse;
+    float *dq, *dk, *dv;
+    float *delta;  // workspace: D_i = sum_c dO_ic O_ic, [B, Hq, N]
+    float *lse2;   // workspace: LSE_i * log2(e), [B, Hq, N]
+    int B, Hq, Hkv, N, d;
+    float scale;
+    bool causal, deterministic;
+    hipStream_t stream;
+};
+
+hipError_t launch_fwd(const FwdArgs &a);
+hipError_t launch_bwd(const BwdArgs &a);
+
+// Rescale threshold: log2(256) = 8 (conditional rescaling).
+constexpr float kRescaleTau = 8.0f;
+
+}  // namespace fa

@@ -1,0 +1,134 @@
+// fa_tiles.hpp -- staging of bf16 [rows, D] tiles from HBM into LDS.
+//
+// Two LDS layouts, both read by MFMA operand loads of 16 bytes (8 bf16):
+//
+//  RowTile: row-major [ROWS][D].  The 16-byte chunk c of row r is stored at
+//    chunk c ^ (r & 7).  A wave reading the same chunk of 32 consecutive rows
+//    then touches 8 distinct chunk slots per 8 rows: no bank conflicts.
+//
+//  ColTile: transposed [D][ROWS] (one LDS row per head-dimension index d).
+//    Sequence positions inside each group of 16 are stored either in natural
+//    order or in key_pos16 order (the order in which a 32x32 accumulator
+//    presents its rows to a B operand, so a C result can be contracted
+//    against this tile without moving it).  Chunk j of LDS row d is stored
+//    at chunk j ^ f(d), f(d) = (d & 7) ^ ((d >> 3) & 7): reads of one chunk
+//    from 32 consecutive d rows and the transposing writes both spread over
+//    the banks.
+//
+// Loads go global -> registers (16-byte loads, rows >= N read as zero) and
+// registers -> LDS in a separate call, so the next tile's loads can be in
+// flight while the current tile is computed.
+#pragma once
+#include "fa_device.hpp"
+
+namespace fa {
+
+__device__ __forceinline__ uint32_t row_tile_off(int row, int chunk, int D)
+{
+    return row * (D * 2) + ((chunk ^ (row & 7)) << 4);
+}
+
+__device__ __forceinline__ int col_swz(int d) { return (d & 7) ^ ((d >> 3) & 7); }
+
+template <int ROWS>
+__device__ __forceinline__ uint32_t col_tile_off(int d, int chunk)
+{
+    return d * (ROWS * 2) + ((chunk ^ col_swz(d)) << 4);
+}
+
+template <int ROWS, int D, int THREADS>
+struct RowTile {
+    static constexpr int CPR = D / 8;  // 16-byte chunks per row
+    static constexpr int TOTAL = ROWS * CPR;
+    static constexpr int ITEMS = (TOTAL + THREADS - 1) / THREADS;
+    static constexpr int BYTES = ROWS * D * 2;
+    u32x4 x[ITEMS];
+
+    __device__ __forceinline__ void load(const uint16_t *head, int row0, int N, int tid)
+    {
+#pragma unroll
+        for (int i = 0; i < ITEMS; i++) {
+            const int item = tid + i * THREADS;
+            const int row = item / CPR, c = item % CPR;
+            const int n = row0 + row;
+            x[i] = gload16(head, ((size_t)n * D + c * 8) * 2, item < TOTAL && n < N);
+        }
+    }
+    __device__ __forceinline__ void store(char *lds, int tid) const
+    {
+#pragma unroll
+        for (int i = 0; i < ITEMS; i++) {
+            const int item = tid + i * THREADS;
+            if (item < TOTAL) {
+                const int row = item / CPR, c = item % CPR;
+                lds_write_u32x4(lds, row_tile_off(row, c, D), x[i]);
+            }
+        }
+    }
+};
+
+template <int ROWS, int D, int THREADS, bool PERM>
+struct ColTile {
+    static constexpr int CPR = D / 8;
+    static constexpr int TOTAL = (ROWS / 4) * CPR;  // items of 4 rows x 8 columns
+    static constexpr int ITEMS = (TOTAL + THREADS - 1) / THREADS;
+    static constexpr int BYTES = ROWS * D * 2;
+    u32x4 x[ITEMS][4];
+
+    __device__ __forceinline__ void load(const uint16_t *head, int row0, int N, int tid)
+    {
+#pragma unroll
+        for (int i = 0; i < ITEMS; i++) {
+            const int item = tid + i * THREADS;
+            const int e = item % CPR, a = item / CPR;
+            const bool live = item < TOTAL;
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                const int n = row0 + 4 * a + q;
+                x[i][q] = gload16(head, ((size_t)n * D + e * 8) * 2, live && n < N);
+            }
+        }
+    }
+    // Transposed store: LDS row d, positions of rows 4a .. 4a+3.
+    __device__ __forceinline__ void store(char *lds, int tid) const
+    {
+#pragma unroll
+        for (int i = 0; i < ITEMS; i++) {
+            const int item = tid + i * THREADS;
+            if (item < TOTAL) {
+                const int e = item % CPR, a = item / CPR;
+                const int kk = 4 * a;
+                const int pos = PERM ? ((kk & ~15) | key_pos16(kk & 15)) : kk;
+                const int chunk = pos >> 3, within = (pos & 7) * 2;
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    const uint32_t w0 = x[i][0][j], w1 = x[i][1][j], w2 = x[i][2][j],
+                                   w3 = x[i][3][j];
+                    // Column d = 8e + 2j takes the low halves, d + 1 the high halves.
+                    const u32x2 lo = {(w0 & 0xffffu) | (w1 << 16), (w2 & 0xffffu) | (w3 << 16)};
+                    const u32x2 hi = {(w0 >> 16) | (w1 & 0xffff0000u),
+                                      (w2 >> 16) | (w3 & 0xffff0000u)};
+                    const int d0 = 8 * e + 2 * j;
+                    lds_write_u32x2(lds, col_tile_off<ROWS>(d0, chunk) + within, lo);
+                    lds_write_u32x2(lds, col_tile_off<ROWS>(d0 + 1, chunk) + within, hi);
+                }
+            }
+        }
+    }
+    // The same registers stored row-major (RowTile layout).
+    __device__ __forceinline__ void store_rows(char *lds, int tid) const
+    {
+#pragma unroll
+        for (int i = 0; i < ITEMS; i++) {
+            const int item = tid + i * THREADS;
+            if (item < TOTAL) {
+                const int e = item % CPR, a = item / CPR;
+#pragma unroll
+                for (int q = 0; q < 4; q++)
+                    lds_write_u32x4(lds, row_tile_off(4 * a + q, e, D), x[i][q]);
+            }
+        }
+    }
+};
+
+}  // namespace fa

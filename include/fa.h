@@ -1,0 +1,106 @@
+/*
+ * fa.h -- C ABI of the MI355X (gfx950) exact tiled attention library libfa.so.
+ *
+ * What the calls compute (FlashAttention-4 pages):
+ *   Forward: per tile of keys, S = Q K^T * scale, a running row max / row sum
+ *   softmax P = exp(S - m) / l, and O = P V ("The Asymmetric Hardware Scaling
+ *   Wall", three phases per tile; the simulator in "End-to-End Implementation"
+ *   walks key tiles with a running max and sum).  The result is exact
+ *   attention softmax(Q K^T * scale) V up to rounding.  The normalisation is
+ *   skipped unless the running maximum grows by more than log2(256) = 8 in the
+ *   base-2 exponent domain (menfem page, "Key Contributions", item 2).
+ *   Backward: dQ, dK, dV of the same function, with P recomputed from the
+ *   saved log-sum-exp; dQ is summed either with global atomic adds or by a
+ *   separate deterministic pass (menfem page, "Key Contributions" item 3 and
+ *   "Limitations": the deterministic mode trades speed for reproducibility).
+ *
+ * Conventions shared by every call:
+ *   - Tensors are device pointers to dense row-major arrays laid out
+ *     [B, H, N, d] (sequence-major within a head, as in the simulator's
+ *     [Batch, Heads, Len, HeadDim]).  Q, dO, O, dQ use H = Hq; K, V, dK, dV use
+ *     H = Hkv.  LSE and the workspace rows are [B, Hq, N].
+ *   - bf16 tensors hold IEEE bfloat16 bit patterns (uint16).  O, LSE, dQ, dK,
+ *     dV are float32.
+ *   - Grouped-query attention: query head h reads key/value head
+ *     h / (Hq / Hkv).
+ *   - causal != 0 keeps key j for query i iff j <= i.
+ *   - LSE is the natural-log log-sum-exp of the scaled scores of each row:
+ *     LSE_i = ln sum_j exp(scale * q_i . k_j).
+ *   - The caller owns every buffer; the library allocates no device memory,
+ *     keeps no state between calls and may be called concurrently on
+ *     different streams with disjoint outputs.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
+ *     without any host synchronisation.  Argument errors return before any
+ *     work is enqueued.  A launch failure returns FA_ERR_HIP; faults during
+ *     execution surface at the caller's next synchronisation.
+ *   - Supported: d in {64, 128}; B, Hq, Hkv, N >= 1; Hq % Hkv == 0;
+ *     scale > 0 and finite; every pointer 16-byte aligned; N need not be a
+ *     multiple of any tile size.  Element offsets are 64-bit.
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FA_OK = 0,
+    FA_ERR_NULL = 1,        /* a required pointer is NULL                       */
+    FA_ERR_SHAPE = 2,       /* B/Hq/Hkv/N < 1, Hq % Hkv != 0, or scale invalid  */
+    FA_ERR_UNSUPPORTED = 3, /* head dimension d not in {64, 128}                */
+    FA_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned                 */
+    FA_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required       */
+    FA_ERR_HIP = 6          /* the HIP runtime reported an error on launch      */
+} fa_status;
+
+/*
+ * Forward attention.
+ *   q   bf16 [B, Hq,  N, d]   (read)
+ *   k   bf16 [B, Hkv, N, d]   (read)
+ *   v   bf16 [B, Hkv, N, d]   (read)
+ *   o   fp32 [B, Hq,  N, d]   (written: softmax(q k^T * scale) v)
+ *   lse fp32 [B, Hq,  N]      (written; may be NULL when not needed)
+ * Returns an fa_status.
+ */
+int fa_fwd(const void *q, const void *k, const void *v, float *o, float *lse,
+           int B, int Hq, int Hkv, int N, int d, float scale, int causal, void *stream);
+
+/*
+ * Bytes of device workspace fa_bwd needs for this shape (the per-row
+ * D_i = sum_c dO_ic O_ic and the base-2 LSE, fp32 [B, Hq, N] each, rounded
+ * up to 256 bytes).  Returns 0 for an invalid shape.
+ */
+size_t fa_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d, int deterministic);
+
+/*
+ * Backward attention.
+ *   q, k, v   as in fa_fwd (read)
+ *   o, lse    the forward's outputs for the same inputs (read)
+ *   dout      bf16 [B, Hq, N, d], the gradient of the loss w.r.t. o (read)
+ *   dq        fp32 [B, Hq,  N, d]  (written)
+ *   dk, dv    fp32 [B, Hkv, N, d]  (written; summed over each group's heads)
+ *   deterministic == 0: dq is accumulated with fp32 global atomic adds
+ *     (bits may differ from run to run); != 0: a separate dq pass with no
+ *     atomics (bitwise identical run to run on the same device and shape).
+ *   workspace / workspace_bytes: device scratch of at least
+ *     fa_bwd_workspace_bytes(...) bytes, 16-byte aligned, owned by the
+ *     caller; its contents on entry are ignored.
+ * Returns an fa_status.
+ */
+int fa_bwd(const void *q, const void *k, const void *v, const float *o, const float *lse,
+           const void *dout, float *dq, float *dk, float *dv,
+           int B, int Hq, int Hkv, int N, int d, float scale, int causal, int deterministic,
+           void *workspace, size_t workspace_bytes, void *stream);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char *fa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

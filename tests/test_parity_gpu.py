@@ -1,0 +1,265 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Bar (fp32 outputs O, dQ, dK, dV): max |err| <= 1e-2 and mean |err| <= 1e-3 over
+every compared element; LSE: |err| <= 1e-3 * max(1, |LSE_ref|).  One derived
+exception: with N < 64 an element of dV/dK/dQ sums only a handful of terms, so
+the bf16 rounding of P and dS (relative error up to 2^-9) does not average out;
+there the mean bar is 2e-3 (rounding P alone, emulated in numpy, already gives
+mean 1.25e-3 at N = 3, d = 128, GQA 2:1, and the kernel matches that emulation).
+
+Every output buffer is NaN-poisoned before the call and sits between NaN guard
+zones: afterwards the guards must still be NaN (nothing written out of bounds)
+and the output must hold no NaN (every element written).
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from synth import WORKLOADS, make_inputs, random_bf16, f32_to_bf16_bits
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+MAX_ABS, MEAN_ABS, LSE_REL = 1e-2, 1e-3, 1e-3
+GUARD = 64  # fp32 elements of NaN on each side of every output
+
+
+def note(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def fa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import exact_tiled_attention_27_amd as m
+    return m
+
+
+def dev(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+class Guarded:
+    """fp32 device tensor of `shape` inside a NaN-filled buffer with guard zones."""
+
+    def __init__(self, shape):
+        n = int(np.prod(shape))
+        self.buf = torch.full((n + 2 * GUARD,), float("nan"), dtype=torch.float32, device="cuda")
+        self.t = self.buf[GUARD:GUARD + n].view(shape)
+        assert self.t.data_ptr() % 16 == 0
+
+    def result(self, name):
+        torch.cuda.synchronize()
+        g = torch.cat([self.buf[:GUARD], self.buf[-GUARD:]])
+        assert torch.isnan(g).all(), f"{name}: write outside the output buffer"
+        out = self.t.cpu().numpy()
+        assert not np.isnan(out).any(), f"{name}: {int(np.isnan(out).sum())} elements not written"
+        return out
+
+
+MEAN_ABS_FEW_TERMS = 2e-3  # N < 64 only (see the module docstring)
+
+
+def compare(name, got, ref, mean_bar=MEAN_ABS):
+    err = np.abs(got.astype(np.float64) - ref)
+    mx, mean = float(err.max()), float(err.mean())
+    note(f"  {name}: max_abs={mx:.3e} mean_abs={mean:.3e} (|ref| max {np.abs(ref).max():.3f})")
+    assert mx <= MAX_ABS and mean <= mean_bar, f"{name}: max_abs {mx:.3e}, mean_abs {mean:.3e}"
+
+
+def compare_lse(got, ref):
+    err = np.abs(got.astype(np.float64) - ref) / np.maximum(1.0, np.abs(ref))
+    note(f"  lse: max_rel={float(err.max()):.3e}")
+    assert float(err.max()) <= LSE_REL
+
+
+def gpu_fwd(fa, q, k, v, scale, causal):
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    o = Guarded((B, Hq, N, d))
+    lse = Guarded((B, Hq, N))
+    st = fa.fa_fwd(dev(q), dev(k), dev(v), o.t, lse.t, B, Hq, Hkv, N, d, scale, causal)
+    assert st == 0, fa.fa_status_string(st)
+    return o.result("o"), lse.result("lse")
+
+
+def gpu_bwd(fa, q, k, v, dout, o, lse, scale, causal, deterministic):
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    dq, dk, dv = Guarded((B, Hq, N, d)), Guarded((B, Hkv, N, d)), Guarded((B, Hkv, N, d))
+    need = fa.fa_bwd_workspace_bytes(B, Hq, Hkv, N, d, deterministic)
+    ws = torch.full((need,), 255, dtype=torch.uint8, device="cuda")
+    st = fa.fa_bwd(dev(q), dev(k), dev(v), torch.from_numpy(o).cuda(), torch.from_numpy(lse).cuda(),
+                   dev(dout), dq.t, dk.t, dv.t, B, Hq, Hkv, N, d, scale, causal, deterministic,
+                   ws, need)
+    assert st == 0, fa.fa_status_string(st)
+    return dq.result("dq"), dk.result("dk"), dv.result("dv")
+
+
+# -------------------------------------------------------------- small sweep
+
+SWEEP = [(n, d, c) for n in (1, 2, 3, 17, 64, 127, 128, 129, 300) for d in (64, 128) for c in (False, True)]
+
+
+def sweep_shape(N):
+    return (2, 4, 2) if N % 2 else (1, 2, 2)  # (B, Hq, Hkv): odd N also exercises GQA
+
+
+@pytest.mark.parametrize("N,d,causal", SWEEP)
+def test_fwd_small(fa, N, d, causal):
+    B, Hq, Hkv = sweep_shape(N)
+    note(f"fwd small B={B} Hq={Hq} Hkv={Hkv} N={N} d={d} causal={causal}")
+    q, k, v = random_bf16((B, Hq, N, d), N), random_bf16((B, Hkv, N, d), N + 1), random_bf16((B, Hkv, N, d), N + 2)
+    scale = 1 / math.sqrt(d)
+    o, lse = gpu_fwd(fa, q, k, v, scale, causal)
+    o_ref, lse_ref = oracle.fwd(q, k, v, scale, causal)
+    compare("o", o, o_ref)
+    compare_lse(lse, lse_ref)
+
+
+@pytest.mark.parametrize("N,d,causal", SWEEP)
+@pytest.mark.parametrize("deterministic", [0, 1])
+def test_bwd_small(fa, N, d, causal, deterministic):
+    B, Hq, Hkv = sweep_shape(N)
+    note(f"bwd small B={B} Hq={Hq} Hkv={Hkv} N={N} d={d} causal={causal} det={deterministic}")
+    q, k, v = random_bf16((B, Hq, N, d), N), random_bf16((B, Hkv, N, d), N + 1), random_bf16((B, Hkv, N, d), N + 2)
+    dout = random_bf16((B, Hq, N, d), N + 3)
+    scale = 1 / math.sqrt(d)
+    o, lse = gpu_fwd(fa, q, k, v, scale, causal)
+    dq, dk, dv = gpu_bwd(fa, q, k, v, dout, o, lse, scale, causal, deterministic)
+    ref = oracle.bwd(q, k, v, dout, scale, causal)
+    bar = MEAN_ABS if N >= 64 else MEAN_ABS_FEW_TERMS
+    compare("dq", dq, ref["dq"], bar)
+    compare("dk", dk, ref["dk"], bar)
+    compare("dv", dv, ref["dv"], bar)
+
+
+# --------------------------------------------------------- special inputs
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_zero_keys_running_mean(fa, causal):
+    """K = 0: O_i is the mean of the valid V rows (exercises masking and the
+    accumulation across tiles); LSE_i = ln(n_i)."""
+    B, H, N, d = 1, 2, 300, 128
+    note(f"zero keys causal={causal}")
+    q, v = random_bf16((B, H, N, d), 7), random_bf16((B, H, N, d), 8)
+    k = np.zeros((B, H, N, d), np.uint16)
+    o, lse = gpu_fwd(fa, q, k, v, 1 / math.sqrt(d), causal)
+    vf = (v.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    n = np.arange(1, N + 1) if causal else np.full(N, N)
+    ref = np.cumsum(vf, axis=2) / n[None, None, :, None] if causal else np.broadcast_to(vf.mean(2, keepdims=True), vf.shape)
+    compare("o", o, ref)
+    compare_lse(lse, np.broadcast_to(np.log(n), lse.shape))
+
+
+def test_first_causal_row_is_v0(fa):
+    B, H, N, d = 2, 3, 200, 64
+    note("first causal row")
+    q, k, v = random_bf16((B, H, N, d), 1), random_bf16((B, H, N, d), 2), random_bf16((B, H, N, d), 3)
+    o, _ = gpu_fwd(fa, q, k, v, 0.125, True)
+    vf = (v[:, :, 0].astype(np.uint32) << 16).view(np.float32)
+    # p = exp2(fma(s, c, -fl(s*c))) is 1 up to the rounding residual of fl(s*c)
+    np.testing.assert_allclose(o[:, :, 0], vf, rtol=1e-6, atol=0)
+
+
+@pytest.mark.parametrize("jump", [7.875, 8.125, 40.0, -30.0])
+@pytest.mark.parametrize("causal", [False, True])
+def test_planted_max_jump(fa, jump, causal):
+    """Scores of every row jump by `jump` (base-2 units) at key 160, inside the
+    third 64-key tile: below the threshold (7.875) the reference maximum must be
+    kept, above it (8.125, 40) it must move, and a drop (-30) never moves it.
+    q_i = e_0, scale * log2(e) = 1, K[:, 0] = 0 before key 160 and `jump` after."""
+    B, H, N, d = 1, 2, 320, 64
+    note(f"planted jump {jump} causal={causal}")
+    rng = np.random.default_rng(5)
+    qf = np.zeros((B, H, N, d), np.float32)
+    qf[..., 0] = 1.0
+    kf = rng.uniform(-0.25, 0.25, size=(B, H, N, d)).astype(np.float32)
+    kf[..., 0] = 0.0
+    kf[..., 160:, 0] = jump
+    q, k = f32_to_bf16_bits(qf), f32_to_bf16_bits(kf)
+    v = random_bf16((B, H, N, d), 6)
+    scale = float(np.float32(math.log(2.0)))
+    o, lse = gpu_fwd(fa, q, k, v, scale, causal)
+    o_ref, lse_ref = oracle.fwd(q, k, v, scale, causal)
+    compare("o", o, o_ref)
+    compare_lse(lse, lse_ref)
+
+
+# ---------------------------------------------------- full-size workloads
+
+def sampled_rows(w, n_rows, seed):
+    """Rows spread over every head, including the first and last row of each
+    head and rows at 64/128-row tile edges."""
+    rng = np.random.default_rng(seed)
+    BH = w.B * w.Hq
+    edges = np.array([0, 63, 64, 127, 128, w.N // 2, w.N - 129, w.N - 65, w.N - 1])
+    per = max(1, n_rows // BH)
+    rows = []
+    for bh in range(BH):
+        r = np.concatenate([edges, rng.integers(0, w.N, size=per)])
+        rows.append(bh * w.N + np.clip(r, 0, w.N - 1))
+    return np.unique(np.concatenate(rows))
+
+
+@pytest.mark.parametrize("name", ["fwd_small_d64", "fwd_n4096", "fwd_causal_rowscale_n8192",
+                                  "fwd_causal_gqa_n32768", "fwdbwd_causal_n8192"])
+def test_workload_forward(fa, name):
+    w = WORKLOADS[name]
+    note(f"workload forward {name}")
+    x = make_inputs(w)
+    o, lse = gpu_fwd(fa, x["q"], x["k"], x["v"], w.scale, w.causal)
+    assert np.isfinite(lse).all()
+    if w.B * w.Hq * w.N <= 1024:
+        o_ref, lse_ref = oracle.fwd(x["q"], x["k"], x["v"], w.scale, w.causal)
+        compare("o", o, o_ref)
+        compare_lse(lse, lse_ref)
+        return
+    rows = sampled_rows(w, 512, w.seed)
+    o_ref, lse_ref = oracle.fwd_rows(x["q"], x["k"], x["v"], w.scale, w.causal, rows)
+    compare("o (sampled rows)", o.reshape(-1, w.d)[rows], o_ref)
+    compare_lse(lse.reshape(-1)[rows], lse_ref)
+
+
+def test_workload_backward_both_modes(fa):
+    """Full-size causal backward: one key/value group per batch compared element
+    by element with the oracle in both modes; the deterministic mode must repeat
+    bit for bit; exact identities sum_j dK_j = 0 and sum_j dV_j = sum_i dO_i
+    checked on every group."""
+    w = WORKLOADS["fwdbwd_causal_n8192"]
+    note("workload backward fwdbwd_causal_n8192")
+    x = make_inputs(w)
+    o, lse = gpu_fwd(fa, x["q"], x["k"], x["v"], w.scale, w.causal)
+    groups = [0, w.B * w.Hkv - 1]
+    ref = oracle.bwd_groups(x["q"], x["k"], x["v"], x["dout"], w.scale, w.causal, groups)
+    grp = w.Hq // w.Hkv
+    results = {}
+    for det in (0, 1):
+        note(f"  deterministic={det}")
+        dq, dk, dv = gpu_bwd(fa, x["q"], x["k"], x["v"], x["dout"], o, lse, w.scale, w.causal, det)
+        results[det] = (dq, dk, dv)
+        for t, gflat in enumerate(groups):
+            b, g = divmod(gflat, w.Hkv)
+            compare(f"dq[{b},{g}]", dq[b, g * grp:(g + 1) * grp], ref["dq"][t])
+            compare(f"dk[{b},{g}]", dk[b, g], ref["dk"][t])
+            compare(f"dv[{b},{g}]", dv[b, g], ref["dv"][t])
+        dsum = dk.astype(np.float64).sum(2)
+        scale_k = np.abs(dk).astype(np.float64).sum(2)
+        note(f"  max |sum_j dK_j| / sum_j |dK_j| = {float((np.abs(dsum) / scale_k).max()):.2e}")
+        assert (np.abs(dsum) <= 1e-3 * scale_k + 1e-3).all()
+        dof = (x["dout"].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        want = dof.reshape(w.B, w.Hkv, grp, w.N, w.d).sum((2, 3))
+        err = np.abs(dv.astype(np.float64).sum(2) - want)
+        note(f"  max |sum_j dV_j - sum_i dO_i| = {float(err.max()):.2e}")
+        assert (err <= 1e-3 * np.abs(dof).reshape(w.B, w.Hkv, -1, w.d).sum(2) + 1e-2).all()
+    note("  deterministic repeat")
+    again = gpu_bwd(fa, x["q"], x["k"], x["v"], x["dout"], o, lse, w.scale, w.causal, 1)
+    for a, b_ in zip(again, results[1]):
+        assert np.array_equal(a.view(np.uint32), b_.view(np.uint32))
+    for a, b_ in zip(results[0], results[1]):
+        assert float(np.abs(a - b_).max()) <= 5e-3
