@@ -29,6 +29,13 @@
 #include "fa_launch.hpp"
 #include "fa_tiles.hpp"
 
+#ifndef FA_BWD_MIN_WAVES
+#define FA_BWD_MIN_WAVES 1  // waves per SIMD the dK/dV kernel's registers must allow
+#endif
+#ifndef FA_DQ_MIN_WAVES
+#define FA_DQ_MIN_WAVES 1   // waves per SIMD the deterministic dQ kernel's registers must allow
+#endif
+
 namespace fa {
 
 // ---------------------------------------------------------------- preprocess
@@ -93,7 +100,7 @@ struct DkdvShape {
 };
 
 template <int D, bool CAUSAL, bool ATOMIC_DQ>
-__global__ __launch_bounds__(256) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(256, FA_BWD_MIN_WAVES) void bwd_dkdv_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, const uint16_t *__restrict__ dout,
     const float *__restrict__ lse2, const float *__restrict__ delta, float *__restrict__ dq,
@@ -148,29 +155,44 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
 
     const int first_qt = CAUSAL ? kv0 / S::BM : 0;
     const int n_qt = (N + S::BM - 1) / S::BM;
+    const int steps_per_head = n_qt - first_qt;
+    const int n_steps = grp * steps_per_head;  // (query head of the group, query tile) pairs
     typename S::QTile qtile, dotile;
     float *rowbuf = reinterpret_cast<float *>(smem + S::OFF_ROW);
+    float row_l2 = INFINITY, row_dl = 0.f;  // this thread's lse2 / delta entry (tid < BM)
 
-    for (int hl = 0; hl < grp; hl++) {
-        const int hq = g * grp + hl;
+    // Global -> registers for step `st`; the loads stay in flight during the
+    // previous step's compute.
+    auto fetch = [&](int st) {
+        const int hq = g * grp + st / steps_per_head;
+        const int qs = (first_qt + st % steps_per_head) * S::BM;
+        const size_t ho = ((size_t)b * Hq + hq) * N;
+        qtile.load(q + ho * D, qs, N, tid);
+        dotile.load(dout + ho * D, qs, N, tid);
+        if (tid < S::BM) {
+            const int qi = qs + tid;
+            row_l2 = qi < N ? lse2[ho + qi] : INFINITY;  // P = 0 for rows >= N
+            row_dl = qi < N ? delta[ho + qi] : 0.f;
+        }
+    };
+    if (n_steps > 0) fetch(0);
+
+    for (int st = 0; st < n_steps; st++) {
+        const int hq = g * grp + st / steps_per_head;
+        const int qs = (first_qt + st % steps_per_head) * S::BM;
         const size_t head_off = ((size_t)b * Hq + hq) * N;
-        const uint16_t *qh = q + head_off * D;
-        const uint16_t *doh = dout + head_off * D;
-        for (int it = first_qt; it < n_qt; it++) {
-            const int qs = it * S::BM;
-            qtile.load(qh, qs, N, tid);
-            dotile.load(doh, qs, N, tid);
-            __syncthreads();  // the previous step is done with the LDS tiles
+        {
+            lds_barrier();  // every wave is done with the previous step's LDS tiles
             qtile.store_rows(smem + S::OFF_Q, tid);
             qtile.store(smem + S::OFF_QT, tid);
             dotile.store_rows(smem + S::OFF_DO, tid);
             dotile.store(smem + S::OFF_DOT, tid);
             if (tid < S::BM) {
-                const int qi = qs + tid;
-                rowbuf[tid] = qi < N ? lse2[head_off + qi] : INFINITY;       // P = 0 for rows >= N
-                rowbuf[S::BM + tid] = qi < N ? delta[head_off + qi] : 0.f;
+                rowbuf[tid] = row_l2;
+                rowbuf[S::BM + tid] = row_dl;
             }
-            __syncthreads();
+            lds_barrier();
+            if (st + 1 < n_steps) fetch(st + 1);
 
             // S = Q K^T and dP = dO V^T, rows = queries, one key column per lane.
             f32x16 sc[2], dp[2];
@@ -233,7 +255,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
                         const uint32_t off = qr * (S::BN * 2) + (((kin >> 3) ^ (qr & 7)) << 4) + (kin & 7) * 2;
                         dsl[off >> 1] = __builtin_bit_cast(uint16_t, x);
                     }
-                __syncthreads();
+                lds_barrier();
                 // dQ[BM x D] += dS[BM x BN] K[BN x D]; 2*DBLK tiles of 32x32 over 4 waves.
                 constexpr int TILES = 2 * S::DBLK;
 #pragma unroll
@@ -298,7 +320,7 @@ struct DqShape {
 };
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void bwd_dq_kernel(
+__global__ __launch_bounds__(256, FA_DQ_MIN_WAVES) void bwd_dq_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, const uint16_t *__restrict__ dout,
     const float *__restrict__ lse2, const float *__restrict__ delta, float *__restrict__ dq,

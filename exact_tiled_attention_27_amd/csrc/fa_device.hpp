@@ -19,6 +19,9 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -66,11 +69,37 @@ __device__ __forceinline__ void lds_write_u32x2(char *lds, uint32_t byte_off, u3
     *reinterpret_cast<u32x2 *>(lds + byte_off) = v;
 }
 
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// lane j names 4 consecutive 16-bit values, row j of a 16 x 4 block M; lane i
+// receives M[i/4 + 4u][i%4] for u = 0..3.  When lane j points at row
+// (r0 + j/4), columns c0 + 4*(j%4) .. +3 of a row-major matrix, lane i receives
+// column c0 + i of rows r0 .. r0+3: a 4 x 16 block transposed into registers.
+__device__ __forceinline__ i16x4 lds_read_tr16(const char *lds, uint32_t byte_off)
+{
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(lds + byte_off));
+}
+
+// Two 4-element transposed reads as one 8-element bf16 MFMA operand.
+__device__ __forceinline__ bf16x8 join_bf16x8(i16x4 lo, i16x4 hi)
+{
+    i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, v);
+}
+
 // 16-byte global load with a zero fill when the row is out of range.
 __device__ __forceinline__ u32x4 gload16(const void *base, size_t byte_off, bool ok)
 {
     u32x4 z = {0u, 0u, 0u, 0u};
     return ok ? *reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(base) + byte_off) : z;
+}
+
+// Workgroup barrier that only hands off LDS: waits for this wave's LDS
+// operations, not for its outstanding global loads, stores or atomics (a plain
+// __syncthreads() also drains those, which would stall every loop iteration on
+// the previous iteration's fire-and-forget atomics).
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // Value of lane l ^ 32 (the other half of the wave).

@@ -3,27 +3,35 @@
 // The method (FlashAttention-4 pages): walk the keys tile by tile; per tile
 // compute S = Q K^T * scale, update a running row maximum m and row sum l,
 // accumulate O += P V with P = exp(S - m), and divide by l at the end
-// ("The Asymmetric Hardware Scaling Wall", the three phases per tile; the
-// guide's simulator walks key tiles the same way).  The accumulator is only
-// renormalised when the running maximum grows by more than log2(256) = 8 in
-// the base-2 exponent domain (FlashAttention-4 summary page, Key
-// Contributions, item 2); P never goes through shared memory (the guide's
-// "Register-Level Softmax Streaming").
+// (FlashAttention-4 Guide, "The Asymmetric Hardware Scaling Wall": the three
+// phases per tile; its simulator walks key tiles the same way).  The
+// accumulator is only renormalised when the running maximum grows by more
+// than log2(256) = 8 in the base-2 exponent domain (FlashAttention-4 summary
+// page, Key Contributions, item 2); P never goes through shared memory (the
+// guide's "Register-Level Softmax Streaming").
 //
-// gfx950 mapping (one workgroup = 4 waves = BM = 128 query rows of one head):
+// gfx950 mapping (one workgroup = 4 waves = BM = 128 query rows of one head,
+// two workgroups per CU):
 //   * each wave owns 32 query rows; it computes S^T = K Q^T (keys x queries)
 //     with v_mfma_f32_32x32x16_bf16, so every lane holds one query column:
 //     row max and row sum are in-lane, plus one swap between the wave halves;
 //   * the bf16 P^T tile, still in the accumulator layout, is the B operand of
 //     O^T += V^T P^T (contraction over keys), so P stays in registers;
-//   * K is staged to LDS row-major, V transposed with its keys permuted to
-//     the order the P^T registers present (see key_pos16); both are
-//     double-buffered and XOR-swizzled so the 16-byte MFMA operand reads are
-//     free of bank conflicts;
-//   * queries and scores use the base-2 domain: x = s * (scale * log2 e) - m.
+//   * K and V tiles are staged to LDS row-major, double-buffered and
+//     XOR-swizzled; the V^T operand is read with transposing LDS loads
+//     (ds_read_b64_tr_b16) in exactly the key order the P^T registers present;
+//   * tiles that need no mask (all keys < N and, when causal, all keys <= the
+//     workgroup's first query) run a loop body compiled without mask code;
+//   * scores use the base-2 domain: x = s * (scale * log2 e) - m.
+#include <type_traits>
+
 #include "fa_device.hpp"
 #include "fa_launch.hpp"
 #include "fa_tiles.hpp"
+
+#ifndef FA_FWD_MIN_WAVES
+#define FA_FWD_MIN_WAVES 2  // waves per SIMD the register allocation must allow
+#endif
 
 namespace fa {
 
@@ -36,20 +44,18 @@ struct FwdShape {
     static constexpr int DBLK = D / 32;      // 32-row blocks of O^T
     static constexpr int NKB = BN / 32;      // 32-key blocks of S^T
     static constexpr int KVSTEPS = BN / 16;  // k-steps of O^T += V^T P^T
-    using KTile = RowTile<BN, D, THREADS>;         // K row-major
-    using VTile = ColTile<BN, D, THREADS, true>;   // V transposed, keys in key_pos16 order
+    using KTile = RowTile<BN, D, THREADS>;
+    using VTile = RowTile<BN, D, THREADS, true>;
     static constexpr int K_BYTES = KTile::BYTES;
     static constexpr int BUF_BYTES = KTile::BYTES + VTile::BYTES;
     static constexpr int LDS_BYTES = 2 * BUF_BYTES;
 };
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void fwd_kernel(const uint16_t *__restrict__ q,
-                                                  const uint16_t *__restrict__ k,
-                                                  const uint16_t *__restrict__ v,
-                                                  float *__restrict__ o, float *__restrict__ lse,
-                                                  int Hq, int Hkv, int N, int BH, int QT,
-                                                  float scale_log2, float tau)
+__global__ __launch_bounds__(256, FA_FWD_MIN_WAVES) void fwd_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
+    const uint16_t *__restrict__ v, float *__restrict__ o, float *__restrict__ lse, int Hq,
+    int Hkv, int N, int BH, int QT, float scale_log2, float tau)
 {
     using S = FwdShape<D>;
     extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -57,14 +63,15 @@ __global__ __launch_bounds__(256) void fwd_kernel(const uint16_t *__restrict__ q
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int h = lane >> 5, col = lane & 31;
+    const int g16 = lane >> 4, r16 = lane & 15;  // 16-lane group and lane within it
 
     int bh, qt;
     xcd_tile_map(blockIdx.x, BH, QT, CAUSAL, bh, qt);
     const int b = bh / Hq, hq = bh % Hq;
     const int g = hq / (Hq / Hkv);
     const int q0 = qt * S::BM;
-    const int qw0 = q0 + wave * 32;       // first query row of this wave
-    const int qrow = qw0 + col;           // the query column this lane owns
+    const int qw0 = q0 + wave * 32;  // first query row of this wave
+    const int qrow = qw0 + col;      // the query column this lane owns
 
     const uint16_t *qh = q + ((size_t)b * Hq + hq) * N * D;
     const uint16_t *kh = k + ((size_t)b * Hkv + g) * N * D;
@@ -73,35 +80,39 @@ __global__ __launch_bounds__(256) void fwd_kernel(const uint16_t *__restrict__ q
     // Q^T as B operand: lane holds Q[qrow][16 s + 8 h .. +7].
     bf16x8 qf[S::KSTEPS];
 #pragma unroll
-    for (int s = 0; s < S::KSTEPS; s++) {
-        u32x4 raw = gload16(qh, ((size_t)qrow * D + 16 * s + 8 * h) * 2, qrow < N);
-        qf[s] = __builtin_bit_cast(bf16x8, raw);
-    }
+    for (int s = 0; s < S::KSTEPS; s++)
+        qf[s] = __builtin_bit_cast(bf16x8, gload16(qh, ((size_t)qrow * D + 16 * s + 8 * h) * 2, qrow < N));
 
-    // Per-lane LDS byte offsets of the MFMA A operands: K row kb*32 + col,
-    // chunk 2s + h; V^T row 32*db + col, chunk 2ks + h.  Row offsets that are
-    // multiples of 8 rows leave the swizzle unchanged except for bit 2 of the
-    // V^T row group, so only db & 1 needs its own offset.
+    // LDS byte offsets.  K (A operand of S^T): row kb*32 + col, chunk 2s + h;
+    // the swizzle only sees row & 15, so kb*32 rows are an immediate offset.
     uint32_t koff[S::KSTEPS];
 #pragma unroll
     for (int s = 0; s < S::KSTEPS; s++) koff[s] = row_tile_off(col, 2 * s + h, D);
-    uint32_t voff[S::KVSTEPS][2];
+    // V (A operand of O^T via transposing reads): lane (g16, r16) of read rho
+    // of k-step ks points at key 16 ks + 8 rho + 4 h + r16/4, columns
+    // 32 db + 16 (g16 & 1) + 4 (r16 & 3) .. +3.  The swizzle depends on the key
+    // only through 4 h + r16/4, so ks and rho are immediate offsets.
+    uint32_t voff[S::DBLK];
 #pragma unroll
-    for (int ks = 0; ks < S::KVSTEPS; ks++)
-#pragma unroll
-        for (int p = 0; p < 2; p++) voff[ks][p] = col_tile_off<S::BN>(32 * p + col, 2 * ks + h);
+    for (int db = 0; db < S::DBLK; db++) {
+        const int key = 4 * h + (r16 >> 2);
+        const int chunk = 4 * db + 2 * (g16 & 1) + ((r16 & 3) >> 1);
+        voff[db] = vtile_off(key, chunk, D) + 8 * (r16 & 1);
+    }
 
     f32x16 acc[S::DBLK];
 #pragma unroll
     for (int db = 0; db < S::DBLK; db++)
 #pragma unroll
         for (int r = 0; r < 16; r++) acc[db][r] = 0.f;
-    float m_ref = -INFINITY;  // reference maximum (base-2 domain) used by the exponent
+    float m_ref = -INFINITY;  // reference maximum (base-2 domain) the exponent subtracts
     float l_part = 0.f;       // this lane's part of the row sum
 
     const int n_tiles_all = (N + S::BN - 1) / S::BN;
     const int n_tiles = CAUSAL ? min(n_tiles_all, (min(q0 + S::BM, N) + S::BN - 1) / S::BN)
                                : n_tiles_all;
+    // Tiles every key of which is < N and (causal) <= q0 need no mask.
+    const int n_full = CAUSAL ? min(N / S::BN, (q0 + 1) / S::BN) : N / S::BN;
 
     typename S::KTile kst;
     typename S::VTile vst;
@@ -111,33 +122,35 @@ __global__ __launch_bounds__(256) void fwd_kernel(const uint16_t *__restrict__ q
     vst.store(smem + S::K_BYTES, tid);
     __syncthreads();
 
-    for (int t = 0; t < n_tiles; t++) {
+    auto step = [&](auto masked, int t) {
+        constexpr bool MASK = decltype(masked)::value;
         const int key0 = t * S::BN;
         const bool more = t + 1 < n_tiles;
         if (more) {
-            kst.load(kh, key0 + S::BN, N, tid);
-            vst.load(vh, key0 + S::BN, N, tid);
+            const int nk = key0 + S::BN;
+            if (nk + S::BN <= N) {
+                kst.load_full(kh, nk, tid);
+                vst.load_full(vh, nk, tid);
+            } else {
+                kst.load(kh, nk, N, tid);
+                vst.load(vh, nk, N, tid);
+            }
         }
         const char *kl = smem + (t & 1) * S::BUF_BYTES;
         const char *vl = kl + S::K_BYTES;
 
         // Waves whose rows all precede this tile see only masked keys: skip.
-        if (!CAUSAL || key0 <= qw0 + 31) {
-            // S^T = K Q^T for the tile's 32-key blocks.
+        if (!MASK || !CAUSAL || key0 <= qw0 + 31) {
             f32x16 st[S::NKB];
 #pragma unroll
             for (int kb = 0; kb < S::NKB; kb++) {
 #pragma unroll
                 for (int r = 0; r < 16; r++) st[kb][r] = 0.f;
 #pragma unroll
-                for (int s = 0; s < S::KSTEPS; s++) {
-                    bf16x8 a = lds_read_bf16x8(kl, koff[s] + kb * 32 * D * 2);
-                    st[kb] = mfma32(a, qf[s], st[kb]);
-                }
+                for (int s = 0; s < S::KSTEPS; s++)
+                    st[kb] = mfma32(lds_read_bf16x8(kl, koff[s] + kb * 32 * D * 2), qf[s], st[kb]);
             }
-            // Mask keys past N and, when causal, keys after the query.
-            const bool need_mask = (key0 + S::BN > N) || (CAUSAL && key0 + S::BN - 1 > qw0);
-            if (need_mask) {
+            if (MASK) {
 #pragma unroll
                 for (int kb = 0; kb < S::NKB; kb++)
 #pragma unroll
@@ -186,11 +199,12 @@ __global__ __launch_bounds__(256) void fwd_kernel(const uint16_t *__restrict__ q
 
             // O^T += V^T P^T.
 #pragma unroll
-            for (int db = 0; db < S::DBLK; db++)
+            for (int ks = 0; ks < S::KVSTEPS; ks++)
 #pragma unroll
-                for (int ks = 0; ks < S::KVSTEPS; ks++) {
-                    bf16x8 a = lds_read_bf16x8(vl, voff[ks][db & 1] + (db >> 1) * 64 * S::BN * 2);
-                    acc[db] = mfma32(a, pf[ks], acc[db]);
+                for (int db = 0; db < S::DBLK; db++) {
+                    const i16x4 lo = lds_read_tr16(vl, voff[db] + (16 * ks) * D * 2);
+                    const i16x4 hi = lds_read_tr16(vl, voff[db] + (16 * ks + 8) * D * 2);
+                    acc[db] = mfma32(join_bf16x8(lo, hi), pf[ks], acc[db]);
                 }
         }
 
@@ -200,7 +214,11 @@ __global__ __launch_bounds__(256) void fwd_kernel(const uint16_t *__restrict__ q
             vst.store(nb + S::K_BYTES, tid);
         }
         __syncthreads();
-    }
+    };
+
+    int t = 0;
+    for (; t < n_full; t++) step(std::false_type{}, t);
+    for (; t < n_tiles; t++) step(std::true_type{}, t);
 
     // Epilogue: O = O / l, LSE = (m + log2 l) * ln 2.
     const float l_tot = l_part + swap_halves(l_part);

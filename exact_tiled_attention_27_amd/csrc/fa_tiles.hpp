@@ -3,8 +3,15 @@
 // Two LDS layouts, both read by MFMA operand loads of 16 bytes (8 bf16):
 //
 //  RowTile: row-major [ROWS][D].  The 16-byte chunk c of row r is stored at
-//    chunk c ^ (r & 7).  A wave reading the same chunk of 32 consecutive rows
-//    then touches 8 distinct chunk slots per 8 rows: no bank conflicts.
+//    chunk c ^ (r & 15) when D = 128 (c ^ (r & 7) when D = 64).  Sixteen
+//    lanes reading the same chunk of 16 consecutive rows then hit 16 distinct
+//    16-byte bank groups, which keeps 16-byte reads conflict-free whether the
+//    LDS serves 8 or 16 lanes of them per clock.
+//
+//  VTile: row-major [ROWS][D] read with transposing 8-byte loads
+//    (ds_read_b64_tr_b16): 16 lanes read 4 consecutive rows x 32 bytes.  The
+//    chunk c of row r is stored at chunk c ^ (2 * (r & 7)) (D = 128) so the
+//    4 rows land on 4 distinct 32-byte bank groups.
 //
 //  ColTile: transposed [D][ROWS] (one LDS row per head-dimension index d).
 //    Sequence positions inside each group of 16 are stored either in natural
@@ -25,7 +32,17 @@ namespace fa {
 
 __device__ __forceinline__ uint32_t row_tile_off(int row, int chunk, int D)
 {
-    return row * (D * 2) + ((chunk ^ (row & 7)) << 4);
+    return row * (D * 2) + ((chunk ^ (row & (D == 128 ? 15 : 7))) << 4);
+}
+
+__device__ __forceinline__ int vtile_swz(int row, int D)
+{
+    return D == 128 ? 2 * (row & 7) : 2 * (row & 3);
+}
+
+__device__ __forceinline__ uint32_t vtile_off(int row, int chunk, int D)
+{
+    return row * (D * 2) + ((chunk ^ vtile_swz(row, D)) << 4);
 }
 
 __device__ __forceinline__ int col_swz(int d) { return (d & 7) ^ ((d >> 3) & 7); }
@@ -36,7 +53,7 @@ __device__ __forceinline__ uint32_t col_tile_off(int d, int chunk)
     return d * (ROWS * 2) + ((chunk ^ col_swz(d)) << 4);
 }
 
-template <int ROWS, int D, int THREADS>
+template <int ROWS, int D, int THREADS, bool VSWZ = false>
 struct RowTile {
     static constexpr int CPR = D / 8;  // 16-byte chunks per row
     static constexpr int TOTAL = ROWS * CPR;
@@ -51,17 +68,27 @@ struct RowTile {
             const int item = tid + i * THREADS;
             const int row = item / CPR, c = item % CPR;
             const int n = row0 + row;
-            x[i] = gload16(head, ((size_t)n * D + c * 8) * 2, item < TOTAL && n < N);
+            x[i] = gload16(head, ((size_t)n * D + c * 8) * 2, (TOTAL % THREADS == 0 || item < TOTAL) && n < N);
         }
+    }
+    // Rows row0 .. row0 + ROWS - 1 all < N: no guards, one uniform base.
+    __device__ __forceinline__ void load_full(const uint16_t *head, int row0, int tid)
+    {
+        static_assert(TOTAL % THREADS == 0, "full loads need whole items per thread");
+        const char *base = reinterpret_cast<const char *>(head) + (size_t)row0 * D * 2;
+        const uint32_t toff = ((tid / CPR) * D + (tid % CPR) * 8) * 2;
+#pragma unroll
+        for (int i = 0; i < ITEMS; i++)
+            x[i] = *reinterpret_cast<const u32x4 *>(base + toff + i * (THREADS / CPR) * D * 2);
     }
     __device__ __forceinline__ void store(char *lds, int tid) const
     {
 #pragma unroll
         for (int i = 0; i < ITEMS; i++) {
             const int item = tid + i * THREADS;
-            if (item < TOTAL) {
+            if (TOTAL % THREADS == 0 || item < TOTAL) {
                 const int row = item / CPR, c = item % CPR;
-                lds_write_u32x4(lds, row_tile_off(row, c, D), x[i]);
+                lds_write_u32x4(lds, VSWZ ? vtile_off(row, c, D) : row_tile_off(row, c, D), x[i]);
             }
         }
     }
@@ -81,7 +108,7 @@ struct ColTile {
         for (int i = 0; i < ITEMS; i++) {
             const int item = tid + i * THREADS;
             const int e = item % CPR, a = item / CPR;
-            const bool live = item < TOTAL;
+            const bool live = TOTAL % THREADS == 0 || item < TOTAL;
 #pragma unroll
             for (int q = 0; q < 4; q++) {
                 const int n = row0 + 4 * a + q;
@@ -95,7 +122,7 @@ struct ColTile {
 #pragma unroll
         for (int i = 0; i < ITEMS; i++) {
             const int item = tid + i * THREADS;
-            if (item < TOTAL) {
+            if (TOTAL % THREADS == 0 || item < TOTAL) {
                 const int e = item % CPR, a = item / CPR;
                 const int kk = 4 * a;
                 const int pos = PERM ? ((kk & ~15) | key_pos16(kk & 15)) : kk;
@@ -121,7 +148,7 @@ struct ColTile {
 #pragma unroll
         for (int i = 0; i < ITEMS; i++) {
             const int item = tid + i * THREADS;
-            if (item < TOTAL) {
+            if (TOTAL % THREADS == 0 || item < TOTAL) {
                 const int e = item % CPR, a = item / CPR;
 #pragma unroll
                 for (int q = 0; q < 4; q++)
