@@ -44,8 +44,8 @@ struct FwdShape {
     static constexpr int DBLK = D / 32;      // 32-row blocks of O^T
     static constexpr int NKB = BN / 32;      // 32-key blocks of S^T
     static constexpr int KVSTEPS = BN / 16;  // k-steps of O^T += V^T P^T
-    using KTile = RowTile<BN, D, THREADS>;
-    using VTile = RowTile<BN, D, THREADS, true>;
+    using KTile = DmaTile<BN, D, THREADS, false>;  // row-major K, RowTile swizzle
+    using VTile = DmaTile<BN, D, THREADS, true>;   // row-major V, VTile swizzle
     static constexpr int K_BYTES = KTile::BYTES;
     static constexpr int BUF_BYTES = KTile::BYTES + VTile::BYTES;
     static constexpr int LDS_BYTES = 2 * BUF_BYTES;
@@ -116,40 +116,43 @@ __global__ __launch_bounds__(256, FA_FWD_MIN_WAVES) void fwd_kernel(
 
     typename S::KTile kst;
     typename S::VTile vst;
-    kst.load(kh, 0, N, tid);
-    vst.load(vh, 0, N, tid);
-    kst.store(smem, tid);
-    vst.store(smem + S::K_BYTES, tid);
-    __syncthreads();
+    kst.init(wave, lane);
+    vst.init(wave, lane);
+    auto issue = [&](int tile, char *buf) {
+        const int r0 = tile * S::BN;
+        if (r0 + S::BN <= N) {
+            kst.issue_full(kh, r0, buf, wave);
+            vst.issue_full(vh, r0, buf + S::K_BYTES, wave);
+        } else {
+            kst.issue_tail(kh, r0, N, buf, wave);
+            vst.issue_tail(vh, r0, N, buf + S::K_BYTES, wave);
+        }
+    };
+    issue(0, smem);
+    dma_barrier();
 
     auto step = [&](auto masked, int t) {
         constexpr bool MASK = decltype(masked)::value;
         const int key0 = t * S::BN;
-        const bool more = t + 1 < n_tiles;
-        if (more) {
-            const int nk = key0 + S::BN;
-            if (nk + S::BN <= N) {
-                kst.load_full(kh, nk, tid);
-                vst.load_full(vh, nk, tid);
-            } else {
-                kst.load(kh, nk, N, tid);
-                vst.load(vh, nk, N, tid);
-            }
-        }
+        // The buffer for tile t + 1 was last read in step t - 1, which every
+        // wave has finished (barrier at the end of that step).
+        if (t + 1 < n_tiles) issue(t + 1, smem + ((t + 1) & 1) * S::BUF_BYTES);
         const char *kl = smem + (t & 1) * S::BUF_BYTES;
         const char *vl = kl + S::K_BYTES;
 
         // Waves whose rows all precede this tile see only masked keys: skip.
         if (!MASK || !CAUSAL || key0 <= qw0 + 31) {
+            // k-step outer: each step's two K reads feed two independent chains.
             f32x16 st[S::NKB];
 #pragma unroll
-            for (int kb = 0; kb < S::NKB; kb++) {
+            for (int kb = 0; kb < S::NKB; kb++)
 #pragma unroll
                 for (int r = 0; r < 16; r++) st[kb][r] = 0.f;
 #pragma unroll
-                for (int s = 0; s < S::KSTEPS; s++)
+            for (int s = 0; s < S::KSTEPS; s++)
+#pragma unroll
+                for (int kb = 0; kb < S::NKB; kb++)
                     st[kb] = mfma32(lds_read_bf16x8(kl, koff[s] + kb * 32 * D * 2), qf[s], st[kb]);
-            }
             if (MASK) {
 #pragma unroll
                 for (int kb = 0; kb < S::NKB; kb++)
@@ -208,12 +211,7 @@ __global__ __launch_bounds__(256, FA_FWD_MIN_WAVES) void fwd_kernel(
                 }
         }
 
-        if (more) {
-            char *nb = smem + ((t + 1) & 1) * S::BUF_BYTES;
-            kst.store(nb, tid);
-            vst.store(nb + S::K_BYTES, tid);
-        }
-        __syncthreads();
+        dma_barrier();  // tile t + 1 has landed in LDS; tile t is no longer read
     };
 
     int t = 0;

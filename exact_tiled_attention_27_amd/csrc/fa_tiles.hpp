@@ -9,9 +9,12 @@
 //    LDS serves 8 or 16 lanes of them per clock.
 //
 //  VTile: row-major [ROWS][D] read with transposing 8-byte loads
-//    (ds_read_b64_tr_b16): 16 lanes read 4 consecutive rows x 32 bytes.  The
-//    chunk c of row r is stored at chunk c ^ (2 * (r & 7)) (D = 128) so the
-//    4 rows land on 4 distinct 32-byte bank groups.
+//    (ds_read_b64_tr_b16): each 16-lane group reads 4 consecutive rows x 32
+//    bytes, and the two groups of a 32-lane half read the same 4 rows 32 bytes
+//    apart.  The chunk c of row r is stored at chunk c ^ (4 * (r & 3))
+//    (D = 128): the 4 rows of one group land on 4 distinct 32-byte bank groups
+//    and the two groups on disjoint ones, so the 32 lanes the LDS serves per
+//    clock (256 bytes over 64 banks) never collide.
 //
 //  ColTile: transposed [D][ROWS] (one LDS row per head-dimension index d).
 //    Sequence positions inside each group of 16 are stored either in natural
@@ -37,7 +40,7 @@ __device__ __forceinline__ uint32_t row_tile_off(int row, int chunk, int D)
 
 __device__ __forceinline__ int vtile_swz(int row, int D)
 {
-    return D == 128 ? 2 * (row & 7) : 2 * (row & 3);
+    return D == 128 ? 4 * (row & 3) : 2 * (row & 3);
 }
 
 __device__ __forceinline__ uint32_t vtile_off(int row, int chunk, int D)
@@ -51,6 +54,84 @@ template <int ROWS>
 __device__ __forceinline__ uint32_t col_tile_off(int d, int chunk)
 {
     return d * (ROWS * 2) + ((chunk ^ col_swz(d)) << 4);
+}
+
+__device__ __forceinline__ int row_swz(int row, int D) { return row & (D == 128 ? 15 : 7); }
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// 16-byte global -> LDS copy (global_load_lds_dwordx4; LDS base wave-uniform).
+// The builtin exists only for the device target; the host pass, which only
+// needs the kernels' launch stubs, must not see it (when it does, clang drops
+// some template instantiations of the kernels from the host object).
+__device__ __forceinline__ void lds_dma16(const void *src, lds_void_t *dst)
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+#else
+    (void)src;
+    (void)dst;
+#endif
+}
+
+// HBM -> LDS staging without registers (global_load_lds_dwordx4).  One wave
+// instruction writes 1 KB of LDS: lane L's 16 bytes land at base + 16 L.  Each
+// lane therefore fetches the logical chunk that the swizzled layout (RowTile
+// or VTile) stores at that position: physical chunk p of row r holds logical
+// chunk p ^ swz(r).  The tile's 1 KB blocks are split evenly over the waves;
+// the per-lane byte offsets inside a tile are fixed, so a full tile costs no
+// address arithmetic beyond one uniform base.  Completion is tracked by vmcnt.
+template <int ROWS, int D, int THREADS, bool VSWZ>
+struct DmaTile {
+    static constexpr int CPR = D / 8;                // 16-byte chunks per row
+    static constexpr int BLOCKS = ROWS * CPR / 64;   // 1 KB blocks in the tile
+    static constexpr int WAVES = THREADS / 64;
+    static constexpr int PER_WAVE = BLOCKS / WAVES;
+    static constexpr int BYTES = ROWS * D * 2;
+    static_assert(BLOCKS % WAVES == 0, "tile must split evenly over the waves");
+    uint32_t goff[PER_WAVE];  // byte offset of this lane's source chunk inside the tile
+    int grow[PER_WAVE];       // tile row this lane fills for each block
+
+    __device__ __forceinline__ void init(int wave, int lane)
+    {
+#pragma unroll
+        for (int i = 0; i < PER_WAVE; i++) {
+            const int pos = (wave * PER_WAVE + i) * 64 + lane;
+            const int row = pos / CPR, pc = pos % CPR;
+            const int c = pc ^ (VSWZ ? vtile_swz(row, D) : row_swz(row, D));
+            grow[i] = row;
+            goff[i] = (row * D + c * 8) * 2;
+        }
+    }
+    // All ROWS rows from row0 are < N.
+    __device__ __forceinline__ void issue_full(const uint16_t *head, int row0, char *lds,
+                                               int wave) const
+    {
+        const char *base = reinterpret_cast<const char *>(head) + (size_t)row0 * D * 2;
+#pragma unroll
+        for (int i = 0; i < PER_WAVE; i++)
+            lds_dma16(base + goff[i], (lds_void_t *)(lds + (wave * PER_WAVE + i) * 1024));
+    }
+    // Tail tile: rows >= N re-read row N - 1 (finite data the caller masks).
+    __device__ __forceinline__ void issue_tail(const uint16_t *head, int row0, int N, char *lds,
+                                               int wave) const
+    {
+#pragma unroll
+        for (int i = 0; i < PER_WAVE; i++) {
+            const int n = min(row0 + grow[i], N - 1);
+            const uint32_t within = goff[i] - grow[i] * D * 2;
+            const char *src = reinterpret_cast<const char *>(head) + (size_t)n * D * 2 + within;
+            lds_dma16(src, (lds_void_t *)(lds + (wave * PER_WAVE + i) * 1024));
+        }
+    }
+};
+
+// Wait for this wave's outstanding global loads (including loads into LDS)
+// and LDS operations, then meet the workgroup: afterwards every wave's
+// direct-to-LDS tile is complete and visible.
+__device__ __forceinline__ void dma_barrier()
+{
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 template <int ROWS, int D, int THREADS, bool VSWZ = false>
