@@ -23,6 +23,37 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA peak (published)
 PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+
+
+def kernel_source_sha256():
+    """Hash of the kernel sources, to tell whether stored counters still apply."""
+    import hashlib
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "exact_tiled_attention_27_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        if f.endswith((".hip", ".hpp", ".cpp")):
+            h.update(f.encode())
+            with open(os.path.join(d, f), "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernels, workload):
+    """HBM bytes per launch (read + write) of `kernels` from the rocprofv3
+    FETCH_SIZE / WRITE_SIZE passes stored in profiles/, or None when they were
+    taken on another workload or before the kernel sources last changed."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("workload") != workload or t.get("source_sha256") != kernel_source_sha256():
+        return None
+    try:
+        return sum(t["kernels"][k]["read_bytes"] + t["kernels"][k]["write_bytes"] for k in kernels)
+    except KeyError:
+        return None
 
 
 def parse():
@@ -34,6 +65,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--extra", action="store_true",
                    help="also time the deterministic backward (reported under parts)")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="run one 256 MiB device-to-device copy before the timed region "
+                        "(reference kernel for scaling HBM byte counters)")
     return p.parse_args()
 
 
@@ -88,6 +122,12 @@ def main():
 
     print(f"bench: workload {w.name} ({w.note}); warmup {args.warmup}, steps {args.steps}",
           file=sys.stderr, flush=True)
+    if args.copy_calibration:
+        src = torch.ones(64 * 1024 * 1024, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
         fwd()
         bwd(0)
@@ -139,32 +179,36 @@ def main():
     # Roofline of the dominant launch: the forward kernel is one launch per
     # fa_fwd; fa_bwd (atomic mode) is a short preprocess kernel plus the dK/dV
     # kernel that carries all backward MFMA work.
+    cz = "true" if w.causal else "false"
     if parts["fwd_ms_avg"] >= parts["bwd_atomic_ms_avg"]:
-        rl_name, rl_flops, rl_ms = "fa::fwd_kernel", f_fwd, parts["fwd_ms_avg"]
+        rl_kernels = [f"fa::fwd_kernel<{d}, {cz}>"]
+        rl_flops, rl_ms = f_fwd, parts["fwd_ms_avg"]
     else:
-        rl_name, rl_flops, rl_ms = "fa_bwd (bwd_pre_kernel + bwd_dkdv_kernel)", f_bwd, parts["bwd_atomic_ms_avg"]
+        rl_kernels = [f"fa::bwd_pre_kernel<{d}>", f"fa::bwd_dkdv_kernel<{d}, {cz}, true>"]
+        rl_flops, rl_ms = f_bwd, parts["bwd_atomic_ms_avg"]
     achieved = rl_flops / (rl_ms * 1e-3) / 1e12
-    roofline = {"bound": "mfma", "kernel": rl_name, "achieved": achieved,
+    roofline = {"bound": "mfma", "kernel": " + ".join(rl_kernels), "achieved": achieved,
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                "traffic": None, "flops_per_launch": rl_flops, "avg_launch_ms": rl_ms}
+                "traffic": measured_traffic(rl_kernels, w.name), "traffic_unit": "bytes",
+                "flops_per_launch": rl_flops, "avg_launch_ms": rl_ms}
 
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
         threads = oracle.default_threads()
-        # Sample: the forward and backward of one (batch, head) pair.
-        groups = [0]
+        # Sample: the forward and backward of the first 16 (batch, kv-head)
+        # groups, about 10 s on 16 host cores.
+        groups = list(range(min(16, B * Hkv)))
         t0 = time.perf_counter()
         oracle.bwd_groups(x["q"], x["k"], x["v"], x["dout"], w.scale, w.causal, groups,
                           threads=threads)
         secs = time.perf_counter() - t0
-        grp = Hq // Hkv
-        frac = grp / (B * Hq)
-        sample_flops = (f_fwd + f_bwd) * frac
+        heads = len(groups) * (Hq // Hkv)
+        sample_flops = (f_fwd + f_bwd) * heads / (B * Hq)
         cpu = {"value": sample_flops / secs / 1e12, "unit": "TFLOP/s", "cores": threads,
                "kind": "oracle",
-               "sample": f"fp64 forward+backward of {grp} of {B * Hq} heads "
-                         f"(N={N}, d={d}); {secs:.1f} s"}
+               "sample": f"fp64 forward+backward of {heads} of {B * Hq} heads "
+                         f"(N={N}, d={d}, same inputs); {secs:.1f} s"}
 
     out = {
         "metric": "attention fwd/bwd TFLOP/s (bf16, d=128) and % of MI355X bf16 MFMA peak",
