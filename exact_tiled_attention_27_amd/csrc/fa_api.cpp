@@ -27,6 +27,9 @@ int check_common(int B, int Hq, int Hkv, int N, int d, float scale)
 
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Backward workspace rows: every head's rows padded to a multiple of 64.
+size_t workspace_rows(int B, int Hq, int N) { return (size_t)B * Hq * (size_t)((N + 63) & ~63); }
+
 int hip_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
 
 }  // namespace
@@ -65,8 +68,7 @@ size_t fa_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d, int determin
 {
     (void)deterministic;
     if (check_common(B, Hq, Hkv, N, d, 1.0f) != FA_OK) return 0;
-    const size_t rows = (size_t)B * Hq * N;
-    return 2 * round256(rows * sizeof(float));
+    return 2 * round256(workspace_rows(B, Hq, N) * sizeof(float));
 }
 
 int fa_bwd(const void *q, const void *k, const void *v, const float *o, const float *lse,
@@ -83,7 +85,7 @@ int fa_bwd(const void *q, const void *k, const void *v, const float *o, const fl
     const size_t need = fa_bwd_workspace_bytes(B, Hq, Hkv, N, d, deterministic);
     if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
     if (!aligned16(workspace)) return FA_ERR_ALIGN;
-    const size_t rows = (size_t)B * Hq * N;
+    const size_t rows = workspace_rows(B, Hq, N);
     float *delta = reinterpret_cast<float *>(workspace);
     float *lse2 = reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) +
                                             round256(rows * sizeof(float)));

@@ -7,20 +7,25 @@
 //   D_i  = sum_c dO_ic O_ic           dS_ij = P_ij (dP_ij - D_i)
 //   dK_j = scale * sum_i dS_ij q_i    dQ_i  = scale * sum_j dS_ij k_j
 // dQ is summed with fp32 global atomic adds, or in a separate pass that owns
-// each dQ row (reproducible), the trade the FlashAttention-4 summary page
+// each dQ row (reproducible): the trade the FlashAttention-4 summary page
 // describes under Limitations (deterministic backward) and Key Contributions
 // item 3 (fewer dQ atomics).
 //
 // Kernels (all on the caller's stream, in order):
-//   1. bwd_pre:   D_i, LSE_i * log2(e) per row; zero dQ in atomic mode.
+//   1. bwd_pre:   D_i and LSE_i * log2(e) per row into a workspace padded to
+//                 64 rows per head (padding rows: D = 0, LSE2 = +inf, so
+//                 P = 0); zero dQ in atomic mode.
 //   2. bwd_dkdv:  one workgroup per (batch, kv head, 128 keys); each of the 4
 //                 waves keeps 32 keys' K and V in registers and dK^T, dV^T
 //                 accumulators, and walks 64-query tiles of every query head
-//                 of the group.  S = Q K^T and dP = dO V^T put one key per lane
-//                 (accumulator layout), so P and dS feed dV^T += dO^T P and
-//                 dK^T += Q^T dS as B operands straight from registers.  In
-//                 atomic mode dS goes through LDS and the workgroup adds
-//                 dS K into dQ with global atomics.
+//                 of the group.  Q and dO tiles arrive in LDS by
+//                 direct-to-LDS loads, double-buffered; S = Q K^T and
+//                 dP = dO V^T read them row-wise, dV^T += dO^T P and
+//                 dK^T += Q^T dS read them with transposing loads, and P, dS
+//                 stay in registers as B operands.  In atomic mode dS goes to
+//                 LDS and the workgroup adds dS K into dQ with fp32 atomics one
+//                 step later, so the atomics are long finished when a step
+//                 waits for its loads.
 //   3. bwd_dq:    (deterministic mode) one workgroup per (batch, query head,
 //                 128 queries) walks the key tiles, recomputes S^T, P^T,
 //                 dP^T = V dO^T, dS^T, and accumulates dQ^T += K^T dS^T in
@@ -29,14 +34,14 @@
 #include "fa_launch.hpp"
 #include "fa_tiles.hpp"
 
-#ifndef FA_BWD_MIN_WAVES
-#define FA_BWD_MIN_WAVES 1  // waves per SIMD the dK/dV kernel's registers must allow
-#endif
 #ifndef FA_DQ_MIN_WAVES
-#define FA_DQ_MIN_WAVES 1   // waves per SIMD the deterministic dQ kernel's registers must allow
+#define FA_DQ_MIN_WAVES 2   // waves per SIMD the deterministic dQ kernel's registers must allow
 #endif
 
 namespace fa {
+
+// Rows per head in the backward workspace (D, LSE2): N rounded up to 64.
+__host__ __device__ inline int pad_rows(int N) { return (N + 63) & ~63; }
 
 // ---------------------------------------------------------------- preprocess
 template <int D>
@@ -45,14 +50,19 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t *__restrict
                                                       const float *__restrict__ lse,
                                                       float *__restrict__ delta,
                                                       float *__restrict__ lse2,
-                                                      float *__restrict__ dq, size_t rows,
+                                                      float *__restrict__ dq, int BH, int N,
                                                       int zero_dq)
 {
     constexpr int TPR = D / 8;  // threads per row, 8 elements each
-    const size_t row = (size_t)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
+    const int NP = pad_rows(N);
+    const size_t prow = (size_t)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;  // padded row
     const int part = threadIdx.x % TPR;
+    const bool in_range = prow < (size_t)BH * NP;
+    const int i = (int)(prow % NP);
+    const size_t row = (prow / NP) * N + i;  // row of the [B, Hq, N] tensors
+    const bool live = in_range && i < N;
     float acc = 0.f;
-    if (row < rows) {
+    if (live) {
         const size_t base = row * D + part * 8;
         const u32x4 raw = *reinterpret_cast<const u32x4 *>(dout + base);
         const f32x4 o0 = *reinterpret_cast<const f32x4 *>(o + base);
@@ -73,9 +83,9 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t *__restrict
     }
 #pragma unroll
     for (int m = 1; m < TPR; m <<= 1) acc += __shfl_xor(acc, m, 64);
-    if (row < rows && part == 0) {
-        delta[row] = acc;
-        lse2[row] = lse[row] * kLog2e;
+    if (in_range && part == 0) {
+        delta[prow] = live ? acc : 0.f;
+        lse2[prow] = live ? lse[row] * kLog2e : INFINITY;
     }
 }
 
@@ -87,20 +97,20 @@ struct DkdvShape {
     static constexpr int THREADS = 256;
     static constexpr int KSTEPS = D / 16;
     static constexpr int DBLK = D / 32;
-    using QTile = ColTile<BM, D, THREADS, true>;     // Q^T (and Q row-major from the same registers)
-    using KTile = ColTile<BN, D, THREADS, false>;    // K^T, natural key order (dQ = dS K)
-    static constexpr int OFF_Q = 0;                          // Q   row-major [BM][D]
-    static constexpr int OFF_QT = OFF_Q + BM * D * 2;        // Q^T [D][BM]
-    static constexpr int OFF_DO = OFF_QT + BM * D * 2;       // dO  row-major
-    static constexpr int OFF_DOT = OFF_DO + BM * D * 2;      // dO^T
-    static constexpr int OFF_DS = OFF_DOT + BM * D * 2;      // dS  row-major [BM][BN] bf16
-    static constexpr int OFF_KT = OFF_DS + BM * BN * 2;      // K^T [D][BN]
-    static constexpr int OFF_ROW = OFF_KT + BN * D * 2;      // lse2[BM], delta[BM]
-    static constexpr int LDS_BYTES = OFF_ROW + 2 * BM * 4;
+    using QTile = DmaTile<BM, D, THREADS>;   // Q and dO tiles
+    using KTile = DmaTile<BN, D, THREADS>;   // the workgroup's K rows (dQ = dS K)
+    static constexpr int TILE = BM * D * 2;
+    static constexpr int OFF_STAGE = 0;                          // 2 x {Q, dO}
+    static constexpr int STAGE = 2 * TILE;
+    static constexpr int OFF_DS = OFF_STAGE + 2 * STAGE;         // 2 x dS [BM][BN] bf16
+    static constexpr int DS_BYTES = BM * BN * 2;
+    static constexpr int OFF_K = OFF_DS + 2 * DS_BYTES;          // K [BN][D]
+    static constexpr int LDS_ATOMIC = OFF_K + BN * D * 2;
+    static constexpr int LDS_PLAIN = OFF_DS;
 };
 
 template <int D, bool CAUSAL, bool ATOMIC_DQ>
-__global__ __launch_bounds__(256, FA_BWD_MIN_WAVES) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(256) void bwd_dkdv_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, const uint16_t *__restrict__ dout,
     const float *__restrict__ lse2, const float *__restrict__ delta, float *__restrict__ dq,
@@ -112,29 +122,25 @@ __global__ __launch_bounds__(256, FA_BWD_MIN_WAVES) void bwd_dkdv_kernel(
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int h = lane >> 5, col = lane & 31;
+    const int g16 = lane >> 4;
 
     int bg, kt;
     xcd_tile_map(blockIdx.x, BHkv, KT, false, bg, kt);
     const int b = bg / Hkv, g = bg % Hkv;
     const int grp = Hq / Hkv;
+    const int NP = pad_rows(N);
     const int kv0 = kt * S::BN;
-    const int kw0 = kv0 + wave * 32;
-    const int key = kw0 + col;  // the key this lane owns in S / dP / dS
+    const int key = kv0 + wave * 32 + col;  // the key this lane owns in S / dP / dS
 
     const uint16_t *kh = k + ((size_t)b * Hkv + g) * N * D;
     const uint16_t *vh = v + ((size_t)b * Hkv + g) * N * D;
 
-    // K and V rows of this lane's key as B operands (K^T / V^T k-slices).
+    // K and V rows of this lane's key as B operands.
     bf16x8 kf[S::KSTEPS], vf[S::KSTEPS];
 #pragma unroll
     for (int s = 0; s < S::KSTEPS; s++) {
         kf[s] = __builtin_bit_cast(bf16x8, gload16(kh, ((size_t)key * D + 16 * s + 8 * h) * 2, key < N));
         vf[s] = __builtin_bit_cast(bf16x8, gload16(vh, ((size_t)key * D + 16 * s + 8 * h) * 2, key < N));
-    }
-    if (ATOMIC_DQ) {
-        typename S::KTile kt_tile;
-        kt_tile.load(kh, kv0, N, tid);
-        kt_tile.store(smem + S::OFF_KT, tid);
     }
 
     f32x16 dva[S::DBLK], dka[S::DBLK];
@@ -143,148 +149,165 @@ __global__ __launch_bounds__(256, FA_BWD_MIN_WAVES) void bwd_dkdv_kernel(
 #pragma unroll
         for (int r = 0; r < 16; r++) dva[db][r] = dka[db][r] = 0.f;
 
-    // Offsets of the A-operand reads.
-    uint32_t rowoff[S::KSTEPS];  // row-major [BM][D] tile, row col (+32 qb), chunk 2s + h
+    // LDS offsets.  Row reads of a Q / dO tile (A operand of S and dP): row
+    // 32 qb + col, chunk 2 s + h.  Transposing reads (A operand of dV^T and
+    // dK^T): rows 16 ks + 8 rho + 4 h .. +3 in the key order of the P / dS
+    // registers, columns 32 db + (lane % 32).
+    uint32_t rowoff[S::KSTEPS];
 #pragma unroll
-    for (int s = 0; s < S::KSTEPS; s++) rowoff[s] = row_tile_off(col, 2 * s + h, D);
-    uint32_t coloff[4][2];       // transposed [D][BM] tile, row 32 p + col, chunk 2 ks + h
+    for (int s = 0; s < S::KSTEPS; s++) rowoff[s] = tile_off(col, 2 * s + h, D);
+    uint32_t troff[S::DBLK][2];
 #pragma unroll
-    for (int ks = 0; ks < 4; ks++)
+    for (int db = 0; db < S::DBLK; db++)
 #pragma unroll
-        for (int p = 0; p < 2; p++) coloff[ks][p] = col_tile_off<S::BM>(32 * p + col, 2 * ks + h);
+        for (int rho = 0; rho < 2; rho++)
+            troff[db][rho] = tr_off(8 * rho + 4 * h, 32 * db + 16 * (g16 & 1), lane, D);
 
     const int first_qt = CAUSAL ? kv0 / S::BM : 0;
     const int n_qt = (N + S::BM - 1) / S::BM;
     const int steps_per_head = n_qt - first_qt;
     const int n_steps = grp * steps_per_head;  // (query head of the group, query tile) pairs
-    typename S::QTile qtile, dotile;
-    float *rowbuf = reinterpret_cast<float *>(smem + S::OFF_ROW);
-    float row_l2 = INFINITY, row_dl = 0.f;  // this thread's lse2 / delta entry (tid < BM)
 
-    // Global -> registers for step `st`; the loads stay in flight during the
-    // previous step's compute.
-    auto fetch = [&](int st) {
+    typename S::QTile qtile;  // the Q and dO tiles share one load pattern
+    qtile.init(wave, lane);
+    auto issue = [&](int st, char *stage) {
         const int hq = g * grp + st / steps_per_head;
         const int qs = (first_qt + st % steps_per_head) * S::BM;
         const size_t ho = ((size_t)b * Hq + hq) * N;
-        qtile.load(q + ho * D, qs, N, tid);
-        dotile.load(dout + ho * D, qs, N, tid);
-        if (tid < S::BM) {
-            const int qi = qs + tid;
-            row_l2 = qi < N ? lse2[ho + qi] : INFINITY;  // P = 0 for rows >= N
-            row_dl = qi < N ? delta[ho + qi] : 0.f;
+        qtile.issue(q + ho * D, qs, N, stage, wave);
+        qtile.issue(dout + ho * D, qs, N, stage + S::TILE, wave);
+    };
+
+    // dQ[BM x D] += dS[BM x BN] K[BN x D] for the step whose dS sits in `dsl`;
+    // 2 * DBLK tiles of 32 x 32 spread over the 4 waves.  A = dS rows (natural
+    // key order), B = K by transposing reads (keys 16 ks + 8 h + 4 rho ..).
+    auto dq_update = [&](int st, const char *dsl) {
+        const int hq = g * grp + st / steps_per_head;
+        const int qs = (first_qt + st % steps_per_head) * S::BM;
+        float *dqh = dq + ((size_t)b * Hq + hq) * N * D;
+        constexpr int TILES = 2 * S::DBLK;
+#pragma unroll
+        for (int tt = wave; tt < TILES; tt += 4) {
+            const int qb = tt / S::DBLK, db = tt % S::DBLK;
+            f32x16 acc;
+#pragma unroll
+            for (int r = 0; r < 16; r++) acc[r] = 0.f;
+            const uint32_t ao = tile_off(32 * qb + col, h, 128);
+            const uint32_t bo0 = tr_off(8 * h, 32 * db + 16 * (g16 & 1), lane, D);
+            const uint32_t bo1 = tr_off(8 * h + 4, 32 * db + 16 * (g16 & 1), lane, D);
+#pragma unroll
+            for (int ks = 0; ks < S::BN / 16; ks++) {
+                // chunk 2 ks + h of dS row 32 qb + col: XOR-ing the logical
+                // chunk into the swizzled one is linear, so add it by XOR.
+                const bf16x8 a = lds_read_bf16x8(dsl, ao ^ ((2 * ks) << 4));
+                const char *kl = smem + S::OFF_K + 16 * ks * D * 2;
+                const bf16x8 bb = join_bf16x8(lds_read_tr16(kl, bo0), lds_read_tr16(kl, bo1));
+                acc = mfma32(a, bb, acc);
+            }
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                const int qi = qs + 32 * qb + 8 * (r >> 2) + 4 * h + (r & 3);
+                if (qi < N) unsafeAtomicAdd(dqh + (size_t)qi * D + 32 * db + col, acc[r] * scale);
+            }
         }
     };
-    if (n_steps > 0) fetch(0);
+
+    if (ATOMIC_DQ) {
+        typename S::KTile ktile;
+        ktile.init(wave, lane);
+        ktile.issue(kh, kv0, N, smem + S::OFF_K, wave);
+    }
+    if (n_steps > 0) issue(0, smem + S::OFF_STAGE);
+    dma_barrier();
 
     for (int st = 0; st < n_steps; st++) {
         const int hq = g * grp + st / steps_per_head;
         const int qs = (first_qt + st % steps_per_head) * S::BM;
-        const size_t head_off = ((size_t)b * Hq + hq) * N;
-        {
-            lds_barrier();  // every wave is done with the previous step's LDS tiles
-            qtile.store_rows(smem + S::OFF_Q, tid);
-            qtile.store(smem + S::OFF_QT, tid);
-            dotile.store_rows(smem + S::OFF_DO, tid);
-            dotile.store(smem + S::OFF_DOT, tid);
-            if (tid < S::BM) {
-                rowbuf[tid] = row_l2;
-                rowbuf[S::BM + tid] = row_dl;
-            }
-            lds_barrier();
-            if (st + 1 < n_steps) fetch(st + 1);
+        const size_t rbase = ((size_t)b * Hq + hq) * NP + qs;  // padded workspace rows
+        const char *stage = smem + S::OFF_STAGE + (st & 1) * S::STAGE;
+        const char *ql = stage;
+        const char *dol = stage + S::TILE;
 
-            // S = Q K^T and dP = dO V^T, rows = queries, one key column per lane.
-            f32x16 sc[2], dp[2];
+        // This lane's rows of the tile: 32 qb + 8 gq + 4 h + i.
+        f32x4 l2[2][4], dl[2][4];
+#pragma unroll
+        for (int qb = 0; qb < 2; qb++)
+#pragma unroll
+            for (int gq = 0; gq < 4; gq++) {
+                const size_t r0 = rbase + 32 * qb + 8 * gq + 4 * h;
+                l2[qb][gq] = *reinterpret_cast<const f32x4 *>(lse2 + r0);
+                dl[qb][gq] = *reinterpret_cast<const f32x4 *>(delta + r0);
+            }
+        // Next step's tiles go to the other stage, last read in step st - 1.
+        if (st + 1 < n_steps) issue(st + 1, smem + S::OFF_STAGE + ((st + 1) & 1) * S::STAGE);
+        if (ATOMIC_DQ && st > 0) dq_update(st - 1, smem + S::OFF_DS + ((st - 1) & 1) * S::DS_BYTES);
+
+        // S = Q K^T and dP = dO V^T, rows = queries, one key column per lane.
+        f32x16 sc[2], dp[2];
+#pragma unroll
+        for (int qb = 0; qb < 2; qb++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) sc[qb][r] = dp[qb][r] = 0.f;
+#pragma unroll
+        for (int s = 0; s < S::KSTEPS; s++)
 #pragma unroll
             for (int qb = 0; qb < 2; qb++) {
-#pragma unroll
-                for (int r = 0; r < 16; r++) sc[qb][r] = dp[qb][r] = 0.f;
-#pragma unroll
-                for (int s = 0; s < S::KSTEPS; s++) {
-                    const uint32_t ro = rowoff[s] + qb * 32 * D * 2;
-                    sc[qb] = mfma32(lds_read_bf16x8(smem + S::OFF_Q, ro), kf[s], sc[qb]);
-                    dp[qb] = mfma32(lds_read_bf16x8(smem + S::OFF_DO, ro), vf[s], dp[qb]);
-                }
+                const uint32_t ro = rowoff[s] + qb * 32 * D * 2;
+                sc[qb] = mfma32(lds_read_bf16x8(ql, ro), kf[s], sc[qb]);
+                dp[qb] = mfma32(lds_read_bf16x8(dol, ro), vf[s], dp[qb]);
             }
-            // P = exp2(s * scale * log2 e - LSE2), dS = P (dP - D).
-            bf16x8 pf[4], dsf[4];
+        // P = exp2(s * scale * log2 e - LSE2), dS = P (dP - D); rows >= N and
+        // (causal) keys after the query give P = 0.
+        bf16x8 pf[4], dsf[4];
 #pragma unroll
-            for (int qb = 0; qb < 2; qb++) {
+        for (int qb = 0; qb < 2; qb++) {
 #pragma unroll
-                for (int gq = 0; gq < 4; gq++) {
-                    const int qr = 32 * qb + 8 * gq + 4 * h;  // rows qr .. qr+3 of the tile
-                    const f32x4 l2 = lds_read_f32x4(smem + S::OFF_ROW, qr * 4);
-                    const f32x4 dl = lds_read_f32x4(smem + S::OFF_ROW, (S::BM + qr) * 4);
+            for (int gq = 0; gq < 4; gq++)
 #pragma unroll
-                    for (int i = 0; i < 4; i++) {
-                        const int r = 4 * gq + i;
-                        const int qi = qs + qr + i;
-                        float p = exp2_hw(__builtin_fmaf(sc[qb][r], scale_log2, -l2[i]));
-                        const bool dead = key >= N || (CAUSAL && key > qi);
-                        p = dead ? 0.f : p;
-                        sc[qb][r] = p;
-                        dp[qb][r] = p * (dp[qb][r] - dl[i]);
-                    }
+                for (int i = 0; i < 4; i++) {
+                    const int r = 4 * gq + i;
+                    const int qi = qs + 32 * qb + 8 * gq + 4 * h + i;
+                    float p = exp2_hw(__builtin_fmaf(sc[qb][r], scale_log2, -l2[qb][gq][i]));
+                    const bool dead = key >= N || qi >= N || (CAUSAL && key > qi);
+                    p = dead ? 0.f : p;
+                    sc[qb][r] = p;
+                    dp[qb][r] = p * (dp[qb][r] - dl[qb][gq][i]);
                 }
-                pf[2 * qb] = pack_half(sc[qb], 0);
-                pf[2 * qb + 1] = pack_half(sc[qb], 1);
-                dsf[2 * qb] = pack_half(dp[qb], 0);
-                dsf[2 * qb + 1] = pack_half(dp[qb], 1);
-            }
-            // dV^T += dO^T P,  dK^T += Q^T dS  (contraction over the tile's queries).
-#pragma unroll
-            for (int db = 0; db < S::DBLK; db++)
-#pragma unroll
-                for (int ks = 0; ks < 4; ks++) {
-                    const uint32_t co = coloff[ks][db & 1] + (db >> 1) * 64 * S::BM * 2;
-                    dva[db] = mfma32(lds_read_bf16x8(smem + S::OFF_DOT, co), pf[ks], dva[db]);
-                    dka[db] = mfma32(lds_read_bf16x8(smem + S::OFF_QT, co), dsf[ks], dka[db]);
-                }
-
-            if (ATOMIC_DQ) {
-                // dS (bf16) -> LDS row-major [BM queries][BN keys], natural key order.
-                uint16_t *dsl = reinterpret_cast<uint16_t *>(smem + S::OFF_DS);
-                const int kin = wave * 32 + col;  // key index within the workgroup
-#pragma unroll
-                for (int qb = 0; qb < 2; qb++)
-#pragma unroll
-                    for (int r = 0; r < 16; r++) {
-                        const int qr = 32 * qb + 8 * (r >> 2) + 4 * h + (r & 3);
-                        const __bf16 x = (__bf16)dp[qb][r];
-                        const uint32_t off = qr * (S::BN * 2) + (((kin >> 3) ^ (qr & 7)) << 4) + (kin & 7) * 2;
-                        dsl[off >> 1] = __builtin_bit_cast(uint16_t, x);
-                    }
-                lds_barrier();
-                // dQ[BM x D] += dS[BM x BN] K[BN x D]; 2*DBLK tiles of 32x32 over 4 waves.
-                constexpr int TILES = 2 * S::DBLK;
-#pragma unroll
-                for (int tt = wave; tt < TILES; tt += 4) {
-                    const int qb = tt / S::DBLK, db = tt % S::DBLK;
-                    f32x16 acc;
-#pragma unroll
-                    for (int r = 0; r < 16; r++) acc[r] = 0.f;
-#pragma unroll
-                    for (int ks = 0; ks < S::BN / 16; ks++) {
-                        const int qr = 32 * qb + col;
-                        const uint32_t ao = qr * (S::BN * 2) + (((2 * ks + h) ^ (qr & 7)) << 4);
-                        const bf16x8 a = lds_read_bf16x8(smem + S::OFF_DS, ao);
-                        const bf16x8 bb = lds_read_bf16x8(smem + S::OFF_KT,
-                                                          col_tile_off<S::BN>(32 * db + col, 2 * ks + h));
-                        acc = mfma32(a, bb, acc);
-                    }
-                    float *dqh = dq + head_off * D;
-#pragma unroll
-                    for (int r = 0; r < 16; r++) {
-                        const int qi = qs + 32 * qb + 8 * (r >> 2) + 4 * h + (r & 3);
-                        if (qi < N) unsafeAtomicAdd(dqh + (size_t)qi * D + 32 * db + col, acc[r] * scale);
-                    }
-                }
-            }
+            pf[2 * qb] = pack_half(sc[qb], 0);
+            pf[2 * qb + 1] = pack_half(sc[qb], 1);
+            dsf[2 * qb] = pack_half(dp[qb], 0);
+            dsf[2 * qb + 1] = pack_half(dp[qb], 1);
         }
-    }
+        // dV^T += dO^T P,  dK^T += Q^T dS  (contraction over the tile's queries).
+#pragma unroll
+        for (int ks = 0; ks < 4; ks++)
+#pragma unroll
+            for (int db = 0; db < S::DBLK; db++) {
+                const uint32_t o0 = troff[db][0] + 16 * ks * D * 2;
+                const uint32_t o1 = troff[db][1] + 16 * ks * D * 2;
+                dva[db] = mfma32(join_bf16x8(lds_read_tr16(dol, o0), lds_read_tr16(dol, o1)), pf[ks], dva[db]);
+                dka[db] = mfma32(join_bf16x8(lds_read_tr16(ql, o0), lds_read_tr16(ql, o1)), dsf[ks], dka[db]);
+            }
 
-    // dV = dV^T^T, dK = scale * dK^T^T: lane holds d = 32 db + 8 gq + 4 h + i of key `key`.
+        if (ATOMIC_DQ) {
+            // dS (bf16) -> LDS [BM queries][BN keys], natural key order.
+            char *dsl = smem + S::OFF_DS + (st & 1) * S::DS_BYTES;
+            const int kin = wave * 32 + col;  // key index within the workgroup
+#pragma unroll
+            for (int qb = 0; qb < 2; qb++)
+#pragma unroll
+                for (int r = 0; r < 16; r++) {
+                    const int qr = 32 * qb + 8 * (r >> 2) + 4 * h + (r & 3);
+                    const __bf16 x = (__bf16)dp[qb][r];
+                    *reinterpret_cast<uint16_t *>(dsl + tile_off(qr, kin >> 3, 128) + (kin & 7) * 2) =
+                        __builtin_bit_cast(uint16_t, x);
+                }
+        }
+        dma_barrier();  // next stage landed; this stage and dS are complete
+    }
+    if (ATOMIC_DQ && n_steps > 0) dq_update(n_steps - 1, smem + S::OFF_DS + ((n_steps - 1) & 1) * S::DS_BYTES);
+
+    // dV = (dV^T)^T, dK = scale * (dK^T)^T: lane holds d = 32 db + 8 gq + 4 h + i of `key`.
     if (key < N) {
         float *dvr = dv + (((size_t)b * Hkv + g) * N + key) * D;
         float *dkr = dk + (((size_t)b * Hkv + g) * N + key) * D;
@@ -310,12 +333,9 @@ struct DqShape {
     static constexpr int THREADS = 256;
     static constexpr int KSTEPS = D / 16;
     static constexpr int DBLK = D / 32;
-    using KTile = ColTile<BN, D, THREADS, true>;   // K row-major + K^T in key_pos16 order
-    using VTile = RowTile<BN, D, THREADS>;         // V row-major
-    static constexpr int OFF_K = 0;
-    static constexpr int OFF_KT = OFF_K + BN * D * 2;
-    static constexpr int OFF_V = OFF_KT + BN * D * 2;
-    static constexpr int BUF_BYTES = OFF_V + BN * D * 2;
+    using Tile = DmaTile<BN, D, THREADS>;   // K and V tiles, row-major
+    static constexpr int TILE = BN * D * 2;
+    static constexpr int BUF_BYTES = 2 * TILE;   // K, V
     static constexpr int LDS_BYTES = 2 * BUF_BYTES;
 };
 
@@ -331,6 +351,7 @@ __global__ __launch_bounds__(256, FA_DQ_MIN_WAVES) void bwd_dq_kernel(
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int h = lane >> 5, col = lane & 31;
+    const int g16 = lane >> 4;
 
     int bh, qt;
     xcd_tile_map(blockIdx.x, BH, QT, CAUSAL, bh, qt);
@@ -352,17 +373,22 @@ __global__ __launch_bounds__(256, FA_DQ_MIN_WAVES) void bwd_dq_kernel(
         qf[s] = __builtin_bit_cast(bf16x8, gload16(qh, ((size_t)qrow * D + 16 * s + 8 * h) * 2, qrow < N));
         df[s] = __builtin_bit_cast(bf16x8, gload16(doh, ((size_t)qrow * D + 16 * s + 8 * h) * 2, qrow < N));
     }
-    const float l2 = qrow < N ? lse2[head_off + qrow] : INFINITY;
-    const float dl = qrow < N ? delta[head_off + qrow] : 0.f;
+    const size_t prow = ((size_t)b * Hq + hq) * pad_rows(N) + qrow;  // padded workspace row
+    const float l2 = qrow < N ? lse2[prow] : INFINITY;
+    const float dl = qrow < N ? delta[prow] : 0.f;
 
+    // K and V row reads (A operands of S^T and dP^T): row 32 kb + col, chunk
+    // 2 s + h.  K^T by transposing reads (A operand of dQ^T): keys
+    // 16 ks + 8 rho + 4 h .. +3 (the key order of the dS^T registers).
     uint32_t rowoff[S::KSTEPS];
 #pragma unroll
-    for (int s = 0; s < S::KSTEPS; s++) rowoff[s] = row_tile_off(col, 2 * s + h, D);
-    uint32_t coloff[S::BN / 16][2];
+    for (int s = 0; s < S::KSTEPS; s++) rowoff[s] = tile_off(col, 2 * s + h, D);
+    uint32_t troff[S::DBLK][2];
 #pragma unroll
-    for (int ks = 0; ks < S::BN / 16; ks++)
+    for (int db = 0; db < S::DBLK; db++)
 #pragma unroll
-        for (int p = 0; p < 2; p++) coloff[ks][p] = col_tile_off<S::BN>(32 * p + col, 2 * ks + h);
+        for (int rho = 0; rho < 2; rho++)
+            troff[db][rho] = tr_off(8 * rho + 4 * h, 32 * db + 16 * (g16 & 1), lane, D);
 
     f32x16 acc[S::DBLK];
 #pragma unroll
@@ -373,36 +399,34 @@ __global__ __launch_bounds__(256, FA_DQ_MIN_WAVES) void bwd_dq_kernel(
     const int n_tiles_all = (N + S::BN - 1) / S::BN;
     const int n_tiles = CAUSAL ? min(n_tiles_all, (min(q0 + S::BM, N) + S::BN - 1) / S::BN)
                                : n_tiles_all;
-    typename S::KTile kst;
-    typename S::VTile vst;
-    kst.load(kh, 0, N, tid);
-    vst.load(vh, 0, N, tid);
-    kst.store_rows(smem + S::OFF_K, tid);
-    kst.store(smem + S::OFF_KT, tid);
-    vst.store(smem + S::OFF_V, tid);
-    __syncthreads();
+    typename S::Tile tile;
+    tile.init(wave, lane);
+    auto issue = [&](int t, char *buf) {
+        tile.issue(kh, t * S::BN, N, buf, wave);
+        tile.issue(vh, t * S::BN, N, buf + S::TILE, wave);
+    };
+    issue(0, smem);
+    dma_barrier();
 
     for (int t = 0; t < n_tiles; t++) {
         const int key0 = t * S::BN;
-        const bool more = t + 1 < n_tiles;
-        if (more) {
-            kst.load(kh, key0 + S::BN, N, tid);
-            vst.load(vh, key0 + S::BN, N, tid);
-        }
-        const char *buf = smem + (t & 1) * S::BUF_BYTES;
+        if (t + 1 < n_tiles) issue(t + 1, smem + ((t + 1) & 1) * S::BUF_BYTES);
+        const char *kl = smem + (t & 1) * S::BUF_BYTES;
+        const char *vl = kl + S::TILE;
         if (!CAUSAL || key0 <= qw0 + 31) {
             f32x16 st[2], dpt[2];
 #pragma unroll
-            for (int kb = 0; kb < 2; kb++) {
+            for (int kb = 0; kb < 2; kb++)
 #pragma unroll
                 for (int r = 0; r < 16; r++) st[kb][r] = dpt[kb][r] = 0.f;
 #pragma unroll
-                for (int s = 0; s < S::KSTEPS; s++) {
+            for (int s = 0; s < S::KSTEPS; s++)
+#pragma unroll
+                for (int kb = 0; kb < 2; kb++) {
                     const uint32_t ro = rowoff[s] + kb * 32 * D * 2;
-                    st[kb] = mfma32(lds_read_bf16x8(buf + S::OFF_K, ro), qf[s], st[kb]);
-                    dpt[kb] = mfma32(lds_read_bf16x8(buf + S::OFF_V, ro), df[s], dpt[kb]);
+                    st[kb] = mfma32(lds_read_bf16x8(kl, ro), qf[s], st[kb]);
+                    dpt[kb] = mfma32(lds_read_bf16x8(vl, ro), df[s], dpt[kb]);
                 }
-            }
             bf16x8 dsf[S::BN / 16];
 #pragma unroll
             for (int kb = 0; kb < 2; kb++) {
@@ -419,20 +443,15 @@ __global__ __launch_bounds__(256, FA_DQ_MIN_WAVES) void bwd_dq_kernel(
             }
             // dQ^T += K^T dS^T (contraction over the tile's keys).
 #pragma unroll
-            for (int db = 0; db < S::DBLK; db++)
+            for (int ks = 0; ks < S::BN / 16; ks++)
 #pragma unroll
-                for (int ks = 0; ks < S::BN / 16; ks++) {
-                    const uint32_t co = coloff[ks][db & 1] + (db >> 1) * 64 * S::BN * 2;
-                    acc[db] = mfma32(lds_read_bf16x8(buf + S::OFF_KT, co), dsf[ks], acc[db]);
+                for (int db = 0; db < S::DBLK; db++) {
+                    const i16x4 lo = lds_read_tr16(kl, troff[db][0] + 16 * ks * D * 2);
+                    const i16x4 hi = lds_read_tr16(kl, troff[db][1] + 16 * ks * D * 2);
+                    acc[db] = mfma32(join_bf16x8(lo, hi), dsf[ks], acc[db]);
                 }
         }
-        if (more) {
-            char *nb = smem + ((t + 1) & 1) * S::BUF_BYTES;
-            kst.store_rows(nb + S::OFF_K, tid);
-            kst.store(nb + S::OFF_KT, tid);
-            vst.store(nb + S::OFF_V, tid);
-        }
-        __syncthreads();
+        dma_barrier();
     }
 
     if (qrow < N) {
@@ -460,13 +479,14 @@ template <int D, bool CAUSAL>
 static hipError_t launch_bwd_t(const BwdArgs &a)
 {
     (void)hipGetLastError();  // clear an error left by an earlier, unrelated call
-    const size_t rows = (size_t)a.B * a.Hq * a.N;
+    const int BH = a.B * a.Hq;
     const float scale_log2 = a.scale * kLog2e;
     {
         constexpr int RPB = 256 / (D / 8);
+        const size_t rows = (size_t)BH * pad_rows(a.N);
         const unsigned grid = (unsigned)((rows + RPB - 1) / RPB);
         hipLaunchKernelGGL(bwd_pre_kernel<D>, dim3(grid), dim3(256), 0, a.stream,
-                           (const uint16_t *)a.dout, a.o, a.lse, a.delta, a.lse2, a.dq, rows,
+                           (const uint16_t *)a.dout, a.o, a.lse, a.delta, a.lse2, a.dq, BH, a.N,
                            a.deterministic ? 0 : 1);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -478,15 +498,15 @@ static hipError_t launch_bwd_t(const BwdArgs &a)
         hipError_t e;
         if (a.deterministic) {
             auto kern = bwd_dkdv_kernel<D, CAUSAL, false>;
-            if ((e = set_lds(kern, S::LDS_BYTES)) != hipSuccess) return e;
-            hipLaunchKernelGGL(kern, dim3(BHkv * KT), dim3(S::THREADS), S::LDS_BYTES, a.stream,
+            if ((e = set_lds(kern, S::LDS_PLAIN)) != hipSuccess) return e;
+            hipLaunchKernelGGL(kern, dim3(BHkv * KT), dim3(S::THREADS), S::LDS_PLAIN, a.stream,
                                (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v,
                                (const uint16_t *)a.dout, a.lse2, a.delta, a.dq, a.dk, a.dv, a.Hq,
                                a.Hkv, a.N, BHkv, KT, a.scale, scale_log2);
         } else {
             auto kern = bwd_dkdv_kernel<D, CAUSAL, true>;
-            if ((e = set_lds(kern, S::LDS_BYTES)) != hipSuccess) return e;
-            hipLaunchKernelGGL(kern, dim3(BHkv * KT), dim3(S::THREADS), S::LDS_BYTES, a.stream,
+            if ((e = set_lds(kern, S::LDS_ATOMIC)) != hipSuccess) return e;
+            hipLaunchKernelGGL(kern, dim3(BHkv * KT), dim3(S::THREADS), S::LDS_ATOMIC, a.stream,
                                (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v,
                                (const uint16_t *)a.dout, a.lse2, a.delta, a.dq, a.dk, a.dv, a.Hq,
                                a.Hkv, a.N, BHkv, KT, a.scale, scale_log2);
@@ -496,7 +516,6 @@ static hipError_t launch_bwd_t(const BwdArgs &a)
     if (a.deterministic) {
         using S = DqShape<D>;
         const int QT = (a.N + S::BM - 1) / S::BM;
-        const int BH = a.B * a.Hq;
         auto kern = bwd_dq_kernel<D, CAUSAL>;
         hipError_t e;
         if ((e = set_lds(kern, S::LDS_BYTES)) != hipSuccess) return e;

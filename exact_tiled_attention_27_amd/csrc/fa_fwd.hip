@@ -44,8 +44,8 @@ struct FwdShape {
     static constexpr int DBLK = D / 32;      // 32-row blocks of O^T
     static constexpr int NKB = BN / 32;      // 32-key blocks of S^T
     static constexpr int KVSTEPS = BN / 16;  // k-steps of O^T += V^T P^T
-    using KTile = DmaTile<BN, D, THREADS, false>;  // row-major K, RowTile swizzle
-    using VTile = DmaTile<BN, D, THREADS, true>;   // row-major V, VTile swizzle
+    using KTile = DmaTile<BN, D, THREADS>;  // row-major K tile
+    using VTile = DmaTile<BN, D, THREADS>;  // row-major V tile
     static constexpr int K_BYTES = KTile::BYTES;
     static constexpr int BUF_BYTES = KTile::BYTES + VTile::BYTES;
     static constexpr int LDS_BYTES = 2 * BUF_BYTES;
@@ -63,7 +63,7 @@ __global__ __launch_bounds__(256, FA_FWD_MIN_WAVES) void fwd_kernel(
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int h = lane >> 5, col = lane & 31;
-    const int g16 = lane >> 4, r16 = lane & 15;  // 16-lane group and lane within it
+    const int g16 = lane >> 4;  // 16-lane group
 
     int bh, qt;
     xcd_tile_map(blockIdx.x, BH, QT, CAUSAL, bh, qt);
@@ -87,18 +87,16 @@ __global__ __launch_bounds__(256, FA_FWD_MIN_WAVES) void fwd_kernel(
     // the swizzle only sees row & 15, so kb*32 rows are an immediate offset.
     uint32_t koff[S::KSTEPS];
 #pragma unroll
-    for (int s = 0; s < S::KSTEPS; s++) koff[s] = row_tile_off(col, 2 * s + h, D);
-    // V (A operand of O^T via transposing reads): lane (g16, r16) of read rho
-    // of k-step ks points at key 16 ks + 8 rho + 4 h + r16/4, columns
-    // 32 db + 16 (g16 & 1) + 4 (r16 & 3) .. +3.  The swizzle depends on the key
-    // only through 4 h + r16/4, so ks and rho are immediate offsets.
-    uint32_t voff[S::DBLK];
+    for (int s = 0; s < S::KSTEPS; s++) koff[s] = tile_off(col, 2 * s + h, D);
+    // V^T (A operand of O^T) by transposing reads: read rho of k-step ks covers
+    // keys 16 ks + 8 rho + 4 h .. +3 (the key order of the P^T registers) and
+    // head-dimension columns 32 db + (lane % 32); 16 ks rows are an immediate.
+    uint32_t voff[S::DBLK][2];
 #pragma unroll
-    for (int db = 0; db < S::DBLK; db++) {
-        const int key = 4 * h + (r16 >> 2);
-        const int chunk = 4 * db + 2 * (g16 & 1) + ((r16 & 3) >> 1);
-        voff[db] = vtile_off(key, chunk, D) + 8 * (r16 & 1);
-    }
+    for (int db = 0; db < S::DBLK; db++)
+#pragma unroll
+        for (int rho = 0; rho < 2; rho++)
+            voff[db][rho] = tr_off(8 * rho + 4 * h, 32 * db + 16 * (g16 & 1), lane, D);
 
     f32x16 acc[S::DBLK];
 #pragma unroll
@@ -119,14 +117,8 @@ __global__ __launch_bounds__(256, FA_FWD_MIN_WAVES) void fwd_kernel(
     kst.init(wave, lane);
     vst.init(wave, lane);
     auto issue = [&](int tile, char *buf) {
-        const int r0 = tile * S::BN;
-        if (r0 + S::BN <= N) {
-            kst.issue_full(kh, r0, buf, wave);
-            vst.issue_full(vh, r0, buf + S::K_BYTES, wave);
-        } else {
-            kst.issue_tail(kh, r0, N, buf, wave);
-            vst.issue_tail(vh, r0, N, buf + S::K_BYTES, wave);
-        }
+        kst.issue(kh, tile * S::BN, N, buf, wave);
+        vst.issue(vh, tile * S::BN, N, buf + S::K_BYTES, wave);
     };
     issue(0, smem);
     dma_barrier();
@@ -205,8 +197,8 @@ __global__ __launch_bounds__(256, FA_FWD_MIN_WAVES) void fwd_kernel(
             for (int ks = 0; ks < S::KVSTEPS; ks++)
 #pragma unroll
                 for (int db = 0; db < S::DBLK; db++) {
-                    const i16x4 lo = lds_read_tr16(vl, voff[db] + (16 * ks) * D * 2);
-                    const i16x4 hi = lds_read_tr16(vl, voff[db] + (16 * ks + 8) * D * 2);
+                    const i16x4 lo = lds_read_tr16(vl, voff[db][0] + 16 * ks * D * 2);
+                    const i16x4 hi = lds_read_tr16(vl, voff[db][1] + 16 * ks * D * 2);
                     acc[db] = mfma32(join_bf16x8(lo, hi), pf[ks], acc[db]);
                 }
         }

@@ -1,24 +1,27 @@
 /*
  * fa.h -- C ABI of the MI355X (gfx950) exact tiled attention library libfa.so.
  *
- * What the calls compute (FlashAttention-4 pages):
+ * What the calls compute:
  *   Forward: per tile of keys, S = Q K^T * scale, a running row max / row sum
- *   softmax P = exp(S - m) / l, and O = P V ("The Asymmetric Hardware Scaling
- *   Wall", three phases per tile; the simulator in "End-to-End Implementation"
- *   walks key tiles with a running max and sum).  The result is exact
- *   attention softmax(Q K^T * scale) V up to rounding.  The normalisation is
- *   skipped unless the running maximum grows by more than log2(256) = 8 in the
- *   base-2 exponent domain (menfem page, "Key Contributions", item 2).
+ *   softmax P = exp(S - m) / l, and O = P V (page "FlashAttention-4 Guide:
+ *   Kernel Pipelining on Blackwell", section "The Asymmetric Hardware Scaling
+ *   Wall": three phases per tile; its simulator in "End-to-End
+ *   Implementation" walks key tiles with a running max and sum).  The result
+ *   is exact attention softmax(Q K^T * scale) V up to rounding.  The
+ *   normalisation is skipped unless the running maximum grows by more than
+ *   log2(256) = 8 in the base-2 exponent domain (page "FlashAttention-4",
+ *   section "Key Contributions", item 2).
  *   Backward: dQ, dK, dV of the same function, with P recomputed from the
  *   saved log-sum-exp; dQ is summed either with global atomic adds or by a
- *   separate deterministic pass (menfem page, "Key Contributions" item 3 and
- *   "Limitations": the deterministic mode trades speed for reproducibility).
+ *   separate deterministic pass (page "FlashAttention-4", "Key Contributions"
+ *   item 3 and "Limitations": the deterministic mode trades speed for
+ *   reproducibility).
  *
  * Conventions shared by every call:
  *   - Tensors are device pointers to dense row-major arrays laid out
  *     [B, H, N, d] (sequence-major within a head, as in the simulator's
  *     [Batch, Heads, Len, HeadDim]).  Q, dO, O, dQ use H = Hq; K, V, dK, dV use
- *     H = Hkv.  LSE and the workspace rows are [B, Hq, N].
+ *     H = Hkv.  LSE is [B, Hq, N].
  *   - bf16 tensors hold IEEE bfloat16 bit patterns (uint16).  O, LSE, dQ, dK,
  *     dV are float32.
  *   - Grouped-query attention: query head h reads key/value head
@@ -70,9 +73,10 @@ int fa_fwd(const void *q, const void *k, const void *v, float *o, float *lse,
            int B, int Hq, int Hkv, int N, int d, float scale, int causal, void *stream);
 
 /*
- * Bytes of device workspace fa_bwd needs for this shape (the per-row
- * D_i = sum_c dO_ic O_ic and the base-2 LSE, fp32 [B, Hq, N] each, rounded
- * up to 256 bytes).  Returns 0 for an invalid shape.
+ * Bytes of device workspace fa_bwd needs for this shape: the per-row
+ * D_i = sum_c dO_ic O_ic and the base-2 LSE, two fp32 arrays [B, Hq, N']
+ * with N' = N rounded up to a multiple of 64, each rounded up to 256 bytes.
+ * Returns 0 for an invalid shape.
  */
 size_t fa_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d, int deterministic);
 

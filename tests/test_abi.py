@@ -87,7 +87,9 @@ def test_workspace_bytes():
     per = (rows * 4 + 255) // 256 * 256
     for det in (0, 1):
         assert fa.fa_bwd_workspace_bytes(2, 16, 16, 8192, 128, det) == 2 * per
-    assert fa.fa_bwd_workspace_bytes(1, 2, 2, 3, 64, 0) == 2 * 256
+    # rows are padded to a multiple of 64 per head: N = 3 -> 64 rows per head
+    assert fa.fa_bwd_workspace_bytes(1, 2, 2, 3, 64, 0) == 2 * 512
+    assert fa.fa_bwd_workspace_bytes(1, 1, 1, 65, 64, 1) == 2 * 512
     assert fa.fa_bwd_workspace_bytes(0, 2, 2, 3, 64, 0) == 0
     assert fa.fa_bwd_workspace_bytes(1, 2, 2, 3, 48, 0) == 0
     # exactly the required size passes validation far enough to reach the other checks
