@@ -30,6 +30,8 @@
 //                 128 queries) walks the key tiles, recomputes S^T, P^T,
 //                 dP^T = V dO^T, dS^T, and accumulates dQ^T += K^T dS^T in
 //                 registers; one plain store per element.
+#include <type_traits>
+
 #include "fa_device.hpp"
 #include "fa_launch.hpp"
 #include "fa_tiles.hpp"
@@ -100,8 +102,9 @@ struct DkdvShape {
     using QTile = DmaTile<BM, D, THREADS>;   // Q and dO tiles
     using KTile = DmaTile<BN, D, THREADS>;   // the workgroup's K rows (dQ = dS K)
     static constexpr int TILE = BM * D * 2;
-    static constexpr int OFF_STAGE = 0;                          // 2 x {Q, dO}
-    static constexpr int STAGE = 2 * TILE;
+    static constexpr int OFF_STAGE = 0;                          // 2 x {Q, dO, LSE2, D}
+    static constexpr int ROWS = 2 * TILE;                        // LSE2[BM], then D[BM] (fp32)
+    static constexpr int STAGE = 2 * TILE + 2 * BM * 4;
     static constexpr int OFF_DS = OFF_STAGE + 2 * STAGE;         // 2 x dS [BM][BN] bf16
     static constexpr int DS_BYTES = BM * BN * 2;
     static constexpr int OFF_K = OFF_DS + 2 * DS_BYTES;          // K [BN][D]
@@ -176,6 +179,13 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
         const size_t ho = ((size_t)b * Hq + hq) * N;
         qtile.issue(q + ho * D, qs, N, stage, wave);
         qtile.issue(dout + ho * D, qs, N, stage + S::TILE, wave);
+        // LSE2 and D of the tile's 64 rows (padded workspace: always in
+        // bounds): lanes 0-15 fetch LSE2, lanes 16-31 fetch D, 16 bytes each.
+        if (wave == 0 && lane < 32) {
+            const size_t r0 = ((size_t)b * Hq + hq) * NP + qs + 4 * (lane & 15);
+            lds_dma16(lane < 16 ? (const void *)(lse2 + r0) : (const void *)(delta + r0),
+                      (lds_void_t *)(stage + S::ROWS));
+        }
     };
 
     // dQ[BM x D] += dS[BM x BN] K[BN x D] for the step whose dS sits in `dsl`;
@@ -223,21 +233,9 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
     for (int st = 0; st < n_steps; st++) {
         const int hq = g * grp + st / steps_per_head;
         const int qs = (first_qt + st % steps_per_head) * S::BM;
-        const size_t rbase = ((size_t)b * Hq + hq) * NP + qs;  // padded workspace rows
         const char *stage = smem + S::OFF_STAGE + (st & 1) * S::STAGE;
         const char *ql = stage;
         const char *dol = stage + S::TILE;
-
-        // This lane's rows of the tile: 32 qb + 8 gq + 4 h + i.
-        f32x4 l2[2][4], dl[2][4];
-#pragma unroll
-        for (int qb = 0; qb < 2; qb++)
-#pragma unroll
-            for (int gq = 0; gq < 4; gq++) {
-                const size_t r0 = rbase + 32 * qb + 8 * gq + 4 * h;
-                l2[qb][gq] = *reinterpret_cast<const f32x4 *>(lse2 + r0);
-                dl[qb][gq] = *reinterpret_cast<const f32x4 *>(delta + r0);
-            }
         // Next step's tiles go to the other stage, last read in step st - 1.
         if (st + 1 < n_steps) issue(st + 1, smem + S::OFF_STAGE + ((st + 1) & 1) * S::STAGE);
         if (ATOMIC_DQ && st > 0) dq_update(st - 1, smem + S::OFF_DS + ((st - 1) & 1) * S::DS_BYTES);
@@ -256,23 +254,41 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
                 sc[qb] = mfma32(lds_read_bf16x8(ql, ro), kf[s], sc[qb]);
                 dp[qb] = mfma32(lds_read_bf16x8(dol, ro), vf[s], dp[qb]);
             }
-        // P = exp2(s * scale * log2 e - LSE2), dS = P (dP - D); rows >= N and
-        // (causal) keys after the query give P = 0.
+        // P = exp2(s * scale * log2 e - LSE2), dS = P (dP - D).  Rows >= N,
+        // keys >= N and (causal) keys after the query get a -inf exponent
+        // (P = 0); only steps that contain such pairs evaluate the mask.
+        const bool need_mask = kv0 + S::BN > N || qs + S::BM > N || (CAUSAL && qs < kv0 + S::BN - 1);
+        auto softmax = [&](auto masked) {
+            constexpr bool MASK = decltype(masked)::value;
+#pragma unroll
+            for (int qb = 0; qb < 2; qb++)
+#pragma unroll
+                for (int gq = 0; gq < 4; gq++) {
+                    const int qr = 32 * qb + 8 * gq + 4 * h;  // rows qr .. qr + 3 of the tile
+                    const f32x4 l2 = lds_read_f32x4(stage + S::ROWS, qr * 4);
+                    const f32x4 dl = lds_read_f32x4(stage + S::ROWS, (S::BM + qr) * 4);
+#pragma unroll
+                    for (int i = 0; i < 4; i++) {
+                        const int r = 4 * gq + i;
+                        float x = __builtin_fmaf(sc[qb][r], scale_log2, -l2[i]);
+                        if (MASK) {
+                            const int qi = qs + qr + i;
+                            const bool dead = key >= N || qi >= N || (CAUSAL && key > qi);
+                            x = dead ? -INFINITY : x;
+                        }
+                        const float p = exp2_hw(x);
+                        sc[qb][r] = p;
+                        dp[qb][r] = p * (dp[qb][r] - dl[i]);
+                    }
+                }
+        };
+        if (need_mask)
+            softmax(std::true_type{});
+        else
+            softmax(std::false_type{});
         bf16x8 pf[4], dsf[4];
 #pragma unroll
         for (int qb = 0; qb < 2; qb++) {
-#pragma unroll
-            for (int gq = 0; gq < 4; gq++)
-#pragma unroll
-                for (int i = 0; i < 4; i++) {
-                    const int r = 4 * gq + i;
-                    const int qi = qs + 32 * qb + 8 * gq + 4 * h + i;
-                    float p = exp2_hw(__builtin_fmaf(sc[qb][r], scale_log2, -l2[qb][gq][i]));
-                    const bool dead = key >= N || qi >= N || (CAUSAL && key > qi);
-                    p = dead ? 0.f : p;
-                    sc[qb][r] = p;
-                    dp[qb][r] = p * (dp[qb][r] - dl[qb][gq][i]);
-                }
             pf[2 * qb] = pack_half(sc[qb], 0);
             pf[2 * qb + 1] = pack_half(sc[qb], 1);
             dsf[2 * qb] = pack_half(dp[qb], 0);
@@ -427,17 +443,32 @@ __global__ __launch_bounds__(256, FA_DQ_MIN_WAVES) void bwd_dq_kernel(
                     st[kb] = mfma32(lds_read_bf16x8(kl, ro), qf[s], st[kb]);
                     dpt[kb] = mfma32(lds_read_bf16x8(vl, ro), df[s], dpt[kb]);
                 }
+            // Keys >= N and (causal) keys after the query get a -inf exponent;
+            // only tiles that contain such keys for this workgroup evaluate it.
+            const bool need_mask = key0 + S::BN > N || (CAUSAL && key0 + S::BN - 1 > q0);
+            auto softmax = [&](auto masked) {
+                constexpr bool MASK = decltype(masked)::value;
+#pragma unroll
+                for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+                    for (int r = 0; r < 16; r++) {
+                        float x = __builtin_fmaf(st[kb][r], scale_log2, -l2);
+                        if (MASK) {
+                            const int kk = key0 + kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                            const bool dead = kk >= N || (CAUSAL && kk > qrow);
+                            x = dead ? -INFINITY : x;
+                        }
+                        const float p = exp2_hw(x);
+                        dpt[kb][r] = p * (dpt[kb][r] - dl);
+                    }
+            };
+            if (need_mask)
+                softmax(std::true_type{});
+            else
+                softmax(std::false_type{});
             bf16x8 dsf[S::BN / 16];
 #pragma unroll
             for (int kb = 0; kb < 2; kb++) {
-#pragma unroll
-                for (int r = 0; r < 16; r++) {
-                    const int kk = key0 + kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                    float p = exp2_hw(__builtin_fmaf(st[kb][r], scale_log2, -l2));
-                    const bool dead = kk >= N || (CAUSAL && kk > qrow);
-                    p = dead ? 0.f : p;
-                    dpt[kb][r] = p * (dpt[kb][r] - dl);
-                }
                 dsf[2 * kb] = pack_half(dpt[kb], 0);
                 dsf[2 * kb + 1] = pack_half(dpt[kb], 1);
             }
