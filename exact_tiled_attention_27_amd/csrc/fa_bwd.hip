@@ -341,6 +341,203 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
     }
 }
 
+// ------------------------------------------- dK/dV kernel, two waves per key slice
+// Deterministic mode.  One workgroup of 8 waves per (batch, kv head, 128 keys);
+// the 32 keys of slice p are shared by two waves (both on the same SIMD):
+//   wave A (w = p):     S = Q K^T, P = exp2(S * c - LSE2), dV^T += dO^T P;
+//   wave B (w = p + 4): dP = dO V^T, then (after A publishes P through LDS)
+//                       dS = P (dP - D), dK^T += Q^T dS.
+// Each wave holds one operand set and one accumulator set (about 200
+// registers), so two waves fit per SIMD and the MFMA phases of one overlap
+// the exponent / elementwise phases of the other.
+template <int D>
+struct DkdvSplitShape {
+    static constexpr int BN = 128;   // keys per workgroup (32 per wave pair)
+    static constexpr int BM = 64;    // queries per step
+    static constexpr int THREADS = 512;
+    static constexpr int KSTEPS = D / 16;
+    static constexpr int DBLK = D / 32;
+    using QTile = DmaTile<BM, D, THREADS>;
+    static constexpr int TILE = BM * D * 2;
+    static constexpr int ROWS = 2 * TILE;                  // LSE2[BM], then D[BM] (fp32)
+    static constexpr int STAGE = 2 * TILE + 2 * BM * 4;    // Q, dO, rows
+    static constexpr int OFF_X = 2 * STAGE;                // P exchange: 4 slices x 64 lanes x 32 fp32
+    static constexpr int X_SLICE = 64 * 32 * 4;
+    static constexpr int LDS_BYTES = OFF_X + 4 * X_SLICE;
+};
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(512) void bwd_dkdv_split_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
+    const uint16_t *__restrict__ v, const uint16_t *__restrict__ dout,
+    const float *__restrict__ lse2, const float *__restrict__ delta, float *__restrict__ dk,
+    float *__restrict__ dv, int Hq, int Hkv, int N, int BHkv, int KT, float scale,
+    float scale_log2)
+{
+    using S = DkdvSplitShape<D>;
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int slice = wave & 3;
+    const bool wave_a = wave < 4;
+    const int h = lane >> 5, col = lane & 31;
+    const int g16 = lane >> 4;
+
+    int bg, kt;
+    xcd_tile_map(blockIdx.x, BHkv, KT, false, bg, kt);
+    const int b = bg / Hkv, g = bg % Hkv;
+    const int grp = Hq / Hkv;
+    const int NP = pad_rows(N);
+    const int kv0 = kt * S::BN;
+    const int key = kv0 + slice * 32 + col;  // the key this lane owns in S / dP / dS
+
+    // Wave A keeps K rows (B operand of S), wave B keeps V rows (of dP).
+    const uint16_t *kvh = (wave_a ? k : v) + ((size_t)b * Hkv + g) * N * D;
+    bf16x8 kvf[S::KSTEPS];
+#pragma unroll
+    for (int s = 0; s < S::KSTEPS; s++)
+        kvf[s] = __builtin_bit_cast(bf16x8, gload16(kvh, ((size_t)key * D + 16 * s + 8 * h) * 2, key < N));
+
+    f32x16 acc[S::DBLK];  // A: dV^T, B: dK^T
+#pragma unroll
+    for (int db = 0; db < S::DBLK; db++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) acc[db][r] = 0.f;
+
+    uint32_t rowoff[S::KSTEPS];
+#pragma unroll
+    for (int s = 0; s < S::KSTEPS; s++) rowoff[s] = tile_off(col, 2 * s + h, D);
+    uint32_t troff[S::DBLK][2];
+#pragma unroll
+    for (int db = 0; db < S::DBLK; db++)
+#pragma unroll
+        for (int rho = 0; rho < 2; rho++)
+            troff[db][rho] = tr_off(8 * rho + 4 * h, 32 * db + 16 * (g16 & 1), lane, D);
+    char *xchg = smem + S::OFF_X + slice * S::X_SLICE + lane * 16;  // + (qb*4 + gq) * 1024
+
+    const int first_qt = CAUSAL ? kv0 / S::BM : 0;
+    const int n_qt = (N + S::BM - 1) / S::BM;
+    const int steps_per_head = n_qt - first_qt;
+    const int n_steps = grp * steps_per_head;
+
+    typename S::QTile qtile;
+    qtile.init(wave, lane);
+    auto issue = [&](int st, char *stage) {
+        const int hq = g * grp + st / steps_per_head;
+        const int qs = (first_qt + st % steps_per_head) * S::BM;
+        const size_t ho = ((size_t)b * Hq + hq) * N;
+        qtile.issue(q + ho * D, qs, N, stage, wave);
+        qtile.issue(dout + ho * D, qs, N, stage + S::TILE, wave);
+        if (wave == 0 && lane < 32) {
+            const size_t r0 = ((size_t)b * Hq + hq) * NP + qs + 4 * (lane & 15);
+            lds_dma16(lane < 16 ? (const void *)(lse2 + r0) : (const void *)(delta + r0),
+                      (lds_void_t *)(stage + S::ROWS));
+        }
+    };
+    if (n_steps > 0) issue(0, smem);
+    dma_barrier();
+
+    for (int st = 0; st < n_steps; st++) {
+        const int qs = (first_qt + st % steps_per_head) * S::BM;
+        const char *stage = smem + (st & 1) * S::STAGE;
+        const char *ql = stage;
+        const char *dol = stage + S::TILE;
+        if (st + 1 < n_steps) issue(st + 1, smem + ((st + 1) & 1) * S::STAGE);
+
+        // A: S = Q K^T.  B: dP = dO V^T.  (rows = queries, one key per lane)
+        const char *rl = wave_a ? ql : dol;
+        f32x16 x[2];
+#pragma unroll
+        for (int qb = 0; qb < 2; qb++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) x[qb][r] = 0.f;
+#pragma unroll
+        for (int s = 0; s < S::KSTEPS; s++)
+#pragma unroll
+            for (int qb = 0; qb < 2; qb++)
+                x[qb] = mfma32(lds_read_bf16x8(rl, rowoff[s] + qb * 32 * D * 2), kvf[s], x[qb]);
+
+        if (wave_a) {
+            // P = exp2(s * c - LSE2); masked pairs get a -inf exponent.
+            const bool need_mask = kv0 + S::BN > N || qs + S::BM > N || (CAUSAL && qs < kv0 + S::BN - 1);
+            auto softmax = [&](auto masked) {
+                constexpr bool MASK = decltype(masked)::value;
+#pragma unroll
+                for (int qb = 0; qb < 2; qb++)
+#pragma unroll
+                    for (int gq = 0; gq < 4; gq++) {
+                        const int qr = 32 * qb + 8 * gq + 4 * h;
+                        const f32x4 l2 = lds_read_f32x4(stage + S::ROWS, qr * 4);
+#pragma unroll
+                        for (int i = 0; i < 4; i++) {
+                            float e = __builtin_fmaf(x[qb][4 * gq + i], scale_log2, -l2[i]);
+                            if (MASK) {
+                                const int qi = qs + qr + i;
+                                const bool dead = key >= N || qi >= N || (CAUSAL && key > qi);
+                                e = dead ? -INFINITY : e;
+                            }
+                            x[qb][4 * gq + i] = exp2_hw(e);
+                        }
+                        const f32x4 pv = {x[qb][4 * gq], x[qb][4 * gq + 1], x[qb][4 * gq + 2], x[qb][4 * gq + 3]};
+                        *reinterpret_cast<f32x4 *>(xchg + (qb * 4 + gq) * 1024) = pv;
+                    }
+            };
+            if (need_mask)
+                softmax(std::true_type{});
+            else
+                softmax(std::false_type{});
+        }
+        lds_barrier();  // P of every slice published
+
+        bf16x8 bop[4];  // A: P, B: dS (B operands, key order of the accumulator rows)
+        if (wave_a) {
+#pragma unroll
+            for (int qb = 0; qb < 2; qb++) {
+                bop[2 * qb] = pack_half(x[qb], 0);
+                bop[2 * qb + 1] = pack_half(x[qb], 1);
+            }
+        } else {
+#pragma unroll
+            for (int qb = 0; qb < 2; qb++) {
+#pragma unroll
+                for (int gq = 0; gq < 4; gq++) {
+                    const int qr = 32 * qb + 8 * gq + 4 * h;
+                    const f32x4 dl = lds_read_f32x4(stage + S::ROWS, (S::BM + qr) * 4);
+                    const f32x4 pv = *reinterpret_cast<const f32x4 *>(xchg + (qb * 4 + gq) * 1024);
+#pragma unroll
+                    for (int i = 0; i < 4; i++) x[qb][4 * gq + i] = pv[i] * (x[qb][4 * gq + i] - dl[i]);
+                }
+                bop[2 * qb] = pack_half(x[qb], 0);
+                bop[2 * qb + 1] = pack_half(x[qb], 1);
+            }
+        }
+        // A: dV^T += dO^T P.  B: dK^T += Q^T dS.
+        const char *tl = wave_a ? dol : ql;
+#pragma unroll
+        for (int ks = 0; ks < 4; ks++)
+#pragma unroll
+            for (int db = 0; db < S::DBLK; db++) {
+                const uint32_t o0 = troff[db][0] + 16 * ks * D * 2;
+                const uint32_t o1 = troff[db][1] + 16 * ks * D * 2;
+                acc[db] = mfma32(join_bf16x8(lds_read_tr16(tl, o0), lds_read_tr16(tl, o1)), bop[ks], acc[db]);
+            }
+        dma_barrier();  // next stage landed; this stage and the exchange are free
+    }
+
+    if (key < N) {
+        float *out = (wave_a ? dv : dk) + (((size_t)b * Hkv + g) * N + key) * D;
+        const float f = wave_a ? 1.f : scale;
+#pragma unroll
+        for (int db = 0; db < S::DBLK; db++)
+#pragma unroll
+            for (int gq = 0; gq < 4; gq++) {
+                f32x4 val = {acc[db][4 * gq] * f, acc[db][4 * gq + 1] * f, acc[db][4 * gq + 2] * f,
+                             acc[db][4 * gq + 3] * f};
+                *reinterpret_cast<f32x4 *>(out + 32 * db + 8 * gq + 4 * h) = val;
+            }
+    }
+}
+
 // ------------------------------------------------- deterministic dQ kernel
 template <int D>
 struct DqShape {
@@ -528,12 +725,13 @@ static hipError_t launch_bwd_t(const BwdArgs &a)
         const int BHkv = a.B * a.Hkv;
         hipError_t e;
         if (a.deterministic) {
-            auto kern = bwd_dkdv_kernel<D, CAUSAL, false>;
-            if ((e = set_lds(kern, S::LDS_PLAIN)) != hipSuccess) return e;
-            hipLaunchKernelGGL(kern, dim3(BHkv * KT), dim3(S::THREADS), S::LDS_PLAIN, a.stream,
+            using SS = DkdvSplitShape<D>;
+            auto kern = bwd_dkdv_split_kernel<D, CAUSAL>;
+            if ((e = set_lds(kern, SS::LDS_BYTES)) != hipSuccess) return e;
+            hipLaunchKernelGGL(kern, dim3(BHkv * KT), dim3(SS::THREADS), SS::LDS_BYTES, a.stream,
                                (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v,
-                               (const uint16_t *)a.dout, a.lse2, a.delta, a.dq, a.dk, a.dv, a.Hq,
-                               a.Hkv, a.N, BHkv, KT, a.scale, scale_log2);
+                               (const uint16_t *)a.dout, a.lse2, a.delta, a.dk, a.dv, a.Hq, a.Hkv,
+                               a.N, BHkv, KT, a.scale, scale_log2);
         } else {
             auto kern = bwd_dkdv_kernel<D, CAUSAL, true>;
             if ((e = set_lds(kern, S::LDS_ATOMIC)) != hipSuccess) return e;
