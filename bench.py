@@ -1,14 +1,16 @@
 """Throughput of exact tiled attention (forward + backward) on one MI355X.
 
 One step = the whole path over one batch: fa_fwd (O, LSE) then fa_bwd (dQ, dK,
-dV; atomic-dQ mode) on the B=4, Hq=Hkv=16, N=4096, d=128 non-causal bf16
-workload (iid N(0,1) inputs, dO drawn after V).  FLOPs are counted nominally:
-forward 4*B*Hq*N^2*d (halved when causal), backward 2.5x the forward.
+dV; deterministic dQ pass) on the B=4, Hq=Hkv=16, N=4096, d=128 non-causal
+bf16 workload (iid N(0,1) inputs, dO drawn after V).  FLOPs are counted
+nominally: forward 4*B*Hq*N^2*d (halved when causal), backward 2.5x the
+forward, the same count for both backward modes.
 
 Prints ONE JSON line.  Inputs are resident in HBM before the timed region; the
 region is bracketed by device synchronisation.  HIP events recorded on the
-launch stream around each call give per-kernel durations for the roofline.
-The fp64 CPU oracle is timed on a bounded sample (one head's forward and
+launch stream around each call give per-call durations for the roofline.  The
+atomic-dQ backward is timed after the step loop and reported under "parts".
+The fp64 CPU oracle is timed on a bounded sample (16 heads' forward and
 backward) of the same workload as a reported baseline.
 """
 import argparse
@@ -63,8 +65,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="fwd_n4096")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--extra", action="store_true",
-                   help="also time the deterministic backward (reported under parts)")
+    p.add_argument("--atomic-reps", type=int, default=10,
+                   help="timed launches of the atomic-dQ backward reported under parts (0: skip)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="run one 256 MiB device-to-device copy before the timed region "
                         "(reference kernel for scaling HBM byte counters)")
@@ -130,7 +132,7 @@ def main():
         del src, dst
     for _ in range(args.warmup):
         fwd()
-        bwd(0)
+        bwd(1)
     torch.cuda.synchronize()
 
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
@@ -142,7 +144,7 @@ def main():
         ev[i][0].record(stream)
         fwd()
         ev[i][1].record(stream)
-        bwd(0)
+        bwd(1)
         ev[i][2].record(stream)
     t_end.record(stream)
     torch.cuda.synchronize()
@@ -155,37 +157,41 @@ def main():
 
     parts = {
         "fwd_ms_avg": float(np.mean(fwd_ms)),
+        "fwd_ms_min": float(np.min(fwd_ms)),
         "fwd_tflops": f_fwd / (np.mean(fwd_ms) * 1e-3) / 1e12,
-        "bwd_atomic_ms_avg": float(np.mean(bwd_ms)),
-        "bwd_atomic_tflops": f_bwd / (np.mean(bwd_ms) * 1e-3) / 1e12,
+        "bwd_deterministic_ms_avg": float(np.mean(bwd_ms)),
+        "bwd_deterministic_ms_min": float(np.min(bwd_ms)),
+        "bwd_deterministic_tflops": f_bwd / (np.mean(bwd_ms) * 1e-3) / 1e12,
     }
     parts["fwd_frac_peak"] = parts["fwd_tflops"] / PEAK_BF16_TFLOPS
-    parts["bwd_atomic_frac_peak"] = parts["bwd_atomic_tflops"] / PEAK_BF16_TFLOPS
+    parts["bwd_deterministic_frac_peak"] = parts["bwd_deterministic_tflops"] / PEAK_BF16_TFLOPS
 
-    if args.extra:
-        reps = max(3, args.steps // 2)
+    if args.atomic_reps > 0:
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        bwd(1)
+        bwd(0)
         torch.cuda.synchronize()
         e0.record(stream)
-        for _ in range(reps):
-            bwd(1)
+        for _ in range(args.atomic_reps):
+            bwd(0)
         e1.record(stream)
         torch.cuda.synchronize()
-        det_ms = e0.elapsed_time(e1) / reps
-        parts["bwd_deterministic_ms_avg"] = det_ms
-        parts["bwd_deterministic_tflops"] = f_bwd / (det_ms * 1e-3) / 1e12
+        at_ms = e0.elapsed_time(e1) / args.atomic_reps
+        parts["bwd_atomic_ms_avg"] = at_ms
+        parts["bwd_atomic_tflops"] = f_bwd / (at_ms * 1e-3) / 1e12
 
-    # Roofline of the dominant launch: the forward kernel is one launch per
-    # fa_fwd; fa_bwd (atomic mode) is a short preprocess kernel plus the dK/dV
-    # kernel that carries all backward MFMA work.
+    # Roofline of the dominant launch.  fa_fwd is one kernel; fa_bwd
+    # (deterministic) is a short preprocess kernel, the dK/dV kernel and the dQ
+    # kernel, timed together by the events around the call.  Algorithmic work
+    # is the nominal count of each call (the dQ pass's recomputation of S and
+    # dP is not counted).
     cz = "true" if w.causal else "false"
-    if parts["fwd_ms_avg"] >= parts["bwd_atomic_ms_avg"]:
+    if parts["fwd_ms_avg"] >= parts["bwd_deterministic_ms_avg"]:
         rl_kernels = [f"fa::fwd_kernel<{d}, {cz}>"]
         rl_flops, rl_ms = f_fwd, parts["fwd_ms_avg"]
     else:
-        rl_kernels = [f"fa::bwd_pre_kernel<{d}>", f"fa::bwd_dkdv_kernel<{d}, {cz}, true>"]
-        rl_flops, rl_ms = f_bwd, parts["bwd_atomic_ms_avg"]
+        rl_kernels = [f"fa::bwd_pre_kernel<{d}>", f"fa::bwd_dkdv_split_kernel<{d}, {cz}>",
+                      f"fa::bwd_dq_kernel<{d}, {cz}>"]
+        rl_flops, rl_ms = f_bwd, parts["bwd_deterministic_ms_avg"]
     achieved = rl_flops / (rl_ms * 1e-3) / 1e12
     roofline = {"bound": "mfma", "kernel": " + ".join(rl_kernels), "achieved": achieved,
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
@@ -217,7 +223,7 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "frac_peak": value / PEAK_BF16_TFLOPS,
         "config": {"workload": w.name, "B": B, "Hq": Hq, "Hkv": Hkv, "N": N, "d": d,
-                   "causal": w.causal, "step": "fa_fwd + fa_bwd (atomic dQ)",
+                   "causal": w.causal, "step": "fa_fwd + fa_bwd (deterministic dQ)",
                    "flops_per_step": f_fwd + f_bwd},
         "parts": parts,
         "roofline": roofline,

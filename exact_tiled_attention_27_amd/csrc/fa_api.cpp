@@ -22,6 +22,9 @@ int check_common(int B, int Hq, int Hkv, int N, int d, float scale)
     // 32-bit grid: B * Hq * ceil(N / 64) workgroups.
     const int64_t rows = (int64_t)B * Hq * N;
     if (rows > ((int64_t)1 << 40) || (int64_t)B * Hq * ((N + 63) / 64) > INT32_MAX) return FA_ERR_SHAPE;
+    // One head's rows, N * d bf16 values, are addressed with 32-bit byte
+    // offsets (the tile copies use buffer resources over a head).
+    if ((int64_t)N * d * 2 >= ((int64_t)1 << 31)) return FA_ERR_SHAPE;
     return FA_OK;
 }
 

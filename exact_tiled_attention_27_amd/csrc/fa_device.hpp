@@ -105,6 +105,34 @@ __device__ __forceinline__ void lds_barrier()
 // Value of lane l ^ 32 (the other half of the wave).
 __device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32, 64); }
 
+// Reductions across the two 32-lane halves of a wave (lanes l and l ^ 32)
+// with one v_permlane32_swap: afterwards lane l holds lanes 0-31's value in
+// the first word and lanes 32-63's in the second, in both halves, so every
+// lane computes the same bits.
+// (The builtin exists only for the device target.)
+__device__ __forceinline__ void halves_pair(float x, float &lo, float &hi)
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    lo = __uint_as_float(r[0]);
+    hi = __uint_as_float(r[1]);
+#else
+    lo = hi = x;
+#endif
+}
+__device__ __forceinline__ float halves_max(float x)
+{
+    float lo, hi;
+    halves_pair(x, lo, hi);
+    return fmaxf(lo, hi);
+}
+__device__ __forceinline__ float halves_sum(float x)
+{
+    float lo, hi;
+    halves_pair(x, lo, hi);
+    return lo + hi;
+}
+
 // Within a group of 16 keys, the key order a 32x32 C tile presents to a B
 // operand: half h, slot t holds key 8*(t/4) + 4*h + t%4.  Stored position of
 // key kk so that half h reads positions 8h .. 8h+7 as one 16-byte chunk:

@@ -44,13 +44,26 @@ struct FwdShape {
     static constexpr int DBLK = D / 32;      // 32-row blocks of O^T
     static constexpr int NKB = BN / 32;      // 32-key blocks of S^T
     static constexpr int KVSTEPS = BN / 16;  // k-steps of O^T += V^T P^T
-    using KTile = DmaTile<BN, D, THREADS>;  // row-major K tile
-    using VTile = DmaTile<BN, D, THREADS>;  // row-major V tile
+    using KTile = DmaTile<BN, D, THREADS>;  // row-major K (and V) tile
+    // LDS: two K slots, then two V slots (tile t uses slot t % 2 of each).
     static constexpr int K_BYTES = KTile::BYTES;
-    static constexpr int BUF_BYTES = KTile::BYTES + VTile::BYTES;
-    static constexpr int LDS_BYTES = 2 * BUF_BYTES;
+    static constexpr int V_BYTES = KTile::BYTES;
+    static constexpr int V_BASE = 2 * K_BYTES;
+    static constexpr int LDS_BYTES = 2 * K_BYTES + 2 * V_BYTES;
 };
 
+// Software pipeline of one wave (tile t, with S_t already computed, masked,
+// and its row maximum folded into the reference m):
+//   1. barrier: V_t and K_{t+1} are in LDS, every wave is done with K_t and
+//      V_{t-1}; start the copies of V_{t+1} and K_{t+2} into the freed slots;
+//   2. one straight-line block: S_{t+1} = K_{t+1} Q^T on the matrix cores,
+//      P_t = exp2(S_t * c - m) with its row sum and bf16 packing on the vector
+//      ALUs, then O^T += V_t^T P_t^T;
+//   3. mask S_{t+1} (diagonal or tail tiles only), take its row maximum and,
+//      rarely, rescale O and l.
+// The exponentials of one tile thus overlap the score products of the next
+// (the overlap the FlashAttention-4 guide obtains with separate softmax and
+// MMA warps), inside each wave and without extra barriers.
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, FA_FWD_MIN_WAVES) void fwd_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
@@ -61,7 +74,8 @@ __global__ __launch_bounds__(256, FA_FWD_MIN_WAVES) void fwd_kernel(
     extern __shared__ __attribute__((aligned(16))) char smem[];
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar LDS bases
     const int h = lane >> 5, col = lane & 31;
     const int g16 = lane >> 4;  // 16-lane group
 
@@ -70,8 +84,7 @@ __global__ __launch_bounds__(256, FA_FWD_MIN_WAVES) void fwd_kernel(
     const int b = bh / Hq, hq = bh % Hq;
     const int g = hq / (Hq / Hkv);
     const int q0 = qt * S::BM;
-    const int qw0 = q0 + wave * 32;  // first query row of this wave
-    const int qrow = qw0 + col;      // the query column this lane owns
+    const int qrow = q0 + wave * 32 + col;  // the query column this lane owns
 
     const uint16_t *qh = q + ((size_t)b * Hq + hq) * N * D;
     const uint16_t *kh = k + ((size_t)b * Hkv + g) * N * D;
@@ -112,106 +125,140 @@ __global__ __launch_bounds__(256, FA_FWD_MIN_WAVES) void fwd_kernel(
     // Tiles every key of which is < N and (causal) <= q0 need no mask.
     const int n_full = CAUSAL ? min(N / S::BN, (q0 + 1) / S::BN) : N / S::BN;
 
-    typename S::KTile kst;
-    typename S::VTile vst;
-    kst.init(wave, lane);
-    vst.init(wave, lane);
-    auto issue = [&](int tile, char *buf) {
-        kst.issue(kh, tile * S::BN, N, buf, wave);
-        vst.issue(vh, tile * S::BN, N, buf + S::K_BYTES, wave);
+    // K and V tiles have one shape, so one set of per-lane copy offsets.
+    typename S::KTile kv_dma;
+    kv_dma.init(wave, lane);
+    // Tile t lives in slot t % 2 of the K and of the V region.  Callers pass
+    // the slot as a compile-time constant, so every LDS address is a per-lane
+    // register plus an immediate.
+    using Slot0 = std::integral_constant<int, 0>;
+    using Slot1 = std::integral_constant<int, 1>;
+    const BufRsrc krs = make_rsrc(kh, (uint32_t)N * D * 2);
+    const BufRsrc vrs = make_rsrc(vh, (uint32_t)N * D * 2);
+    auto issue_k = [&](int t, auto slot) {
+        kv_dma.issue(krs, t * S::BN, N, smem + decltype(slot)::value * S::K_BYTES, wave);
     };
-    issue(0, smem);
-    dma_barrier();
+    auto issue_v = [&](int t, auto slot) {
+        kv_dma.issue(vrs, t * S::BN, N, smem + S::V_BASE + decltype(slot)::value * S::V_BYTES, wave);
+    };
 
-    auto step = [&](auto masked, int t) {
-        constexpr bool MASK = decltype(masked)::value;
-        const int key0 = t * S::BN;
-        // The buffer for tile t + 1 was last read in step t - 1, which every
-        // wave has finished (barrier at the end of that step).
-        if (t + 1 < n_tiles) issue(t + 1, smem + ((t + 1) & 1) * S::BUF_BYTES);
-        const char *kl = smem + (t & 1) * S::BUF_BYTES;
-        const char *vl = kl + S::K_BYTES;
-
-        // Waves whose rows all precede this tile see only masked keys: skip.
-        if (!MASK || !CAUSAL || key0 <= qw0 + 31) {
-            // k-step outer: each step's two K reads feed two independent chains.
-            f32x16 st[S::NKB];
+    // S^T_t = K_t Q^T (raw scores).  k-step outer: two independent chains.
+    auto scores = [&](f32x16(&st)[S::NKB], auto slot) {
+        const char *kl = smem + decltype(slot)::value * S::K_BYTES;
+#pragma unroll
+        for (int s = 0; s < S::KSTEPS; s++)
 #pragma unroll
             for (int kb = 0; kb < S::NKB; kb++)
+                st[kb] = mfma32(lds_read_bf16x8(kl, koff[s] + kb * 32 * D * 2), qf[s],
+                                s == 0 ? f32x16{} : st[kb]);
+    };
+    auto apply_mask = [&](f32x16(&st)[S::NKB], int t) {
 #pragma unroll
-                for (int r = 0; r < 16; r++) st[kb][r] = 0.f;
+        for (int kb = 0; kb < S::NKB; kb++)
 #pragma unroll
-            for (int s = 0; s < S::KSTEPS; s++)
-#pragma unroll
-                for (int kb = 0; kb < S::NKB; kb++)
-                    st[kb] = mfma32(lds_read_bf16x8(kl, koff[s] + kb * 32 * D * 2), qf[s], st[kb]);
-            if (MASK) {
-#pragma unroll
-                for (int kb = 0; kb < S::NKB; kb++)
-#pragma unroll
-                    for (int r = 0; r < 16; r++) {
-                        const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                        const bool dead = key >= N || (CAUSAL && key > qrow);
-                        st[kb][r] = dead ? -INFINITY : st[kb][r];
-                    }
+            for (int r = 0; r < 16; r++) {
+                const int key = t * S::BN + kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                const bool dead = key >= N || (CAUSAL && key > qrow);
+                st[kb][r] = dead ? -INFINITY : st[kb][r];
             }
-            // Tile row maximum (raw scores), in-lane then across the halves.
-            float mx = st[0][0];
+    };
+    // Tile row maximum, then the conditional rescale: the reference moves
+    // only when the tile maximum exceeds it by more than tau, otherwise the
+    // exponents stay <= 2^tau.
+    auto row_max_rescale = [&](f32x16(&st)[S::NKB]) {
+        float mx = st[0][0];
 #pragma unroll
-            for (int kb = 0; kb < S::NKB; kb++)
+        for (int kb = 0; kb < S::NKB; kb++)
 #pragma unroll
-                for (int r = 0; r < 16; r++) mx = fmaxf(mx, st[kb][r]);
-            mx = fmaxf(mx, swap_halves(mx));
-            const float mt = mx * scale_log2;  // scale_log2 > 0, so max commutes
-
-            // Conditional rescale: move the reference only when the tile max
-            // exceeds it by more than tau; otherwise exponents stay <= 2^tau.
-            const bool grow = mt > m_ref + tau;
-            if (__any(grow)) {
-                const float alpha = grow ? exp2_hw(m_ref - mt) : 1.f;
-                m_ref = grow ? mt : m_ref;
-                l_part *= alpha;
+            for (int r = 0; r < 16; r++) mx = fmaxf(mx, st[kb][r]);
+        const float mt = halves_max(mx) * scale_log2;  // scale_log2 > 0: max commutes
+        const bool grow = mt > m_ref + tau;
+        if (__any(grow)) {
+            const float alpha = grow ? exp2_hw(m_ref - mt) : 1.f;
+            m_ref = grow ? mt : m_ref;
+            l_part *= alpha;
 #pragma unroll
-                for (int db = 0; db < S::DBLK; db++)
+            for (int db = 0; db < S::DBLK; db++)
 #pragma unroll
-                    for (int r = 0; r < 16; r++) acc[db][r] *= alpha;
-            }
-            const float msub = (m_ref == -INFINITY) ? 0.f : m_ref;
-
-            // P = exp2(s * scale * log2 e - m), row sum, bf16 B operands.
-            bf16x8 pf[S::KVSTEPS];
-#pragma unroll
-            for (int kb = 0; kb < S::NKB; kb++) {
-#pragma unroll
-                for (int r = 0; r < 16; r++) {
-                    const float p = exp2_hw(__builtin_fmaf(st[kb][r], scale_log2, -msub));
-                    st[kb][r] = p;
-                    l_part += p;
-                }
-                pf[2 * kb] = pack_half(st[kb], 0);
-                pf[2 * kb + 1] = pack_half(st[kb], 1);
-            }
-
-            // O^T += V^T P^T.
-#pragma unroll
-            for (int ks = 0; ks < S::KVSTEPS; ks++)
-#pragma unroll
-                for (int db = 0; db < S::DBLK; db++) {
-                    const i16x4 lo = lds_read_tr16(vl, voff[db][0] + 16 * ks * D * 2);
-                    const i16x4 hi = lds_read_tr16(vl, voff[db][1] + 16 * ks * D * 2);
-                    acc[db] = mfma32(join_bf16x8(lo, hi), pf[ks], acc[db]);
-                }
+                for (int r = 0; r < 16; r++) acc[db][r] *= alpha;
         }
-
-        dma_barrier();  // tile t + 1 has landed in LDS; tile t is no longer read
+    };
+    // P = exp2(s * scale * log2 e - m), its fp32 row sum (four short add
+    // chains) and the bf16 B operands.  The sum uses the fp32 values: the
+    // log-sum-exp output must not inherit bf16 rounding on short rows.
+    auto exp_pack = [&](f32x16(&st)[S::NKB], bf16x8(&pf)[S::KVSTEPS]) {
+        const float msub = (m_ref == -INFINITY) ? 0.f : m_ref;
+        float ls[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < S::NKB; kb++) {
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                const float p = exp2_hw(__builtin_fmaf(st[kb][r], scale_log2, -msub));
+                st[kb][r] = p;
+                ls[r & 3] += p;
+            }
+            pf[2 * kb] = pack_half(st[kb], 0);
+            pf[2 * kb + 1] = pack_half(st[kb], 1);
+        }
+        l_part += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+    };
+    // O^T += V_t^T P_t^T.
+    auto pv = [&](const bf16x8(&pf)[S::KVSTEPS], auto slot) {
+        const char *vl = smem + S::V_BASE + decltype(slot)::value * S::V_BYTES;
+#pragma unroll
+        for (int ks = 0; ks < S::KVSTEPS; ks++)
+#pragma unroll
+            for (int db = 0; db < S::DBLK; db++) {
+                const i16x4 lo = lds_read_tr16(vl, voff[db][0] + 16 * ks * D * 2);
+                const i16x4 hi = lds_read_tr16(vl, voff[db][1] + 16 * ks * D * 2);
+                acc[db] = mfma32(join_bf16x8(lo, hi), pf[ks], acc[db]);
+            }
+    };
+    // One pipeline step for tile t (slot P = t % 2); NEXT: tile t + 1 exists.
+    auto step = [&](auto has_next, auto parity, f32x16(&cur)[S::NKB], f32x16(&nxt)[S::NKB],
+                    int t) {
+        constexpr bool NEXT = decltype(has_next)::value;
+        constexpr int P = decltype(parity)::value;
+        using Here = std::integral_constant<int, P>;
+        using There = std::integral_constant<int, 1 - P>;
+        dma_barrier();
+        if (NEXT) issue_v(t + 1, There{});
+        if (t + 2 < n_tiles) issue_k(t + 2, Here{});
+        bf16x8 pf[S::KVSTEPS];
+        if (NEXT) scores(nxt, There{});
+        exp_pack(cur, pf);
+        pv(pf, Here{});
+        if (NEXT) {
+            if (t + 1 >= n_full) apply_mask(nxt, t + 1);
+            row_max_rescale(nxt);
+        }
     };
 
+    // Prologue: K_0, V_0, K_1 in flight; S_0.
+    f32x16 sa[S::NKB], sb[S::NKB];
+    issue_k(0, Slot0{});
+    issue_v(0, Slot0{});
+    if (n_tiles > 1) issue_k(1, Slot1{});
+    dma_barrier();
+    scores(sa, Slot0{});
+    if (n_full == 0) apply_mask(sa, 0);
+    row_max_rescale(sa);
+
+    // Unrolled by two: the score registers and LDS slots alternate statically.
     int t = 0;
-    for (; t < n_full; t++) step(std::false_type{}, t);
-    for (; t < n_tiles; t++) step(std::true_type{}, t);
+    for (; t + 2 < n_tiles; t += 2) {
+        step(std::true_type{}, Slot0{}, sa, sb, t);
+        step(std::true_type{}, Slot1{}, sb, sa, t + 1);
+    }
+    if (t + 1 < n_tiles) {
+        step(std::true_type{}, Slot0{}, sa, sb, t);
+        step(std::false_type{}, Slot1{}, sb, sb, t + 1);
+    } else {
+        step(std::false_type{}, Slot0{}, sa, sa, t);
+    }
 
     // Epilogue: O = O / l, LSE = (m + log2 l) * ln 2.
-    const float l_tot = l_part + swap_halves(l_part);
+    const float l_tot = halves_sum(l_part);
     const float inv = 1.f / l_tot;
     if (qrow < N) {
         float *orow = o + (((size_t)b * Hq + hq) * N + qrow) * D;

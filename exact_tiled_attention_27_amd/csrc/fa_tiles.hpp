@@ -59,6 +59,45 @@ __device__ __forceinline__ void lds_dma16(const void *src, lds_void_t *dst)
 #endif
 }
 
+// Raw buffer resource over one head's [N][D] bf16 rows (stride 0, size in
+// bytes).  It sits in scalar registers, so a buffer copy into LDS takes a
+// per-lane 32-bit offset plus a scalar row offset and needs no per-copy
+// address arithmetic.  (The descriptor type exists only for the device
+// target; the host pass sees a placeholder of the same size.)
+struct BufRsrc {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __amdgpu_buffer_rsrc_t r;
+#else
+    uint32_t r[4];
+#endif
+};
+
+__device__ __forceinline__ BufRsrc make_rsrc(const void *base, uint32_t bytes)
+{
+    BufRsrc x;
+#if defined(__HIP_DEVICE_COMPILE__)
+    x.r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes, 0x00020000);
+#else
+    (void)base;
+    (void)bytes;
+#endif
+    return x;
+}
+
+// 16-byte buffer -> LDS copy (buffer_load_dwordx4 ... lds; LDS base from M0).
+__device__ __forceinline__ void lds_dma16_buf(const BufRsrc &rs, uint32_t voff, uint32_t soff,
+                                              lds_void_t *dst)
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.r, dst, 16, voff, soff, 0, 0);
+#else
+    (void)rs;
+    (void)voff;
+    (void)soff;
+    (void)dst;
+#endif
+}
+
 // HBM -> LDS staging of a [ROWS][D] bf16 tile without registers
 // (global_load_lds_dwordx4).  One wave instruction writes 1 KB of LDS: lane
 // L's 16 bytes land at base + 16 L, so each lane fetches the logical chunk the
@@ -105,6 +144,25 @@ struct DmaTile {
                 const uint32_t within = goff[i] - grow[i] * D * 2;
                 const char *src = reinterpret_cast<const char *>(head) + (size_t)n * D * 2 + within;
                 lds_dma16(src, (lds_void_t *)(lds + (wave * PER_WAVE + i) * 1024));
+            }
+        }
+    }
+    // The same copy from a buffer resource over the head's rows (every
+    // offset stays below N * D * 2 bytes).
+    __device__ __forceinline__ void issue(const BufRsrc &rs, int row0, int N, char *lds,
+                                          int wave) const
+    {
+        if (row0 + ROWS <= N) {
+            const uint32_t soff = (uint32_t)row0 * (D * 2);
+#pragma unroll
+            for (int i = 0; i < PER_WAVE; i++)
+                lds_dma16_buf(rs, goff[i], soff, (lds_void_t *)(lds + (wave * PER_WAVE + i) * 1024));
+        } else {
+#pragma unroll
+            for (int i = 0; i < PER_WAVE; i++) {
+                const int n = min(row0 + grow[i], N - 1);
+                const uint32_t voff = (uint32_t)n * (D * 2) + (goff[i] - grow[i] * D * 2);
+                lds_dma16_buf(rs, voff, 0u, (lds_void_t *)(lds + (wave * PER_WAVE + i) * 1024));
             }
         }
     }

@@ -38,7 +38,8 @@
  *     execution surface at the caller's next synchronisation.
  *   - Supported: d in {64, 128}; B, Hq, Hkv, N >= 1; Hq % Hkv == 0;
  *     scale > 0 and finite; every pointer 16-byte aligned; N need not be a
- *     multiple of any tile size.  Element offsets are 64-bit.
+ *     multiple of any tile size; one head's bf16 rows, N * d * 2 bytes, must
+ *     stay below 2 GiB (N < 8388608 at d = 128).  Element offsets are 64-bit.
  */
 #ifndef FA_H
 #define FA_H
@@ -53,7 +54,8 @@ extern "C" {
 typedef enum {
     FA_OK = 0,
     FA_ERR_NULL = 1,        /* a required pointer is NULL                       */
-    FA_ERR_SHAPE = 2,       /* B/Hq/Hkv/N < 1, Hq % Hkv != 0, or scale invalid  */
+    FA_ERR_SHAPE = 2,       /* B/Hq/Hkv/N < 1, Hq % Hkv != 0, N too large, or
+                               scale invalid                                   */
     FA_ERR_UNSUPPORTED = 3, /* head dimension d not in {64, 128}                */
     FA_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned                 */
     FA_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required       */

@@ -54,6 +54,8 @@ def fwd(**kw):
     (dict(Hq=3, Hkv=2), 2), (dict(scale=0.0), 2), (dict(scale=-1.0), 2),
     (dict(scale=float("inf")), 2), (dict(scale=float("nan")), 2),
     (dict(d=32), 3), (dict(d=96), 3), (dict(d=256), 3),
+    # one head's bf16 rows must stay below 2 GiB
+    (dict(N=1 << 23, d=128), 2), (dict(N=1 << 24, d=64), 2),
     (dict(q=MIS), 4), (dict(k=MIS), 4), (dict(v=MIS), 4), (dict(o=MIS), 4), (dict(lse=MIS), 4),
 ])
 def test_fwd_rejects(kw, status):
@@ -73,6 +75,7 @@ def bwd(**kw):
     (dict(lse=None), 1), (dict(dout=None), 1), (dict(dq=None), 1), (dict(dk=None), 1),
     (dict(dv=None), 1),
     (dict(B=0), 2), (dict(Hq=4, Hkv=3), 2), (dict(N=0), 2), (dict(scale=0.0), 2),
+    (dict(N=1 << 23, d=128, workspace_bytes=1 << 40), 2),
     (dict(d=80), 3),
     (dict(dq=MIS), 4), (dict(dout=MIS), 4), (dict(lse=MIS), 4),
     (dict(workspace=None), 5), (dict(workspace_bytes=0), 5), (dict(workspace_bytes=1024), 5),
