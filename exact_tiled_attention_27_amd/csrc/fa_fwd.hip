@@ -45,11 +45,12 @@ struct FwdShape {
     static constexpr int NKB = BN / 32;      // 32-key blocks of S^T
     static constexpr int KVSTEPS = BN / 16;  // k-steps of O^T += V^T P^T
     using KTile = DmaTile<BN, D, THREADS>;  // row-major K (and V) tile
-    // LDS: two K slots, then two V slots (tile t uses slot t % 2 of each).
-    static constexpr int K_BYTES = KTile::BYTES;
-    static constexpr int V_BYTES = KTile::BYTES;
-    static constexpr int V_BASE = 2 * K_BYTES;
-    static constexpr int LDS_BYTES = 2 * K_BYTES + 2 * V_BYTES;
+    // LDS: two K slots and two V slots (tile t uses slot t % 2 of each), four
+    // separate arrays.  A read from one array after a copy into another needs
+    // no wait for that copy; the compiler only proves that for distinct
+    // arrays, and would otherwise drain every copy just issued before the
+    // first transposing read of the step.
+    static constexpr int TILE_BYTES = KTile::BYTES;
 };
 
 // Software pipeline of one wave (tile t, with S_t already computed, masked,
@@ -71,7 +72,10 @@ __global__ __launch_bounds__(256, FA_FWD_MIN_WAVES) void fwd_kernel(
     int Hkv, int N, int BH, int QT, float scale_log2, float tau)
 {
     using S = FwdShape<D>;
-    extern __shared__ __attribute__((aligned(16))) char smem[];
+    __shared__ __attribute__((aligned(16))) char k_lds0[S::TILE_BYTES];
+    __shared__ __attribute__((aligned(16))) char k_lds1[S::TILE_BYTES];
+    __shared__ __attribute__((aligned(16))) char v_lds0[S::TILE_BYTES];
+    __shared__ __attribute__((aligned(16))) char v_lds1[S::TILE_BYTES];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -136,15 +140,15 @@ __global__ __launch_bounds__(256, FA_FWD_MIN_WAVES) void fwd_kernel(
     const BufRsrc krs = make_rsrc(kh, (uint32_t)N * D * 2);
     const BufRsrc vrs = make_rsrc(vh, (uint32_t)N * D * 2);
     auto issue_k = [&](int t, auto slot) {
-        kv_dma.issue(krs, t * S::BN, N, smem + decltype(slot)::value * S::K_BYTES, wave);
+        kv_dma.issue(krs, t * S::BN, N, decltype(slot)::value ? k_lds1 : k_lds0, wave);
     };
     auto issue_v = [&](int t, auto slot) {
-        kv_dma.issue(vrs, t * S::BN, N, smem + S::V_BASE + decltype(slot)::value * S::V_BYTES, wave);
+        kv_dma.issue(vrs, t * S::BN, N, decltype(slot)::value ? v_lds1 : v_lds0, wave);
     };
 
     // S^T_t = K_t Q^T (raw scores).  k-step outer: two independent chains.
     auto scores = [&](f32x16(&st)[S::NKB], auto slot) {
-        const char *kl = smem + decltype(slot)::value * S::K_BYTES;
+        const char *kl = decltype(slot)::value ? k_lds1 : k_lds0;
 #pragma unroll
         for (int s = 0; s < S::KSTEPS; s++)
 #pragma unroll
@@ -204,7 +208,7 @@ __global__ __launch_bounds__(256, FA_FWD_MIN_WAVES) void fwd_kernel(
     };
     // O^T += V_t^T P_t^T.
     auto pv = [&](const bf16x8(&pf)[S::KVSTEPS], auto slot) {
-        const char *vl = smem + S::V_BASE + decltype(slot)::value * S::V_BYTES;
+        const char *vl = decltype(slot)::value ? v_lds1 : v_lds0;
 #pragma unroll
         for (int ks = 0; ks < S::KVSTEPS; ks++)
 #pragma unroll
@@ -214,10 +218,12 @@ __global__ __launch_bounds__(256, FA_FWD_MIN_WAVES) void fwd_kernel(
                 acc[db] = mfma32(join_bf16x8(lo, hi), pf[ks], acc[db]);
             }
     };
-    // One pipeline step for tile t (slot P = t % 2); NEXT: tile t + 1 exists.
-    auto step = [&](auto has_next, auto parity, f32x16(&cur)[S::NKB], f32x16(&nxt)[S::NKB],
+    // One pipeline step for tile t (slot P = t % 2).  NEXT: 0 = tile t + 1
+    // does not exist, 1 = it needs no mask (the common case: one basic block
+    // from the copies to the next row maximum), 2 = it may need a mask.
+    auto step = [&](auto next_kind, auto parity, f32x16(&cur)[S::NKB], f32x16(&nxt)[S::NKB],
                     int t) {
-        constexpr bool NEXT = decltype(has_next)::value;
+        constexpr int NEXT = decltype(next_kind)::value;
         constexpr int P = decltype(parity)::value;
         using Here = std::integral_constant<int, P>;
         using There = std::integral_constant<int, 1 - P>;
@@ -228,11 +234,12 @@ __global__ __launch_bounds__(256, FA_FWD_MIN_WAVES) void fwd_kernel(
         if (NEXT) scores(nxt, There{});
         exp_pack(cur, pf);
         pv(pf, Here{});
-        if (NEXT) {
-            if (t + 1 >= n_full) apply_mask(nxt, t + 1);
-            row_max_rescale(nxt);
-        }
+        if (NEXT == 2 && t + 1 >= n_full) apply_mask(nxt, t + 1);
+        if (NEXT) row_max_rescale(nxt);
     };
+    using Last = std::integral_constant<int, 0>;
+    using Full = std::integral_constant<int, 1>;
+    using Any = std::integral_constant<int, 2>;
 
     // Prologue: K_0, V_0, K_1 in flight; S_0.
     f32x16 sa[S::NKB], sb[S::NKB];
@@ -245,16 +252,22 @@ __global__ __launch_bounds__(256, FA_FWD_MIN_WAVES) void fwd_kernel(
     row_max_rescale(sa);
 
     // Unrolled by two: the score registers and LDS slots alternate statically.
+    // Steps whose next tile is unmasked first, then the (at most a few)
+    // diagonal and tail tiles.
     int t = 0;
+    for (; t + 2 < n_full; t += 2) {
+        step(Full{}, Slot0{}, sa, sb, t);
+        step(Full{}, Slot1{}, sb, sa, t + 1);
+    }
     for (; t + 2 < n_tiles; t += 2) {
-        step(std::true_type{}, Slot0{}, sa, sb, t);
-        step(std::true_type{}, Slot1{}, sb, sa, t + 1);
+        step(Any{}, Slot0{}, sa, sb, t);
+        step(Any{}, Slot1{}, sb, sa, t + 1);
     }
     if (t + 1 < n_tiles) {
-        step(std::true_type{}, Slot0{}, sa, sb, t);
-        step(std::false_type{}, Slot1{}, sb, sb, t + 1);
+        step(Any{}, Slot0{}, sa, sb, t);
+        step(Last{}, Slot1{}, sb, sb, t + 1);
     } else {
-        step(std::false_type{}, Slot0{}, sa, sa, t);
+        step(Last{}, Slot0{}, sa, sa, t);
     }
 
     // Epilogue: O = O / l, LSE = (m + log2 l) * ln 2.
@@ -282,10 +295,7 @@ static hipError_t launch_fwd_t(const FwdArgs &a)
     const int QT = (a.N + S::BM - 1) / S::BM;
     const int BH = a.B * a.Hq;
     auto kern = fwd_kernel<D, CAUSAL>;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, S::LDS_BYTES);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(BH * QT), dim3(S::THREADS), S::LDS_BYTES, a.stream,
+    hipLaunchKernelGGL(kern, dim3(BH * QT), dim3(S::THREADS), 0, a.stream,
                        (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v, a.o,
                        a.lse, a.Hq, a.Hkv, a.N, BH, QT, a.scale * kLog2e, a.tau);
     return hipGetLastError();

@@ -59,43 +59,35 @@ __device__ __forceinline__ void lds_dma16(const void *src, lds_void_t *dst)
 #endif
 }
 
-// Raw buffer resource over one head's [N][D] bf16 rows (stride 0, size in
-// bytes).  It sits in scalar registers, so a buffer copy into LDS takes a
-// per-lane 32-bit offset plus a scalar row offset and needs no per-copy
-// address arithmetic.  (The descriptor type exists only for the device
-// target; the host pass sees a placeholder of the same size.)
+// Raw buffer resource over one head's [N][D] bf16 rows: base address, stride
+// 0, size in bytes, 32-bit data format.  It sits in scalar registers, so a
+// buffer copy into LDS takes a per-lane 32-bit offset plus a scalar row
+// offset and needs no per-copy address arithmetic.
 struct BufRsrc {
-#if defined(__HIP_DEVICE_COMPILE__)
-    __amdgpu_buffer_rsrc_t r;
-#else
-    uint32_t r[4];
-#endif
+    int r __attribute__((ext_vector_type(4)));
 };
 
 __device__ __forceinline__ BufRsrc make_rsrc(const void *base, uint32_t bytes)
 {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
     BufRsrc x;
-#if defined(__HIP_DEVICE_COMPILE__)
-    x.r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes, 0x00020000);
-#else
-    (void)base;
-    (void)bytes;
-#endif
+    x.r[0] = (int)(uint32_t)a;
+    x.r[1] = (int)((a >> 32) & 0xffffu);  // stride 0, no swizzle
+    x.r[2] = (int)bytes;
+    x.r[3] = 0x00020000;
     return x;
 }
 
-// 16-byte buffer -> LDS copy (buffer_load_dwordx4 ... lds; LDS base from M0).
+// 16-byte buffer -> LDS copy (buffer_load_dwordx4 ... lds; LDS base in M0).
+// Issued as inline assembly so that the compiler does not wait for it before
+// unrelated LDS reads; completion is awaited explicitly (dma_barrier).  The
+// s_nop covers the M0-write -> LDS-DMA hazard.
 __device__ __forceinline__ void lds_dma16_buf(const BufRsrc &rs, uint32_t voff, uint32_t soff,
                                               lds_void_t *dst)
 {
-#if defined(__HIP_DEVICE_COMPILE__)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.r, dst, 16, voff, soff, 0, 0);
-#else
-    (void)rs;
-    (void)voff;
-    (void)soff;
-    (void)dst;
-#endif
+    const uint32_t m0 = (uint32_t)reinterpret_cast<uintptr_t>(dst);
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :: "{m0}"(m0), "v"(voff), "s"(rs.r), "s"(soff) : "memory");
 }
 
 // HBM -> LDS staging of a [ROWS][D] bf16 tile without registers
