@@ -231,7 +231,6 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
     dma_barrier();
 
     for (int st = 0; st < n_steps; st++) {
-        const int hq = g * grp + st / steps_per_head;
         const int qs = (first_qt + st % steps_per_head) * S::BM;
         const char *stage = smem + S::OFF_STAGE + (st & 1) * S::STAGE;
         const char *ql = stage;
@@ -349,7 +348,9 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
 //                       dS = P (dP - D), dK^T += Q^T dS.
 // Each wave holds one operand set and one accumulator set (about 200
 // registers), so two waves fit per SIMD and the MFMA phases of one overlap
-// the exponent / elementwise phases of the other.
+// the exponent / elementwise phases of the other.  The Q, dO and row stages
+// live in separate LDS arrays per slot (step st uses slot st % 2), so reads of
+// one slot never wait for the copies into the other.
 template <int D>
 struct DkdvSplitShape {
     static constexpr int BN = 128;   // keys per workgroup (32 per wave pair)
@@ -359,11 +360,8 @@ struct DkdvSplitShape {
     static constexpr int DBLK = D / 32;
     using QTile = DmaTile<BM, D, THREADS>;
     static constexpr int TILE = BM * D * 2;
-    static constexpr int ROWS = 2 * TILE;                  // LSE2[BM], then D[BM] (fp32)
-    static constexpr int STAGE = 2 * TILE + 2 * BM * 4;    // Q, dO, rows
-    static constexpr int OFF_X = 2 * STAGE;                // P exchange: 4 slices x 64 lanes x 32 fp32
-    static constexpr int X_SLICE = 64 * 32 * 4;
-    static constexpr int LDS_BYTES = OFF_X + 4 * X_SLICE;
+    static constexpr int ROWS_BYTES = 2 * BM * 4;          // LSE2[BM], then D[BM] (fp32)
+    static constexpr int X_SLICE = 64 * 32 * 4;            // P exchange per slice: 64 lanes x 32 fp32
 };
 
 template <int D, bool CAUSAL>
@@ -375,9 +373,16 @@ __global__ __launch_bounds__(512) void bwd_dkdv_split_kernel(
     float scale_log2)
 {
     using S = DkdvSplitShape<D>;
-    extern __shared__ __attribute__((aligned(16))) char smem[];
+    __shared__ __attribute__((aligned(16))) char q_lds0[S::TILE];
+    __shared__ __attribute__((aligned(16))) char q_lds1[S::TILE];
+    __shared__ __attribute__((aligned(16))) char do_lds0[S::TILE];
+    __shared__ __attribute__((aligned(16))) char do_lds1[S::TILE];
+    __shared__ __attribute__((aligned(16))) char rows0[S::ROWS_BYTES];
+    __shared__ __attribute__((aligned(16))) char rows1[S::ROWS_BYTES];
+    __shared__ __attribute__((aligned(16))) char xchg_lds[4 * S::X_SLICE];
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int slice = wave & 3;
     const bool wave_a = wave < 4;
     const int h = lane >> 5, col = lane & 31;
@@ -413,7 +418,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_split_kernel(
 #pragma unroll
         for (int rho = 0; rho < 2; rho++)
             troff[db][rho] = tr_off(8 * rho + 4 * h, 32 * db + 16 * (g16 & 1), lane, D);
-    char *xchg = smem + S::OFF_X + slice * S::X_SLICE + lane * 16;  // + (qb*4 + gq) * 1024
+    char *xchg = xchg_lds + slice * S::X_SLICE + lane * 16;  // + (qb*4 + gq) * 1024
 
     const int first_qt = CAUSAL ? kv0 / S::BM : 0;
     const int n_qt = (N + S::BM - 1) / S::BM;
@@ -422,40 +427,43 @@ __global__ __launch_bounds__(512) void bwd_dkdv_split_kernel(
 
     typename S::QTile qtile;
     qtile.init(wave, lane);
-    auto issue = [&](int st, char *stage) {
+    // Step st's tiles: Q and dO rows qs .. qs + 63 of query head hq, and the
+    // tile's LSE2 and D rows (padded workspace, always in range): wave 0's
+    // lanes 0-15 fetch LSE2, lanes 16-31 fetch D, 16 bytes each.
+    auto issue = [&](int st, auto slot) {
+        constexpr int P = decltype(slot)::value;
         const int hq = g * grp + st / steps_per_head;
         const int qs = (first_qt + st % steps_per_head) * S::BM;
         const size_t ho = ((size_t)b * Hq + hq) * N;
-        qtile.issue(q + ho * D, qs, N, stage, wave);
-        qtile.issue(dout + ho * D, qs, N, stage + S::TILE, wave);
-        if (wave == 0 && lane < 32) {
-            const size_t r0 = ((size_t)b * Hq + hq) * NP + qs + 4 * (lane & 15);
-            lds_dma16(lane < 16 ? (const void *)(lse2 + r0) : (const void *)(delta + r0),
-                      (lds_void_t *)(stage + S::ROWS));
+        qtile.issue(make_rsrc(q + ho * D, (uint32_t)N * D * 2), qs, N, P ? q_lds1 : q_lds0, wave);
+        qtile.issue(make_rsrc(dout + ho * D, (uint32_t)N * D * 2), qs, N, P ? do_lds1 : do_lds0, wave);
+        if (wave == 0) {
+            const size_t hrow = ((size_t)b * Hq + hq) * NP;
+            lds_void_t *dst = (lds_void_t *)(P ? rows1 : rows0);
+            if (lane < 16)
+                lds_dma16_buf(make_rsrc(lse2 + hrow, (uint32_t)NP * 4), 16 * lane, qs * 4, dst);
+            else if (lane < 32)
+                lds_dma16_buf(make_rsrc(delta + hrow, (uint32_t)NP * 4), 16 * (lane - 16), qs * 4, dst);
         }
     };
-    if (n_steps > 0) issue(0, smem);
-    dma_barrier();
 
-    for (int st = 0; st < n_steps; st++) {
+    auto step = [&](auto slot, int st) {
+        constexpr int P = decltype(slot)::value;
         const int qs = (first_qt + st % steps_per_head) * S::BM;
-        const char *stage = smem + (st & 1) * S::STAGE;
-        const char *ql = stage;
-        const char *dol = stage + S::TILE;
-        if (st + 1 < n_steps) issue(st + 1, smem + ((st + 1) & 1) * S::STAGE);
+        const char *ql = P ? q_lds1 : q_lds0;
+        const char *dol = P ? do_lds1 : do_lds0;
+        const char *rows = P ? rows1 : rows0;
+        if (st + 1 < n_steps) issue(st + 1, std::integral_constant<int, 1 - P>{});
 
         // A: S = Q K^T.  B: dP = dO V^T.  (rows = queries, one key per lane)
         const char *rl = wave_a ? ql : dol;
         f32x16 x[2];
 #pragma unroll
-        for (int qb = 0; qb < 2; qb++)
-#pragma unroll
-            for (int r = 0; r < 16; r++) x[qb][r] = 0.f;
-#pragma unroll
         for (int s = 0; s < S::KSTEPS; s++)
 #pragma unroll
             for (int qb = 0; qb < 2; qb++)
-                x[qb] = mfma32(lds_read_bf16x8(rl, rowoff[s] + qb * 32 * D * 2), kvf[s], x[qb]);
+                x[qb] = mfma32(lds_read_bf16x8(rl, rowoff[s] + qb * 32 * D * 2), kvf[s],
+                               s == 0 ? f32x16{} : x[qb]);
 
         if (wave_a) {
             // P = exp2(s * c - LSE2); masked pairs get a -inf exponent.
@@ -467,7 +475,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_split_kernel(
 #pragma unroll
                     for (int gq = 0; gq < 4; gq++) {
                         const int qr = 32 * qb + 8 * gq + 4 * h;
-                        const f32x4 l2 = lds_read_f32x4(stage + S::ROWS, qr * 4);
+                        const f32x4 l2 = lds_read_f32x4(rows, qr * 4);
 #pragma unroll
                         for (int i = 0; i < 4; i++) {
                             float e = __builtin_fmaf(x[qb][4 * gq + i], scale_log2, -l2[i]);
@@ -502,7 +510,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_split_kernel(
 #pragma unroll
                 for (int gq = 0; gq < 4; gq++) {
                     const int qr = 32 * qb + 8 * gq + 4 * h;
-                    const f32x4 dl = lds_read_f32x4(stage + S::ROWS, (S::BM + qr) * 4);
+                    const f32x4 dl = lds_read_f32x4(rows, (S::BM + qr) * 4);
                     const f32x4 pv = *reinterpret_cast<const f32x4 *>(xchg + (qb * 4 + gq) * 1024);
 #pragma unroll
                     for (int i = 0; i < 4; i++) x[qb][4 * gq + i] = pv[i] * (x[qb][4 * gq + i] - dl[i]);
@@ -522,7 +530,20 @@ __global__ __launch_bounds__(512) void bwd_dkdv_split_kernel(
                 acc[db] = mfma32(join_bf16x8(lds_read_tr16(tl, o0), lds_read_tr16(tl, o1)), bop[ks], acc[db]);
             }
         dma_barrier();  // next stage landed; this stage and the exchange are free
+    };
+    using Slot0 = std::integral_constant<int, 0>;
+    using Slot1 = std::integral_constant<int, 1>;
+
+#pragma unroll
+    for (int s = 0; s < S::KSTEPS; s++) settle(kvf[s]);
+    if (n_steps > 0) issue(0, Slot0{});
+    dma_barrier();
+    int st = 0;
+    for (; st + 2 <= n_steps; st += 2) {
+        step(Slot0{}, st);
+        step(Slot1{}, st + 1);
     }
+    if (st < n_steps) step(Slot0{}, st);
 
     if (key < N) {
         float *out = (wave_a ? dv : dk) + (((size_t)b * Hkv + g) * N + key) * D;
@@ -548,10 +569,10 @@ struct DqShape {
     static constexpr int DBLK = D / 32;
     using Tile = DmaTile<BN, D, THREADS>;   // K and V tiles, row-major
     static constexpr int TILE = BN * D * 2;
-    static constexpr int BUF_BYTES = 2 * TILE;   // K, V
-    static constexpr int LDS_BYTES = 2 * BUF_BYTES;
 };
 
+// K and V tiles live in four separate LDS arrays (slot t % 2 of each), so
+// that reads of one slot never wait for the copies into the other.
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, FA_DQ_MIN_WAVES) void bwd_dq_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
@@ -560,9 +581,13 @@ __global__ __launch_bounds__(256, FA_DQ_MIN_WAVES) void bwd_dq_kernel(
     int Hq, int Hkv, int N, int BH, int QT, float scale, float scale_log2)
 {
     using S = DqShape<D>;
-    extern __shared__ __attribute__((aligned(16))) char smem[];
+    __shared__ __attribute__((aligned(16))) char k_lds0[S::TILE];
+    __shared__ __attribute__((aligned(16))) char k_lds1[S::TILE];
+    __shared__ __attribute__((aligned(16))) char v_lds0[S::TILE];
+    __shared__ __attribute__((aligned(16))) char v_lds1[S::TILE];
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h = lane >> 5, col = lane & 31;
     const int g16 = lane >> 4;
 
@@ -571,8 +596,7 @@ __global__ __launch_bounds__(256, FA_DQ_MIN_WAVES) void bwd_dq_kernel(
     const int b = bh / Hq, hq = bh % Hq;
     const int g = hq / (Hq / Hkv);
     const int q0 = qt * S::BM;
-    const int qw0 = q0 + wave * 32;
-    const int qrow = qw0 + col;
+    const int qrow = q0 + wave * 32 + col;
     const size_t head_off = ((size_t)b * Hq + hq) * N;
 
     const uint16_t *qh = q + head_off * D;
@@ -612,75 +636,89 @@ __global__ __launch_bounds__(256, FA_DQ_MIN_WAVES) void bwd_dq_kernel(
     const int n_tiles_all = (N + S::BN - 1) / S::BN;
     const int n_tiles = CAUSAL ? min(n_tiles_all, (min(q0 + S::BM, N) + S::BN - 1) / S::BN)
                                : n_tiles_all;
+    // Tiles every key of which is < N and (causal) <= q0 need no mask.
+    const int n_full = CAUSAL ? min(N / S::BN, (q0 + 1) / S::BN) : N / S::BN;
+
     typename S::Tile tile;
     tile.init(wave, lane);
-    auto issue = [&](int t, char *buf) {
-        tile.issue(kh, t * S::BN, N, buf, wave);
-        tile.issue(vh, t * S::BN, N, buf + S::TILE, wave);
+    const BufRsrc krs = make_rsrc(kh, (uint32_t)N * D * 2);
+    const BufRsrc vrs = make_rsrc(vh, (uint32_t)N * D * 2);
+    auto issue = [&](int t, auto slot) {
+        constexpr int P = decltype(slot)::value;
+        tile.issue(krs, t * S::BN, N, P ? k_lds1 : k_lds0, wave);
+        tile.issue(vrs, t * S::BN, N, P ? v_lds1 : v_lds0, wave);
     };
-    issue(0, smem);
-    dma_barrier();
 
-    for (int t = 0; t < n_tiles; t++) {
+    // One key tile t in slot P: S^T = K Q^T, dP^T = V dO^T, P^T, dS^T, then
+    // dQ^T += K^T dS^T.  Tile t + 1 is copied into the other slot meanwhile.
+    auto step = [&](auto masked, auto slot, int t) {
+        constexpr bool MASK = decltype(masked)::value;
+        constexpr int P = decltype(slot)::value;
         const int key0 = t * S::BN;
-        if (t + 1 < n_tiles) issue(t + 1, smem + ((t + 1) & 1) * S::BUF_BYTES);
-        const char *kl = smem + (t & 1) * S::BUF_BYTES;
-        const char *vl = kl + S::TILE;
-        if (!CAUSAL || key0 <= qw0 + 31) {
-            f32x16 st[2], dpt[2];
+        if (t + 1 < n_tiles) issue(t + 1, std::integral_constant<int, 1 - P>{});
+        const char *kl = P ? k_lds1 : k_lds0;
+        const char *vl = P ? v_lds1 : v_lds0;
+        f32x16 st[2], dpt[2];
 #pragma unroll
-            for (int kb = 0; kb < 2; kb++)
-#pragma unroll
-                for (int r = 0; r < 16; r++) st[kb][r] = dpt[kb][r] = 0.f;
-#pragma unroll
-            for (int s = 0; s < S::KSTEPS; s++)
-#pragma unroll
-                for (int kb = 0; kb < 2; kb++) {
-                    const uint32_t ro = rowoff[s] + kb * 32 * D * 2;
-                    st[kb] = mfma32(lds_read_bf16x8(kl, ro), qf[s], st[kb]);
-                    dpt[kb] = mfma32(lds_read_bf16x8(vl, ro), df[s], dpt[kb]);
-                }
-            // Keys >= N and (causal) keys after the query get a -inf exponent;
-            // only tiles that contain such keys for this workgroup evaluate it.
-            const bool need_mask = key0 + S::BN > N || (CAUSAL && key0 + S::BN - 1 > q0);
-            auto softmax = [&](auto masked) {
-                constexpr bool MASK = decltype(masked)::value;
-#pragma unroll
-                for (int kb = 0; kb < 2; kb++)
-#pragma unroll
-                    for (int r = 0; r < 16; r++) {
-                        float x = __builtin_fmaf(st[kb][r], scale_log2, -l2);
-                        if (MASK) {
-                            const int kk = key0 + kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                            const bool dead = kk >= N || (CAUSAL && kk > qrow);
-                            x = dead ? -INFINITY : x;
-                        }
-                        const float p = exp2_hw(x);
-                        dpt[kb][r] = p * (dpt[kb][r] - dl);
-                    }
-            };
-            if (need_mask)
-                softmax(std::true_type{});
-            else
-                softmax(std::false_type{});
-            bf16x8 dsf[S::BN / 16];
+        for (int s = 0; s < S::KSTEPS; s++)
 #pragma unroll
             for (int kb = 0; kb < 2; kb++) {
-                dsf[2 * kb] = pack_half(dpt[kb], 0);
-                dsf[2 * kb + 1] = pack_half(dpt[kb], 1);
+                const uint32_t ro = rowoff[s] + kb * 32 * D * 2;
+                st[kb] = mfma32(lds_read_bf16x8(kl, ro), qf[s], s == 0 ? f32x16{} : st[kb]);
+                dpt[kb] = mfma32(lds_read_bf16x8(vl, ro), df[s], s == 0 ? f32x16{} : dpt[kb]);
             }
-            // dQ^T += K^T dS^T (contraction over the tile's keys).
+        // Keys >= N and (causal) keys after the query get a -inf exponent.
+        bf16x8 dsf[S::BN / 16];
 #pragma unroll
-            for (int ks = 0; ks < S::BN / 16; ks++)
+        for (int kb = 0; kb < 2; kb++) {
 #pragma unroll
-                for (int db = 0; db < S::DBLK; db++) {
-                    const i16x4 lo = lds_read_tr16(kl, troff[db][0] + 16 * ks * D * 2);
-                    const i16x4 hi = lds_read_tr16(kl, troff[db][1] + 16 * ks * D * 2);
-                    acc[db] = mfma32(join_bf16x8(lo, hi), dsf[ks], acc[db]);
+            for (int r = 0; r < 16; r++) {
+                float x = __builtin_fmaf(st[kb][r], scale_log2, -l2);
+                if (MASK) {
+                    const int kk = key0 + kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                    const bool dead = kk >= N || (CAUSAL && kk > qrow);
+                    x = dead ? -INFINITY : x;
                 }
+                dpt[kb][r] = exp2_hw(x) * (dpt[kb][r] - dl);
+            }
+            dsf[2 * kb] = pack_half(dpt[kb], 0);
+            dsf[2 * kb + 1] = pack_half(dpt[kb], 1);
         }
-        dma_barrier();
+        // dQ^T += K^T dS^T (contraction over the tile's keys).
+#pragma unroll
+        for (int ks = 0; ks < S::BN / 16; ks++)
+#pragma unroll
+            for (int db = 0; db < S::DBLK; db++) {
+                const i16x4 lo = lds_read_tr16(kl, troff[db][0] + 16 * ks * D * 2);
+                const i16x4 hi = lds_read_tr16(kl, troff[db][1] + 16 * ks * D * 2);
+                acc[db] = mfma32(join_bf16x8(lo, hi), dsf[ks], acc[db]);
+            }
+        dma_barrier();  // tile t + 1 landed; slot P is free
+    };
+    using Slot0 = std::integral_constant<int, 0>;
+    using Slot1 = std::integral_constant<int, 1>;
+
+#pragma unroll
+    for (int s = 0; s < S::KSTEPS; s++) {
+        settle(qf[s]);
+        settle(df[s]);
     }
+    settle(l2);
+    settle(dl);
+    issue(0, Slot0{});
+    dma_barrier();
+    // Unrolled by two so that LDS slots are compile-time constants; unmasked
+    // tiles first, then the diagonal and tail tiles.
+    int t = 0;
+    for (; t + 2 <= n_full; t += 2) {
+        step(std::false_type{}, Slot0{}, t);
+        step(std::false_type{}, Slot1{}, t + 1);
+    }
+    for (; t + 2 <= n_tiles; t += 2) {
+        step(std::true_type{}, Slot0{}, t);
+        step(std::true_type{}, Slot1{}, t + 1);
+    }
+    if (t < n_tiles) step(std::true_type{}, Slot0{}, t);
 
     if (qrow < N) {
         float *dqr = dq + (head_off + qrow) * D;
@@ -727,8 +765,7 @@ static hipError_t launch_bwd_t(const BwdArgs &a)
         if (a.deterministic) {
             using SS = DkdvSplitShape<D>;
             auto kern = bwd_dkdv_split_kernel<D, CAUSAL>;
-            if ((e = set_lds(kern, SS::LDS_BYTES)) != hipSuccess) return e;
-            hipLaunchKernelGGL(kern, dim3(BHkv * KT), dim3(SS::THREADS), SS::LDS_BYTES, a.stream,
+            hipLaunchKernelGGL(kern, dim3(BHkv * KT), dim3(SS::THREADS), 0, a.stream,
                                (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v,
                                (const uint16_t *)a.dout, a.lse2, a.delta, a.dk, a.dv, a.Hq, a.Hkv,
                                a.N, BHkv, KT, a.scale, scale_log2);
@@ -747,8 +784,7 @@ static hipError_t launch_bwd_t(const BwdArgs &a)
         const int QT = (a.N + S::BM - 1) / S::BM;
         auto kern = bwd_dq_kernel<D, CAUSAL>;
         hipError_t e;
-        if ((e = set_lds(kern, S::LDS_BYTES)) != hipSuccess) return e;
-        hipLaunchKernelGGL(kern, dim3(BH * QT), dim3(S::THREADS), S::LDS_BYTES, a.stream,
+        hipLaunchKernelGGL(kern, dim3(BH * QT), dim3(S::THREADS), 0, a.stream,
                            (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v,
                            (const uint16_t *)a.dout, a.lse2, a.delta, a.dq, a.Hq, a.Hkv, a.N, BH,
                            QT, a.scale, scale_log2);

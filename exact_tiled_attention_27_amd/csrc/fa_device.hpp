@@ -93,6 +93,17 @@ __device__ __forceinline__ u32x4 gload16(const void *base, size_t byte_off, bool
     return ok ? *reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(base) + byte_off) : z;
 }
 
+// Make the compiler wait for the loads that produced `x` here.  Tile copies
+// issued as inline assembly are invisible to its wait counting, so a load of
+// its own still in flight at the first copy would later be waited for with a
+// count that also drains those copies; kernels settle their own loads with
+// this before the first copy.
+template <typename T>
+__device__ __forceinline__ void settle(const T &x)
+{
+    asm volatile("" ::"v"(x));
+}
+
 // Workgroup barrier that only hands off LDS: waits for this wave's LDS
 // operations, not for its outstanding global loads, stores or atomics (a plain
 // __syncthreads() also drains those, which would stall every loop iteration on

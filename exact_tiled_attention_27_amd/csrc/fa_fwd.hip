@@ -243,6 +243,8 @@ __global__ __launch_bounds__(256, FA_FWD_MIN_WAVES) void fwd_kernel(
 
     // Prologue: K_0, V_0, K_1 in flight; S_0.
     f32x16 sa[S::NKB], sb[S::NKB];
+#pragma unroll
+    for (int s = 0; s < S::KSTEPS; s++) settle(qf[s]);
     issue_k(0, Slot0{});
     issue_v(0, Slot0{});
     if (n_tiles > 1) issue_k(1, Slot1{});
