@@ -458,12 +458,26 @@ __global__ __launch_bounds__(512) void bwd_dkdv_split_kernel(
         // A: S = Q K^T.  B: dP = dO V^T.  (rows = queries, one key per lane)
         const char *rl = wave_a ? ql : dol;
         f32x16 x[2];
+        // Operands read two k-steps ahead of the products that use them.
+        bf16x8 ra[S::KSTEPS][2];
 #pragma unroll
-        for (int s = 0; s < S::KSTEPS; s++)
+        for (int s = 0; s < 2; s++)
 #pragma unroll
-            for (int qb = 0; qb < 2; qb++)
-                x[qb] = mfma32(lds_read_bf16x8(rl, rowoff[s] + qb * 32 * D * 2), kvf[s],
-                               s == 0 ? f32x16{} : x[qb]);
+            for (int qb = 0; qb < 2; qb++) ra[s][qb] = lds_read_bf16x8(rl, rowoff[s] + qb * 32 * D * 2);
+#pragma unroll
+        for (int s = 0; s < S::KSTEPS; s++) {
+            if (s + 2 < S::KSTEPS) {
+#pragma unroll
+                for (int qb = 0; qb < 2; qb++)
+                    ra[s + 2][qb] = lds_read_bf16x8(rl, rowoff[s + 2] + qb * 32 * D * 2);
+            }
+#pragma unroll
+            for (int qb = 0; qb < 2; qb++) {
+                x[qb] = mfma32(ra[s][qb], kvf[s], s == 0 ? f32x16{} : x[qb]);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // two LDS reads
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // then one product
+            }
+        }
 
         if (wave_a) {
             // P = exp2(s * c - LSE2); masked pairs get a -inf exponent.
@@ -658,41 +672,64 @@ __global__ __launch_bounds__(256, FA_DQ_MIN_WAVES) void bwd_dq_kernel(
         if (t + 1 < n_tiles) issue(t + 1, std::integral_constant<int, 1 - P>{});
         const char *kl = P ? k_lds1 : k_lds0;
         const char *vl = P ? v_lds1 : v_lds0;
-        f32x16 st[2], dpt[2];
-#pragma unroll
-        for (int s = 0; s < S::KSTEPS; s++)
-#pragma unroll
-            for (int kb = 0; kb < 2; kb++) {
-                const uint32_t ro = rowoff[s] + kb * 32 * D * 2;
-                st[kb] = mfma32(lds_read_bf16x8(kl, ro), qf[s], s == 0 ? f32x16{} : st[kb]);
-                dpt[kb] = mfma32(lds_read_bf16x8(vl, ro), df[s], s == 0 ? f32x16{} : dpt[kb]);
-            }
+        // One 32-key block at a time: S^T and dP^T of block kb (two product
+        // chains, operands read two k-steps ahead), then its P^T and dS^T.
         // Keys >= N and (causal) keys after the query get a -inf exponent.
         bf16x8 dsf[S::BN / 16];
 #pragma unroll
         for (int kb = 0; kb < 2; kb++) {
+            f32x16 st, dpt;
+            bf16x8 ka[S::KSTEPS], va[S::KSTEPS];
+#pragma unroll
+            for (int s = 0; s < 2; s++) {
+                ka[s] = lds_read_bf16x8(kl, rowoff[s] + kb * 32 * D * 2);
+                va[s] = lds_read_bf16x8(vl, rowoff[s] + kb * 32 * D * 2);
+            }
+#pragma unroll
+            for (int s = 0; s < S::KSTEPS; s++) {
+                if (s + 2 < S::KSTEPS) {
+                    ka[s + 2] = lds_read_bf16x8(kl, rowoff[s + 2] + kb * 32 * D * 2);
+                    va[s + 2] = lds_read_bf16x8(vl, rowoff[s + 2] + kb * 32 * D * 2);
+                }
+                st = mfma32(ka[s], qf[s], s == 0 ? f32x16{} : st);
+                dpt = mfma32(va[s], df[s], s == 0 ? f32x16{} : dpt);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // two LDS reads
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // then two products
+            }
 #pragma unroll
             for (int r = 0; r < 16; r++) {
-                float x = __builtin_fmaf(st[kb][r], scale_log2, -l2);
+                float x = __builtin_fmaf(st[r], scale_log2, -l2);
                 if (MASK) {
                     const int kk = key0 + kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
                     const bool dead = kk >= N || (CAUSAL && kk > qrow);
                     x = dead ? -INFINITY : x;
                 }
-                dpt[kb][r] = exp2_hw(x) * (dpt[kb][r] - dl);
+                dpt[r] = exp2_hw(x) * (dpt[r] - dl);
             }
-            dsf[2 * kb] = pack_half(dpt[kb], 0);
-            dsf[2 * kb + 1] = pack_half(dpt[kb], 1);
+            dsf[2 * kb] = pack_half(dpt, 0);
+            dsf[2 * kb + 1] = pack_half(dpt, 1);
         }
-        // dQ^T += K^T dS^T (contraction over the tile's keys).
+        // dQ^T += K^T dS^T (contraction over the tile's keys), transposing
+        // reads two products ahead.
+        constexpr int NP2 = (S::BN / 16) * S::DBLK;
+        i16x4 tl[NP2][2];
 #pragma unroll
-        for (int ks = 0; ks < S::BN / 16; ks++)
-#pragma unroll
-            for (int db = 0; db < S::DBLK; db++) {
-                const i16x4 lo = lds_read_tr16(kl, troff[db][0] + 16 * ks * D * 2);
-                const i16x4 hi = lds_read_tr16(kl, troff[db][1] + 16 * ks * D * 2);
-                acc[db] = mfma32(join_bf16x8(lo, hi), dsf[ks], acc[db]);
+        for (int i = 0; i < NP2; i++) {
+            const int ks = i / S::DBLK, db = i % S::DBLK;
+            tl[i][0] = lds_read_tr16(kl, troff[db][0] + 16 * ks * D * 2);
+            tl[i][1] = lds_read_tr16(kl, troff[db][1] + 16 * ks * D * 2);
+            if (i >= 2) {
+                const int j = i - 2, ksj = j / S::DBLK, dbj = j % S::DBLK;
+                acc[dbj] = mfma32(join_bf16x8(tl[j][0], tl[j][1]), dsf[ksj], acc[dbj]);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);  // two transposing reads
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);  // then one product
             }
+        }
+#pragma unroll
+        for (int j = NP2 - 2; j < NP2; j++) {
+            const int ksj = j / S::DBLK, dbj = j % S::DBLK;
+            acc[dbj] = mfma32(join_bf16x8(tl[j][0], tl[j][1]), dsf[ksj], acc[dbj]);
+        }
         dma_barrier();  // tile t + 1 landed; slot P is free
     };
     using Slot0 = std::integral_constant<int, 0>;
