@@ -4,6 +4,8 @@
 #include "fa.h"
 
 #include <cmath>
+#include <cstdlib>
+#include <cstring>
 #include <cstdint>
 
 #include "fa_launch.hpp"
@@ -35,6 +37,18 @@ size_t workspace_rows(int B, int Hq, int N) { return (size_t)B * Hq * (size_t)((
 
 int hip_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
 
+// FA_EXP2_POLY selects how many of the forward's exponentials run as the
+// cubic polynomial on the FMA units: "1" all, "4" one in four, anything else
+// (or unset) none.  Read on every call.
+int exp2_poly_share()
+{
+    const char *e = std::getenv("FA_EXP2_POLY");
+    if (!e) return 0;
+    if (std::strcmp(e, "1") == 0) return 1;
+    if (std::strcmp(e, "4") == 0) return 4;
+    return 0;
+}
+
 }  // namespace
 
 extern "C" {
@@ -63,7 +77,7 @@ int fa_fwd(const void *q, const void *k, const void *v, float *o, float *lse, in
         (lse && !aligned16(lse)))
         return FA_ERR_ALIGN;
     fa::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, N, d, scale, fa::kRescaleTau, causal != 0,
-                  reinterpret_cast<hipStream_t>(stream)};
+                  exp2_poly_share(), reinterpret_cast<hipStream_t>(stream)};
     return hip_status(fa::launch_fwd(a));
 }
 

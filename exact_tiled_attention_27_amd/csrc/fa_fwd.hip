@@ -26,6 +26,7 @@
 #include <type_traits>
 
 #include "fa_device.hpp"
+#include "fa_exp2_poly.hpp"
 #include "fa_launch.hpp"
 #include "fa_tiles.hpp"
 
@@ -65,7 +66,12 @@ struct FwdShape {
 // The exponentials of one tile thus overlap the score products of the next
 // (the overlap the FlashAttention-4 guide obtains with separate softmax and
 // MMA warps), inside each wave and without extra barriers.
-template <int D, bool CAUSAL>
+// POLY: share of the exponentials computed by the cubic polynomial on the FMA
+// units (FlashAttention-4 summary page, Key Contributions, item 2): 0 none,
+// 4 one in four (score rows r % 4 == 3), 1 all.  v_exp_f32 issues at half the
+// VALU rate on gfx950 and the polynomial costs about seven full-rate
+// operations, so the default is none.
+template <int D, bool CAUSAL, int POLY>
 __global__ __launch_bounds__(256, FA_FWD_MIN_WAVES) void fwd_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, float *__restrict__ o, float *__restrict__ lse, int Hq,
@@ -197,7 +203,9 @@ __global__ __launch_bounds__(256, FA_FWD_MIN_WAVES) void fwd_kernel(
         for (int kb = 0; kb < S::NKB; kb++) {
 #pragma unroll
             for (int r = 0; r < 16; r++) {
-                const float p = exp2_hw(__builtin_fmaf(st[kb][r], scale_log2, -msub));
+                const float x = __builtin_fmaf(st[kb][r], scale_log2, -msub);
+                const bool on_fma = POLY == 1 || (POLY == 4 && (r & 3) == 3);
+                const float p = on_fma ? exp2_poly(x) : exp2_hw(x);
                 st[kb][r] = p;
                 ls[r & 3] += p;
             }
@@ -296,7 +304,9 @@ static hipError_t launch_fwd_t(const FwdArgs &a)
     (void)hipGetLastError();  // clear an error left by an earlier, unrelated call
     const int QT = (a.N + S::BM - 1) / S::BM;
     const int BH = a.B * a.Hq;
-    auto kern = fwd_kernel<D, CAUSAL>;
+    auto kern = a.poly == 1 ? fwd_kernel<D, CAUSAL, 1>
+              : a.poly == 4 ? fwd_kernel<D, CAUSAL, 4>
+                            : fwd_kernel<D, CAUSAL, 0>;
     hipLaunchKernelGGL(kern, dim3(BH * QT), dim3(S::THREADS), 0, a.stream,
                        (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v, a.o,
                        a.lse, a.Hq, a.Hkv, a.N, BH, QT, a.scale * kLog2e, a.tau);

@@ -13,6 +13,7 @@ struct FwdArgs {
     float scale;   // > 0
     float tau;     // rescale threshold in the base-2 exponent domain
     bool causal;
+    int poly;      // exponentials on the FMA units: 0 none, 4 one in four, 1 all
     hipStream_t stream;
 };
 

@@ -36,6 +36,11 @@
  *     without any host synchronisation.  Argument errors return before any
  *     work is enqueued.  A launch failure returns FA_ERR_HIP; faults during
  *     execution surface at the caller's next synchronisation.
+ *   - The environment variable FA_EXP2_POLY, read on every fa_fwd call,
+ *     moves forward exponentials from the transcendental unit to a cubic
+ *     polynomial on the FMA units (page "FlashAttention-4", Key Contributions
+ *     item 2): "1" all of them, "4" one in four; unset or any other value,
+ *     none (the default, and the faster choice on this chip).
  *   - Supported: d in {64, 128}; B, Hq, Hkv, N >= 1; Hq % Hkv == 0;
  *     scale > 0 and finite; every pointer 16-byte aligned; N need not be a
  *     multiple of any tile size; one head's bf16 rows, N * d * 2 bytes, must

@@ -226,6 +226,36 @@ def test_workload_forward(fa, name):
     compare_lse(lse.reshape(-1)[rows], lse_ref)
 
 
+@pytest.mark.parametrize("share", ["1", "4"])
+@pytest.mark.parametrize("N,d,causal", [(3, 64, True), (129, 128, False), (300, 128, True), (300, 64, False)])
+def test_fwd_small_exp2_polynomial(fa, monkeypatch, share, N, d, causal):
+    """The forward with all (share 1) or one in four (share 4) exponentials
+    computed by the cubic polynomial on the FMA units (FA_EXP2_POLY)."""
+    monkeypatch.setenv("FA_EXP2_POLY", share)
+    B, Hq, Hkv = sweep_shape(N)
+    note(f"fwd poly share={share} B={B} Hq={Hq} Hkv={Hkv} N={N} d={d} causal={causal}")
+    q, k, v = random_bf16((B, Hq, N, d), N), random_bf16((B, Hkv, N, d), N + 1), random_bf16((B, Hkv, N, d), N + 2)
+    scale = 1 / math.sqrt(d)
+    o, lse = gpu_fwd(fa, q, k, v, scale, causal)
+    o_ref, lse_ref = oracle.fwd(q, k, v, scale, causal)
+    compare("o", o, o_ref)
+    compare_lse(lse, lse_ref)
+
+
+@pytest.mark.parametrize("share", ["1", "4"])
+def test_workload_forward_exp2_polynomial(fa, monkeypatch, share):
+    """Row-scaled causal workload (rescales taken) with polynomial exponentials."""
+    monkeypatch.setenv("FA_EXP2_POLY", share)
+    w = WORKLOADS["fwd_causal_rowscale_n8192"]
+    note(f"workload forward poly share={share} {w.name}")
+    x = make_inputs(w)
+    o, lse = gpu_fwd(fa, x["q"], x["k"], x["v"], w.scale, w.causal)
+    rows = sampled_rows(w, 256, w.seed + 1)
+    o_ref, lse_ref = oracle.fwd_rows(x["q"], x["k"], x["v"], w.scale, w.causal, rows)
+    compare("o (sampled rows)", o.reshape(-1, w.d)[rows], o_ref)
+    compare_lse(lse.reshape(-1)[rows], lse_ref)
+
+
 def test_workload_backward_both_modes(fa):
     """Full-size causal backward: one key/value group per batch compared element
     by element with the oracle in both modes; the deterministic mode must repeat
