@@ -37,6 +37,20 @@ size_t workspace_rows(int B, int Hq, int N) { return (size_t)B * Hq * (size_t)((
 
 int hip_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
 
+// FA_RESCALE_TAU overrides the rescale threshold (base-2 exponent units, a
+// finite value >= 0; 0 rescales whenever the running maximum grows, the
+// textbook online softmax).  Unset or invalid: log2(256) = 8.  Read on every
+// call.
+float rescale_tau()
+{
+    const char *e = std::getenv("FA_RESCALE_TAU");
+    if (!e) return fa::kRescaleTau;
+    char *end = nullptr;
+    const float t = std::strtof(e, &end);
+    if (end == e || *end != '\0' || !std::isfinite(t) || t < 0.f) return fa::kRescaleTau;
+    return t;
+}
+
 // FA_EXP2_POLY selects how many of the forward's exponentials run as the
 // cubic polynomial on the FMA units: "1" all, "4" one in four, anything else
 // (or unset) none.  Read on every call.
@@ -76,7 +90,7 @@ int fa_fwd(const void *q, const void *k, const void *v, float *o, float *lse, in
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
         (lse && !aligned16(lse)))
         return FA_ERR_ALIGN;
-    fa::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, N, d, scale, fa::kRescaleTau, causal != 0,
+    fa::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, N, d, scale, rescale_tau(), causal != 0,
                   exp2_poly_share(), reinterpret_cast<hipStream_t>(stream)};
     return hip_status(fa::launch_fwd(a));
 }

@@ -41,6 +41,10 @@
  *     polynomial on the FMA units (page "FlashAttention-4", Key Contributions
  *     item 2): "1" all of them, "4" one in four; unset or any other value,
  *     none (the default, and the faster choice on this chip).
+ *   - The environment variable FA_RESCALE_TAU, read on every fa_fwd call,
+ *     replaces the rescale threshold 8 by another finite value >= 0 (0:
+ *     rescale whenever the running maximum grows); the result is the same
+ *     up to rounding.
  *   - Supported: d in {64, 128}; B, Hq, Hkv, N >= 1; Hq % Hkv == 0;
  *     scale > 0 and finite; every pointer 16-byte aligned; N need not be a
  *     multiple of any tile size; one head's bf16 rows, N * d * 2 bytes, must

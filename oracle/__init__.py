@@ -47,6 +47,10 @@ def _load():
                                       c_int, c_float, c_int, i64p, c_i64, f64p, f64p, f64p,
                                       f64p, f64p, c_int]
     lib.oracle_bwd_groups.restype = c_int
+    lib.oracle_bwd_groups_tail.argtypes = [u16p, u16p, u16p, u16p, c_int, c_int, c_int, c_int,
+                                           c_int, c_float, c_int, c_int, i64p, c_i64, f64p, f64p,
+                                           f64p, f64p, f64p, c_int]
+    lib.oracle_bwd_groups_tail.restype = c_int
     _lib = lib
     return lib
 
@@ -147,6 +151,38 @@ def bwd_groups(q, k, v, dout, scale, causal, groups, threads=None):
         threads or default_threads())
     if st:
         raise RuntimeError(f"oracle_bwd_groups failed with status {st}")
+    return out
+
+
+def bwd_groups_tail(q, k, v, dout, scale, row0, groups, threads=None):
+    """Causal backward restricted to rows and keys row0 .. N-1 of the selected
+    groups (exact there: a key only receives gradient from later rows).
+
+    Returns dict with dq [G, Hq/Hkv, N-row0, d], dk [G, N-row0, d],
+    dv [G, N-row0, d], o [G, Hq/Hkv, N-row0, d], lse [G, Hq/Hkv, N-row0]."""
+    lib = _load()
+    q, k, v, dout = _u16(q, "q"), _u16(k, "k"), _u16(v, "v"), _u16(dout, "dout")
+    B, Hq, Hkv, N, d = _shape(q, k, v)
+    if dout.shape != q.shape:
+        raise ValueError("dout must have q's shape")
+    groups = np.ascontiguousarray(groups, dtype=np.int64)
+    G, grp, NT = groups.size, Hq // Hkv, N - int(row0)
+    out = {
+        "dq": np.empty((G, grp, NT, d), np.float64),
+        "dk": np.empty((G, NT, d), np.float64),
+        "dv": np.empty((G, NT, d), np.float64),
+        "o": np.empty((G, grp, NT, d), np.float64),
+        "lse": np.empty((G, grp, NT), np.float64),
+    }
+    st = lib.oracle_bwd_groups_tail(
+        _ptr(q, ctypes.c_uint16), _ptr(k, ctypes.c_uint16), _ptr(v, ctypes.c_uint16),
+        _ptr(dout, ctypes.c_uint16), B, Hq, Hkv, N, d, float(scale), 1, int(row0),
+        _ptr(groups, ctypes.c_int64), G, _ptr(out["dq"], ctypes.c_double),
+        _ptr(out["dk"], ctypes.c_double), _ptr(out["dv"], ctypes.c_double),
+        _ptr(out["o"], ctypes.c_double), _ptr(out["lse"], ctypes.c_double),
+        threads or default_threads())
+    if st:
+        raise RuntimeError(f"oracle_bwd_groups_tail failed with status {st}")
     return out
 
 

@@ -186,19 +186,32 @@ int oracle_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, double *
  * (dK_j, dV_j only touch row j), recomputing s_ij, P_ij and dP_ij, so no two
  * threads write the same element and every sum runs in index order.
  */
-int oracle_bwd_groups(const uint16_t *q, const uint16_t *k, const uint16_t *v,
-                      const uint16_t *dout, int B, int Hq, int Hkv, int N, int d, float scale,
-                      int causal, const int64_t *groups, int64_t ngroups, double *dq, double *dk,
-                      double *dv, double *o, double *lse, int nthreads)
+/*
+ * The same backward restricted to the tail block of a causal problem: rows
+ * and keys row0 .. N - 1.  Under the causal mask key j only receives gradient
+ * from rows i >= j, so dK_j and dV_j for j >= row0 need only the tail rows
+ * (whose forward statistics still run over all their keys), and dQ_i for
+ * i >= row0 is the ordinary row result.  Outputs hold the tail only:
+ * dq [ngroups, Hq/Hkv, N - row0, d], dk and dv [ngroups, N - row0, d], o and
+ * lse likewise.  row0 = 0 is the full backward (and the only value allowed
+ * without the causal mask).
+ */
+int oracle_bwd_groups_tail(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                           const uint16_t *dout, int B, int Hq, int Hkv, int N, int d,
+                           float scale, int causal, int row0, const int64_t *groups,
+                           int64_t ngroups, double *dq, double *dk, double *dv, double *o,
+                           double *lse, int nthreads)
 {
     if (!q || !k || !v || !dout || !groups || !dq || !dk || !dv || ngroups < 0)
         return ORACLE_BAD_ARGS;
     if (!check_shape(B, Hq, Hkv, N, d)) return ORACLE_BAD_ARGS;
+    if (row0 < 0 || row0 >= N || (!causal && row0 != 0)) return ORACLE_BAD_ARGS;
     for (int64_t t = 0; t < ngroups; t++)
         if (groups[t] < 0 || groups[t] >= (int64_t)B * Hkv) return ORACLE_BAD_ARGS;
     const double sc = (double)scale;
     const int group = Hq / Hkv;
-    const size_t rows_per_group = (size_t)group * N;
+    const int NT = N - row0; /* tail rows per head */
+    const size_t rows_per_group = (size_t)group * NT;
     if (nthreads < 1) nthreads = 1;
 
     /* Per-row forward statistics of the group being processed. */
@@ -218,8 +231,8 @@ int oracle_bwd_groups(const uint16_t *q, const uint16_t *k, const uint16_t *v,
         const uint16_t *kh = k + row_off(b, g, Hkv, 0, N, d);
         const uint16_t *vh = v + row_off(b, g, Hkv, 0, N, d);
         double *dq_t = dq + (size_t)t * rows_per_group * d;
-        double *dk_t = dk + (size_t)t * N * d;
-        double *dv_t = dv + (size_t)t * N * d;
+        double *dk_t = dk + (size_t)t * NT * d;
+        double *dv_t = dv + (size_t)t * NT * d;
 
         /* Pass A: per query row of each head of the group -> m, l, O, D, dQ. */
 #pragma omp parallel num_threads(nthreads)
@@ -233,8 +246,8 @@ int oracle_bwd_groups(const uint16_t *q, const uint16_t *k, const uint16_t *v,
 #pragma omp for schedule(dynamic, 4)
             for (int64_t rr = 0; rr < (int64_t)rows_per_group; rr++) {
                 if (!s || !acc) continue;
-                const int hl = (int)(rr / N); /* head within the group */
-                const int i = (int)(rr % N);
+                const int hl = (int)(rr / NT); /* head within the group */
+                const int i = row0 + (int)(rr % NT);
                 const int h = g * group + hl;
                 const uint16_t *qi = q + row_off(b, h, Hq, i, N, d);
                 const uint16_t *doi = dout + row_off(b, h, Hq, i, N, d);
@@ -288,16 +301,16 @@ int oracle_bwd_groups(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                 failed = 1;
             }
 #pragma omp for schedule(dynamic, 4)
-            for (int j = 0; j < N; j++) {
+            for (int j = row0; j < N; j++) {
                 if (!acck || !accv) continue;
                 const uint16_t *kj = kh + (size_t)j * d;
                 const uint16_t *vj = vh + (size_t)j * d;
                 for (int c = 0; c < d; c++) acck[c] = accv[c] = 0.0;
                 for (int hl = 0; hl < group; hl++) {
                     const int h = g * group + hl;
-                    const int i0 = causal ? j : 0; /* queries that see key j */
+                    const int i0 = causal ? j : 0; /* queries that see key j (>= row0) */
                     for (int i = i0; i < N; i++) {
-                        const size_t rr = (size_t)hl * N + i;
+                        const size_t rr = (size_t)hl * NT + (i - row0);
                         const uint16_t *qi = q + row_off(b, h, Hq, i, N, d);
                         const uint16_t *doi = dout + row_off(b, h, Hq, i, N, d);
                         double dot = 0.0, dp = 0.0;
@@ -312,8 +325,8 @@ int oracle_bwd_groups(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                     }
                 }
                 for (int c = 0; c < d; c++) {
-                    dv_t[(size_t)j * d + c] = accv[c];
-                    dk_t[(size_t)j * d + c] = sc * acck[c];
+                    dv_t[(size_t)(j - row0) * d + c] = accv[c];
+                    dk_t[(size_t)(j - row0) * d + c] = sc * acck[c];
                 }
             }
             free(acck);
@@ -330,4 +343,13 @@ int oracle_bwd_groups(const uint16_t *q, const uint16_t *k, const uint16_t *v,
     free(D_buf);
     free(o_buf);
     return failed ? ORACLE_NO_MEMORY : ORACLE_OK;
+}
+
+int oracle_bwd_groups(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                      const uint16_t *dout, int B, int Hq, int Hkv, int N, int d, float scale,
+                      int causal, const int64_t *groups, int64_t ngroups, double *dq, double *dk,
+                      double *dv, double *o, double *lse, int nthreads)
+{
+    return oracle_bwd_groups_tail(q, k, v, dout, B, Hq, Hkv, N, d, scale, causal, 0, groups,
+                                  ngroups, dq, dk, dv, o, lse, nthreads);
 }

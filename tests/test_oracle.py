@@ -364,6 +364,24 @@ def test_bwd_groups_subset_matches_full():
     np.testing.assert_array_equal(sub["dv"][0], full["dv"][1, 1])
 
 
+def test_bwd_tail_block_matches_full():
+    """Causal tail block: rows and keys row0 .. N-1 give exactly the tail of the
+    full backward (a key only receives gradient from later rows)."""
+    B, Hq, Hkv, N, d = 2, 4, 2, 37, 8
+    q, k, v = random_bf16((B, Hq, N, d), 161), random_bf16((B, Hkv, N, d), 162), random_bf16((B, Hkv, N, d), 163)
+    dout = random_bf16((B, Hq, N, d), 164)
+    full = oracle.bwd(q, k, v, dout, 0.3, True)
+    for row0 in (0, 1, 20, 36):
+        tail = oracle.bwd_groups_tail(q, k, v, dout, 0.3, row0, [1, 2])  # (b,g) = (0,1), (1,0)
+        for t, (b, g) in enumerate([(0, 1), (1, 0)]):
+            np.testing.assert_array_equal(tail["dq"][t], full["dq"][b, 2 * g:2 * g + 2, row0:])
+            np.testing.assert_array_equal(tail["dk"][t], full["dk"][b, g, row0:])
+            np.testing.assert_array_equal(tail["dv"][t], full["dv"][b, g, row0:])
+            np.testing.assert_array_equal(tail["lse"][t], full["lse"][b, 2 * g:2 * g + 2, row0:])
+    with pytest.raises(RuntimeError):
+        oracle.bwd_groups_tail(q, k, v, dout, 0.3, N, [0])
+
+
 def test_rejects_bad_shapes():
     q = random_bf16((1, 3, 4, 4), 1)
     k = random_bf16((1, 2, 4, 4), 2)

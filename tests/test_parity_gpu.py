@@ -12,6 +12,7 @@ zones: afterwards the guards must still be NaN (nothing written out of bounds)
 and the output must hold no NaN (every element written).
 """
 import math
+from dataclasses import replace
 import sys
 
 import numpy as np
@@ -242,6 +243,29 @@ def test_fwd_small_exp2_polynomial(fa, monkeypatch, share, N, d, causal):
     compare_lse(lse, lse_ref)
 
 
+def test_rescale_threshold_zero_and_eight_agree(fa, monkeypatch):
+    """tau = 0 (rescale whenever the maximum grows) and tau = 8 (the pages'
+    threshold) both match the oracle on the row-scaled workload, whose rows
+    rescale mid-row, and agree with each other."""
+    w = WORKLOADS["fwd_causal_rowscale_n8192"]
+    x = make_inputs(w)
+    rows = sampled_rows(w, 256, w.seed + 2)
+    o_ref, lse_ref = oracle.fwd_rows(x["q"], x["k"], x["v"], w.scale, w.causal, rows)
+    outs = {}
+    for tau in ("0", "8"):
+        monkeypatch.setenv("FA_RESCALE_TAU", tau)
+        note(f"rescale threshold tau={tau}")
+        o, lse = gpu_fwd(fa, x["q"], x["k"], x["v"], w.scale, w.causal)
+        compare(f"o tau={tau} (sampled rows)", o.reshape(-1, w.d)[rows], o_ref)
+        compare_lse(lse.reshape(-1)[rows], lse_ref)
+        outs[tau] = (o, lse)
+    # Each result is within the max-abs bar of the exact one (their bf16 P
+    # roundings differ, the exponent references being different), so the two
+    # are within twice the bar of each other over the whole tensor.
+    assert float(np.abs(outs["0"][0] - outs["8"][0]).max()) <= 2 * MAX_ABS
+    assert float(np.abs(outs["0"][1] - outs["8"][1]).max()) <= 2e-3 * 20
+
+
 @pytest.mark.parametrize("share", ["1", "4"])
 def test_workload_forward_exp2_polynomial(fa, monkeypatch, share):
     """Row-scaled causal workload (rescales taken) with polynomial exponentials."""
@@ -293,3 +317,42 @@ def test_workload_backward_both_modes(fa):
         assert np.array_equal(a.view(np.uint32), b_.view(np.uint32))
     for a, b_ in zip(results[0], results[1]):
         assert float(np.abs(a - b_).max()) <= 5e-3
+
+
+def test_long_context_gqa_backward(fa):
+    """Backward at the long-context GQA shape (B1 Hq32 Hkv8 N32768 d128,
+    causal), both modes.  Element by element against the oracle on the causal
+    tail block (rows and keys N-256 .. N-1 of the first and last KV group:
+    exact there, since a key only receives gradient from later rows); the
+    exact identities on every group; deterministic mode repeats bit for bit."""
+    w = replace(WORKLOADS["fwd_causal_gqa_n32768"], backward=True)
+    note("long-context GQA backward")
+    x = make_inputs(w)
+    o, lse = gpu_fwd(fa, x["q"], x["k"], x["v"], w.scale, w.causal)
+    row0 = w.N - 256
+    groups = [0, w.B * w.Hkv - 1]
+    ref = oracle.bwd_groups_tail(x["q"], x["k"], x["v"], x["dout"], w.scale, row0, groups)
+    grp = w.Hq // w.Hkv
+    dof = (x["dout"].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    want_dv = dof.reshape(w.B, w.Hkv, grp, w.N, w.d).sum((2, 3))
+    dv_bar = 1e-3 * np.abs(dof).reshape(w.B, w.Hkv, -1, w.d).sum(2) + 1e-2
+    det_result = None
+    for det in (0, 1):
+        note(f"  deterministic={det}")
+        dq, dk, dv = gpu_bwd(fa, x["q"], x["k"], x["v"], x["dout"], o, lse, w.scale, w.causal, det)
+        for t, gflat in enumerate(groups):
+            b, g = divmod(gflat, w.Hkv)
+            compare(f"dq[{b},{g}] tail", dq[b, g * grp:(g + 1) * grp, row0:], ref["dq"][t])
+            compare(f"dk[{b},{g}] tail", dk[b, g, row0:], ref["dk"][t])
+            compare(f"dv[{b},{g}] tail", dv[b, g, row0:], ref["dv"][t])
+        dsum = dk.astype(np.float64).sum(2)
+        scale_k = np.abs(dk).astype(np.float64).sum(2)
+        assert (np.abs(dsum) <= 1e-3 * scale_k + 1e-3).all()
+        assert (np.abs(dv.astype(np.float64).sum(2) - want_dv) <= dv_bar).all()
+        if det:
+            det_result = (dq, dk, dv)
+        del dq, dk, dv
+    note("  deterministic repeat")
+    again = gpu_bwd(fa, x["q"], x["k"], x["v"], x["dout"], o, lse, w.scale, w.causal, 1)
+    for a, b_ in zip(again, det_result):
+        assert np.array_equal(a.view(np.uint32), b_.view(np.uint32))
