@@ -15,21 +15,27 @@
 //   1. bwd_pre:   D_i and LSE_i * log2(e) per row into a workspace padded to
 //                 64 rows per head (padding rows: D = 0, LSE2 = +inf, so
 //                 P = 0); zero dQ in atomic mode.
-//   2. bwd_dkdv:  one workgroup per (batch, kv head, 128 keys); each of the 4
-//                 waves keeps 32 keys' K and V in registers and dK^T, dV^T
-//                 accumulators, and walks 64-query tiles of every query head
-//                 of the group.  Q and dO tiles arrive in LDS by
+//   2. bwd_dkdv (atomic mode): one workgroup per (batch, kv head, 128 keys);
+//                 each of the 4 waves keeps 32 keys' K and V in registers and
+//                 dK^T, dV^T accumulators, and walks 64-query tiles of every
+//                 query head of the group.  Q and dO tiles arrive in LDS by
 //                 direct-to-LDS loads, double-buffered; S = Q K^T and
 //                 dP = dO V^T read them row-wise, dV^T += dO^T P and
 //                 dK^T += Q^T dS read them with transposing loads, and P, dS
-//                 stay in registers as B operands.  In atomic mode dS goes to
-//                 LDS and the workgroup adds dS K into dQ with fp32 atomics one
-//                 step later, so the atomics are long finished when a step
-//                 waits for its loads.
+//                 stay in registers as B operands.  dS goes to LDS and the
+//                 workgroup adds dS K into dQ with fp32 atomics one step
+//                 later, so the atomics are long finished when a step waits
+//                 for its loads.
+//   2. bwd_dkdv_split (deterministic mode): the same work without dQ, split
+//                 over two waves per 32-key slice (S, P, dV and dP, dS, dK).
 //   3. bwd_dq:    (deterministic mode) one workgroup per (batch, query head,
 //                 128 queries) walks the key tiles, recomputes S^T, P^T,
 //                 dP^T = V dO^T, dS^T, and accumulates dQ^T += K^T dS^T in
 //                 registers; one plain store per element.
+// Tile copies in the deterministic kernels are buffer copies into LDS issued
+// as inline assembly (so the compiler never drains them before unrelated LDS
+// reads) into per-slot LDS arrays; each kernel settles its own global loads
+// before the first copy and waits for the copies at its step barriers.
 #include <type_traits>
 
 #include "fa_device.hpp"
