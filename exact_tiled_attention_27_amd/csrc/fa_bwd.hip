@@ -15,7 +15,7 @@
 //   1. bwd_pre:   D_i and LSE_i * log2(e) per row into a workspace padded to
 //                 64 rows per head (padding rows: D = 0, LSE2 = +inf, so
 //                 P = 0); zero dQ in atomic mode.
-//   2. bwd_dkdv (atomic mode): one workgroup per (batch, kv head, 128 keys);
+//   2. bwd_dkdv_atomic (atomic mode): one workgroup per (batch, kv head, 128 keys);
 //                 each of the 4 waves keeps 32 keys' K and V in registers and
 //                 dK^T, dV^T accumulators, and walks 64-query tiles of every
 //                 query head of the group.  Q and dO tiles arrive in LDS by
@@ -114,12 +114,11 @@ struct DkdvShape {
     static constexpr int OFF_DS = OFF_STAGE + 2 * STAGE;         // 2 x dS [BM][BN] bf16
     static constexpr int DS_BYTES = BM * BN * 2;
     static constexpr int OFF_K = OFF_DS + 2 * DS_BYTES;          // K [BN][D]
-    static constexpr int LDS_ATOMIC = OFF_K + BN * D * 2;
-    static constexpr int LDS_PLAIN = OFF_DS;
+    static constexpr int LDS_BYTES = OFF_K + BN * D * 2;
 };
 
-template <int D, bool CAUSAL, bool ATOMIC_DQ>
-__global__ __launch_bounds__(256) void bwd_dkdv_kernel(
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256) void bwd_dkdv_atomic_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, const uint16_t *__restrict__ dout,
     const float *__restrict__ lse2, const float *__restrict__ delta, float *__restrict__ dq,
@@ -228,7 +227,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
         }
     };
 
-    if (ATOMIC_DQ) {
+    {
         typename S::KTile ktile;
         ktile.init(wave, lane);
         ktile.issue(kh, kv0, N, smem + S::OFF_K, wave);
@@ -243,7 +242,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
         const char *dol = stage + S::TILE;
         // Next step's tiles go to the other stage, last read in step st - 1.
         if (st + 1 < n_steps) issue(st + 1, smem + S::OFF_STAGE + ((st + 1) & 1) * S::STAGE);
-        if (ATOMIC_DQ && st > 0) dq_update(st - 1, smem + S::OFF_DS + ((st - 1) & 1) * S::DS_BYTES);
+        if (st > 0) dq_update(st - 1, smem + S::OFF_DS + ((st - 1) & 1) * S::DS_BYTES);
 
         // S = Q K^T and dP = dO V^T, rows = queries, one key column per lane.
         f32x16 sc[2], dp[2];
@@ -310,7 +309,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
                 dka[db] = mfma32(join_bf16x8(lds_read_tr16(ql, o0), lds_read_tr16(ql, o1)), dsf[ks], dka[db]);
             }
 
-        if (ATOMIC_DQ) {
+        {
             // dS (bf16) -> LDS [BM queries][BN keys], natural key order.
             char *dsl = smem + S::OFF_DS + (st & 1) * S::DS_BYTES;
             const int kin = wave * 32 + col;  // key index within the workgroup
@@ -326,7 +325,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
         }
         dma_barrier();  // next stage landed; this stage and dS are complete
     }
-    if (ATOMIC_DQ && n_steps > 0) dq_update(n_steps - 1, smem + S::OFF_DS + ((n_steps - 1) & 1) * S::DS_BYTES);
+    if (n_steps > 0) dq_update(n_steps - 1, smem + S::OFF_DS + ((n_steps - 1) & 1) * S::DS_BYTES);
 
     // dV = (dV^T)^T, dK = scale * (dK^T)^T: lane holds d = 32 db + 8 gq + 4 h + i of `key`.
     if (key < N) {
@@ -813,9 +812,9 @@ static hipError_t launch_bwd_t(const BwdArgs &a)
                                (const uint16_t *)a.dout, a.lse2, a.delta, a.dk, a.dv, a.Hq, a.Hkv,
                                a.N, BHkv, KT, a.scale, scale_log2);
         } else {
-            auto kern = bwd_dkdv_kernel<D, CAUSAL, true>;
-            if ((e = set_lds(kern, S::LDS_ATOMIC)) != hipSuccess) return e;
-            hipLaunchKernelGGL(kern, dim3(BHkv * KT), dim3(S::THREADS), S::LDS_ATOMIC, a.stream,
+            auto kern = bwd_dkdv_atomic_kernel<D, CAUSAL>;
+            if ((e = set_lds(kern, S::LDS_BYTES)) != hipSuccess) return e;
+            hipLaunchKernelGGL(kern, dim3(BHkv * KT), dim3(S::THREADS), S::LDS_BYTES, a.stream,
                                (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v,
                                (const uint16_t *)a.dout, a.lse2, a.delta, a.dq, a.dk, a.dv, a.Hq,
                                a.Hkv, a.N, BHkv, KT, a.scale, scale_log2);

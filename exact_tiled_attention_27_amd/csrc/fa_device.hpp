@@ -51,7 +51,7 @@ __device__ __forceinline__ bf16x8 pack_half(const f32x16 &c, int j)
                        c[8 * j + 5], c[8 * j + 6], c[8 * j + 7]);
 }
 
-// LDS (address space 3) 16-byte and 8-byte accesses at a byte offset.
+// LDS (address space 3) 16-byte reads at a byte offset.
 __device__ __forceinline__ bf16x8 lds_read_bf16x8(const char *lds, uint32_t byte_off)
 {
     return *reinterpret_cast<const bf16x8 *>(lds + byte_off);
@@ -59,14 +59,6 @@ __device__ __forceinline__ bf16x8 lds_read_bf16x8(const char *lds, uint32_t byte
 __device__ __forceinline__ f32x4 lds_read_f32x4(const char *lds, uint32_t byte_off)
 {
     return *reinterpret_cast<const f32x4 *>(lds + byte_off);
-}
-__device__ __forceinline__ void lds_write_u32x4(char *lds, uint32_t byte_off, u32x4 v)
-{
-    *reinterpret_cast<u32x4 *>(lds + byte_off) = v;
-}
-__device__ __forceinline__ void lds_write_u32x2(char *lds, uint32_t byte_off, u32x2 v)
-{
-    *reinterpret_cast<u32x2 *>(lds + byte_off) = v;
 }
 
 // Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
@@ -113,9 +105,6 @@ __device__ __forceinline__ void lds_barrier()
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// Value of lane l ^ 32 (the other half of the wave).
-__device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32, 64); }
-
 // Reductions across the two 32-lane halves of a wave (lanes l and l ^ 32)
 // with one v_permlane32_swap: afterwards lane l holds lanes 0-31's value in
 // the first word and lanes 32-63's in the second, in both halves, so every
@@ -144,14 +133,6 @@ __device__ __forceinline__ float halves_sum(float x)
     return lo + hi;
 }
 
-// Within a group of 16 keys, the key order a 32x32 C tile presents to a B
-// operand: half h, slot t holds key 8*(t/4) + 4*h + t%4.  Stored position of
-// key kk so that half h reads positions 8h .. 8h+7 as one 16-byte chunk:
-// swap quarters 1 and 2 of the group.
-__device__ __host__ __forceinline__ int key_pos16(int kk)
-{
-    return ((kk & 4) << 1) | ((kk & 8) >> 1) | (kk & 3);
-}
 
 // Round-robin dispatch puts workgroup i on XCD i % 8.  Map the hardware id to
 // (head, tile) so each XCD works through whole heads: the workgroups that
