@@ -553,10 +553,12 @@ __global__ __launch_bounds__(512) void bwd_dkdv_split_kernel(
     using Slot0 = std::integral_constant<int, 0>;
     using Slot1 = std::integral_constant<int, 1>;
 
-#pragma unroll
-    for (int s = 0; s < S::KSTEPS; s++) settle(kvf[s]);
+    // First copies while the K/V row loads are in flight; the barrier drains
+    // both, and the loads are settled before the loop's copies start.
     if (n_steps > 0) issue(0, Slot0{});
     dma_barrier();
+#pragma unroll
+    for (int s = 0; s < S::KSTEPS; s++) settle(kvf[s]);
     int st = 0;
     for (; st + 2 <= n_steps; st += 2) {
         step(Slot0{}, st);
@@ -740,6 +742,10 @@ __global__ __launch_bounds__(256, FA_DQ_MIN_WAVES) void bwd_dq_kernel(
     using Slot0 = std::integral_constant<int, 0>;
     using Slot1 = std::integral_constant<int, 1>;
 
+    // First copies while the Q / dO row loads are in flight; the barrier
+    // drains both, and the loads are settled before the loop's copies start.
+    issue(0, Slot0{});
+    dma_barrier();
 #pragma unroll
     for (int s = 0; s < S::KSTEPS; s++) {
         settle(qf[s]);
@@ -747,8 +753,6 @@ __global__ __launch_bounds__(256, FA_DQ_MIN_WAVES) void bwd_dq_kernel(
     }
     settle(l2);
     settle(dl);
-    issue(0, Slot0{});
-    dma_barrier();
     // Unrolled by two so that LDS slots are compile-time constants; unmasked
     // tiles first, then the diagonal and tail tiles.
     int t = 0;

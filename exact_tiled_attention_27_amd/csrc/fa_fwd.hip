@@ -249,14 +249,16 @@ __global__ __launch_bounds__(256, FA_FWD_MIN_WAVES) void fwd_kernel(
     using Full = std::integral_constant<int, 1>;
     using Any = std::integral_constant<int, 2>;
 
-    // Prologue: K_0, V_0, K_1 in flight; S_0.
+    // Prologue: K_0, V_0, K_1 copied while the Q loads are in flight (the
+    // barrier drains both; the loads are settled right after it, so none is
+    // still counted when the loop's copies start); S_0.
     f32x16 sa[S::NKB], sb[S::NKB];
-#pragma unroll
-    for (int s = 0; s < S::KSTEPS; s++) settle(qf[s]);
     issue_k(0, Slot0{});
     issue_v(0, Slot0{});
     if (n_tiles > 1) issue_k(1, Slot1{});
     dma_barrier();
+#pragma unroll
+    for (int s = 0; s < S::KSTEPS; s++) settle(qf[s]);
     scores(sa, Slot0{});
     if (n_full == 0) apply_mask(sa, 0);
     row_max_rescale(sa);
