@@ -12,6 +12,12 @@ launch stream around each call give per-call durations for the roofline.  The
 atomic-dQ backward is timed after the step loop and reported under "parts".
 The fp64 CPU oracle is timed on a bounded sample (16 heads' forward and
 backward) of the same workload as a reported baseline.
+
+"per_config" then times each of the five synthetic workloads on its own
+(forward; both backward modes where the workload has a backward): launches back
+to back after 0.3 s of untimed ones, an event pair around each launch, median
+and minimum reported.  --no-per-config skips it (profiling runs use that, so the
+kernel averages cover the step's launches only).
 """
 import argparse
 import json
@@ -58,15 +64,98 @@ def measured_traffic(kernels, workload):
         return None
 
 
+def time_launches(fn, reps, stream, warm_s=0.3):
+    """Per-launch durations (ms) of `reps` back-to-back calls of fn, from an
+    event pair recorded on `stream` around each call, after `warm_s` seconds of
+    untimed calls (the clock drops while the host draws the next workload's
+    inputs and needs tens of milliseconds of load to come back up)."""
+    import torch
+    t0 = time.perf_counter()
+    while True:
+        for _ in range(4):
+            fn()
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= warm_s:
+            break
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    torch.cuda.synchronize()
+    for e0, e1 in ev:
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return sorted(e0.elapsed_time(e1) for e0, e1 in ev)
+
+
+def per_config(fa, reps, dev, stream):
+    """Forward (and, for the backward workload, both backward modes) of each
+    synthetic workload, timed on its own."""
+    import numpy as np
+    import torch
+    from synth import WORKLOADS, make_inputs
+
+    def to_dev(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    rows = []
+    for w in WORKLOADS.values():
+        x = make_inputs(w)
+        q, k, v = to_dev(x["q"]), to_dev(x["k"]), to_dev(x["v"])
+        B, Hq, Hkv, N, d = w.B, w.Hq, w.Hkv, w.N, w.d
+        o = torch.empty((B, Hq, N, d), dtype=torch.float32, device=dev)
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
+
+        def fwd():
+            st = fa.fa_fwd(q, k, v, o, lse, B, Hq, Hkv, N, d, w.scale, w.causal,
+                           stream.cuda_stream)
+            if st:
+                raise fa.FAError(st, "fa_fwd")
+
+        def entry(call, flops, ms):
+            med = float(np.median(ms))
+            tf = flops / (med * 1e-3) / 1e12
+            return {"call": call, "ms_median": med, "ms_min": float(ms[0]),
+                    "tflops": tf, "frac_peak": tf / PEAK_BF16_TFLOPS}
+
+        row = {"workload": w.name, "B": B, "Hq": Hq, "Hkv": Hkv, "N": N, "d": d,
+               "causal": w.causal, "calls": [entry("fa_fwd", w.fwd_flops(),
+                                                   time_launches(fwd, reps, stream))]}
+        if w.backward:
+            do = to_dev(x["dout"])
+            dq = torch.empty((B, Hq, N, d), dtype=torch.float32, device=dev)
+            dk = torch.empty((B, Hkv, N, d), dtype=torch.float32, device=dev)
+            dv = torch.empty_like(dk)
+            for det in (1, 0):
+                wsb = fa.fa_bwd_workspace_bytes(B, Hq, Hkv, N, d, det)
+                ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+
+                def bwd():
+                    st = fa.fa_bwd(q, k, v, o, lse, do, dq, dk, dv, B, Hq, Hkv, N, d, w.scale,
+                                   w.causal, det, ws, wsb, stream.cuda_stream)
+                    if st:
+                        raise fa.FAError(st, "fa_bwd")
+
+                name = "fa_bwd deterministic" if det else "fa_bwd atomic"
+                row["calls"].append(entry(name, w.bwd_flops(), time_launches(bwd, reps, stream)))
+        rows.append(row)
+        del x, q, k, v, o, lse
+    torch.cuda.synchronize()
+    return rows
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--warmup", type=int, default=40)
     p.add_argument("--workload", default="fwd_n4096")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--atomic-reps", type=int, default=10,
                    help="timed launches of the atomic-dQ backward reported under parts (0: skip)")
+    p.add_argument("--no-per-config", action="store_true",
+                   help="skip timing each synthetic workload on its own")
+    p.add_argument("--per-config-reps", type=int, default=10)
     p.add_argument("--copy-calibration", action="store_true",
                    help="run one 256 MiB device-to-device copy before the timed region "
                         "(reference kernel for scaling HBM byte counters)")
@@ -198,6 +287,10 @@ def main():
                 "traffic": measured_traffic(rl_kernels, w.name), "traffic_unit": "bytes",
                 "flops_per_launch": rl_flops, "avg_launch_ms": rl_ms}
 
+    configs = None
+    if not args.no_per_config:
+        configs = per_config(fa, args.per_config_reps, dev, stream)
+
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
@@ -228,6 +321,7 @@ def main():
         "parts": parts,
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "per_config": configs,
     }
     print(json.dumps(out))
 
