@@ -278,7 +278,7 @@ def main():
         rl_kernels = [f"fa::fwd_kernel<{d}, {cz}, 0>"]
         rl_flops, rl_ms = f_fwd, parts["fwd_ms_avg"]
     else:
-        rl_kernels = [f"fa::bwd_pre_kernel<{d}>", f"fa::bwd_dkdv_split_kernel<{d}, {cz}>",
+        rl_kernels = [f"fa::bwd_pre_kernel<{d}>", f"fa::bwd_dkdv_split_kernel<{d}, {cz}, false>",
                       f"fa::bwd_dq_kernel<{d}, {cz}>"]
         rl_flops, rl_ms = f_bwd, parts["bwd_deterministic_ms_avg"]
     achieved = rl_flops / (rl_ms * 1e-3) / 1e12

@@ -15,27 +15,24 @@
 //   1. bwd_pre:   D_i and LSE_i * log2(e) per row into a workspace padded to
 //                 64 rows per head (padding rows: D = 0, LSE2 = +inf, so
 //                 P = 0); zero dQ in atomic mode.
-//   2. bwd_dkdv_atomic (atomic mode): one workgroup per (batch, kv head, 128 keys);
-//                 each of the 4 waves keeps 32 keys' K and V in registers and
-//                 dK^T, dV^T accumulators, and walks 64-query tiles of every
-//                 query head of the group.  Q and dO tiles arrive in LDS by
-//                 direct-to-LDS loads, double-buffered; S = Q K^T and
-//                 dP = dO V^T read them row-wise, dV^T += dO^T P and
-//                 dK^T += Q^T dS read them with transposing loads, and P, dS
-//                 stay in registers as B operands.  dS goes to LDS and the
-//                 workgroup adds dS K into dQ with fp32 atomics one step
-//                 later, so the atomics are long finished when a step waits
-//                 for its loads.
-//   2. bwd_dkdv_split (deterministic mode): the same work without dQ, split
-//                 over two waves per 32-key slice (S, P, dV and dP, dS, dK).
+//   2. bwd_dkdv_split: one workgroup of 8 waves per (batch, kv head, 128
+//                 keys) walks 64-query tiles of every query head of the
+//                 group; per 32-key slice, wave A computes S, P and dV^T,
+//                 wave B dP, dS and dK^T, accumulators in registers.  Q and
+//                 dO tiles arrive in LDS double-buffered; row reads feed S
+//                 and dP, transposing reads feed dV^T += dO^T P and
+//                 dK^T += Q^T dS, and P, dS stay in registers as B operands.
+//                 Atomic mode: wave B also leaves dS^T in LDS, and at the
+//                 start of the next step the B waves add dS K into dQ with
+//                 fp32 atomics (the end-of-step wait finds them finished).
 //   3. bwd_dq:    (deterministic mode) one workgroup per (batch, query head,
 //                 128 queries) walks the key tiles, recomputes S^T, P^T,
 //                 dP^T = V dO^T, dS^T, and accumulates dQ^T += K^T dS^T in
 //                 registers; one plain store per element.
-// Tile copies in the deterministic kernels are buffer copies into LDS issued
-// as inline assembly (so the compiler never drains them before unrelated LDS
-// reads) into per-slot LDS arrays; each kernel settles its own global loads
-// before the first copy and waits for the copies at its step barriers.
+// Tile copies are buffer copies into LDS issued as inline assembly (so the
+// compiler never drains them before unrelated LDS reads) into per-slot LDS
+// arrays; each kernel settles its own global loads before the first copy and
+// waits for the copies at its step barriers.
 #include <type_traits>
 
 #include "fa_device.hpp"
@@ -97,257 +94,9 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t *__restrict
     }
 }
 
-// ------------------------------------------------------------- dK/dV kernel
-template <int D>
-struct DkdvShape {
-    static constexpr int BN = 128;   // keys per workgroup (32 per wave)
-    static constexpr int BM = 64;    // queries per step
-    static constexpr int THREADS = 256;
-    static constexpr int KSTEPS = D / 16;
-    static constexpr int DBLK = D / 32;
-    using QTile = DmaTile<BM, D, THREADS>;   // Q and dO tiles
-    using KTile = DmaTile<BN, D, THREADS>;   // the workgroup's K rows (dQ = dS K)
-    static constexpr int TILE = BM * D * 2;
-    static constexpr int OFF_STAGE = 0;                          // 2 x {Q, dO, LSE2, D}
-    static constexpr int ROWS = 2 * TILE;                        // LSE2[BM], then D[BM] (fp32)
-    static constexpr int STAGE = 2 * TILE + 2 * BM * 4;
-    static constexpr int OFF_DS = OFF_STAGE + 2 * STAGE;         // 2 x dS [BM][BN] bf16
-    static constexpr int DS_BYTES = BM * BN * 2;
-    static constexpr int OFF_K = OFF_DS + 2 * DS_BYTES;          // K [BN][D]
-    static constexpr int LDS_BYTES = OFF_K + BN * D * 2;
-};
-
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void bwd_dkdv_atomic_kernel(
-    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
-    const uint16_t *__restrict__ v, const uint16_t *__restrict__ dout,
-    const float *__restrict__ lse2, const float *__restrict__ delta, float *__restrict__ dq,
-    float *__restrict__ dk, float *__restrict__ dv, int Hq, int Hkv, int N, int BHkv, int KT,
-    float scale, float scale_log2)
-{
-    using S = DkdvShape<D>;
-    extern __shared__ __attribute__((aligned(16))) char smem[];
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int h = lane >> 5, col = lane & 31;
-    const int g16 = lane >> 4;
-
-    int bg, kt;
-    xcd_tile_map(blockIdx.x, BHkv, KT, false, bg, kt);
-    const int b = bg / Hkv, g = bg % Hkv;
-    const int grp = Hq / Hkv;
-    const int NP = pad_rows(N);
-    const int kv0 = kt * S::BN;
-    const int key = kv0 + wave * 32 + col;  // the key this lane owns in S / dP / dS
-
-    const uint16_t *kh = k + ((size_t)b * Hkv + g) * N * D;
-    const uint16_t *vh = v + ((size_t)b * Hkv + g) * N * D;
-
-    // K and V rows of this lane's key as B operands.
-    bf16x8 kf[S::KSTEPS], vf[S::KSTEPS];
-#pragma unroll
-    for (int s = 0; s < S::KSTEPS; s++) {
-        kf[s] = __builtin_bit_cast(bf16x8, gload16(kh, ((size_t)key * D + 16 * s + 8 * h) * 2, key < N));
-        vf[s] = __builtin_bit_cast(bf16x8, gload16(vh, ((size_t)key * D + 16 * s + 8 * h) * 2, key < N));
-    }
-
-    f32x16 dva[S::DBLK], dka[S::DBLK];
-#pragma unroll
-    for (int db = 0; db < S::DBLK; db++)
-#pragma unroll
-        for (int r = 0; r < 16; r++) dva[db][r] = dka[db][r] = 0.f;
-
-    // LDS offsets.  Row reads of a Q / dO tile (A operand of S and dP): row
-    // 32 qb + col, chunk 2 s + h.  Transposing reads (A operand of dV^T and
-    // dK^T): rows 16 ks + 8 rho + 4 h .. +3 in the key order of the P / dS
-    // registers, columns 32 db + (lane % 32).
-    uint32_t rowoff[S::KSTEPS];
-#pragma unroll
-    for (int s = 0; s < S::KSTEPS; s++) rowoff[s] = tile_off(col, 2 * s + h, D);
-    uint32_t troff[S::DBLK][2];
-#pragma unroll
-    for (int db = 0; db < S::DBLK; db++)
-#pragma unroll
-        for (int rho = 0; rho < 2; rho++)
-            troff[db][rho] = tr_off(8 * rho + 4 * h, 32 * db + 16 * (g16 & 1), lane, D);
-
-    const int first_qt = CAUSAL ? kv0 / S::BM : 0;
-    const int n_qt = (N + S::BM - 1) / S::BM;
-    const int steps_per_head = n_qt - first_qt;
-    const int n_steps = grp * steps_per_head;  // (query head of the group, query tile) pairs
-
-    typename S::QTile qtile;  // the Q and dO tiles share one load pattern
-    qtile.init(wave, lane);
-    auto issue = [&](int st, char *stage) {
-        const int hq = g * grp + st / steps_per_head;
-        const int qs = (first_qt + st % steps_per_head) * S::BM;
-        const size_t ho = ((size_t)b * Hq + hq) * N;
-        qtile.issue(q + ho * D, qs, N, stage, wave);
-        qtile.issue(dout + ho * D, qs, N, stage + S::TILE, wave);
-        // LSE2 and D of the tile's 64 rows (padded workspace: always in
-        // bounds): lanes 0-15 fetch LSE2, lanes 16-31 fetch D, 16 bytes each.
-        if (wave == 0 && lane < 32) {
-            const size_t r0 = ((size_t)b * Hq + hq) * NP + qs + 4 * (lane & 15);
-            lds_dma16(lane < 16 ? (const void *)(lse2 + r0) : (const void *)(delta + r0),
-                      (lds_void_t *)(stage + S::ROWS));
-        }
-    };
-
-    // dQ[BM x D] += dS[BM x BN] K[BN x D] for the step whose dS sits in `dsl`;
-    // 2 * DBLK tiles of 32 x 32 spread over the 4 waves.  A = dS rows (natural
-    // key order), B = K by transposing reads (keys 16 ks + 8 h + 4 rho ..).
-    auto dq_update = [&](int st, const char *dsl) {
-        const int hq = g * grp + st / steps_per_head;
-        const int qs = (first_qt + st % steps_per_head) * S::BM;
-        float *dqh = dq + ((size_t)b * Hq + hq) * N * D;
-        constexpr int TILES = 2 * S::DBLK;
-#pragma unroll
-        for (int tt = wave; tt < TILES; tt += 4) {
-            const int qb = tt / S::DBLK, db = tt % S::DBLK;
-            f32x16 acc;
-#pragma unroll
-            for (int r = 0; r < 16; r++) acc[r] = 0.f;
-            const uint32_t ao = tile_off(32 * qb + col, h, 128);
-            const uint32_t bo0 = tr_off(8 * h, 32 * db + 16 * (g16 & 1), lane, D);
-            const uint32_t bo1 = tr_off(8 * h + 4, 32 * db + 16 * (g16 & 1), lane, D);
-#pragma unroll
-            for (int ks = 0; ks < S::BN / 16; ks++) {
-                // chunk 2 ks + h of dS row 32 qb + col: XOR-ing the logical
-                // chunk into the swizzled one is linear, so add it by XOR.
-                const bf16x8 a = lds_read_bf16x8(dsl, ao ^ ((2 * ks) << 4));
-                const char *kl = smem + S::OFF_K + 16 * ks * D * 2;
-                const bf16x8 bb = join_bf16x8(lds_read_tr16(kl, bo0), lds_read_tr16(kl, bo1));
-                acc = mfma32(a, bb, acc);
-            }
-#pragma unroll
-            for (int r = 0; r < 16; r++) {
-                const int qi = qs + 32 * qb + 8 * (r >> 2) + 4 * h + (r & 3);
-                if (qi < N) unsafeAtomicAdd(dqh + (size_t)qi * D + 32 * db + col, acc[r] * scale);
-            }
-        }
-    };
-
-    {
-        typename S::KTile ktile;
-        ktile.init(wave, lane);
-        ktile.issue(kh, kv0, N, smem + S::OFF_K, wave);
-    }
-    if (n_steps > 0) issue(0, smem + S::OFF_STAGE);
-    dma_barrier();
-
-    for (int st = 0; st < n_steps; st++) {
-        const int qs = (first_qt + st % steps_per_head) * S::BM;
-        const char *stage = smem + S::OFF_STAGE + (st & 1) * S::STAGE;
-        const char *ql = stage;
-        const char *dol = stage + S::TILE;
-        // Next step's tiles go to the other stage, last read in step st - 1.
-        if (st + 1 < n_steps) issue(st + 1, smem + S::OFF_STAGE + ((st + 1) & 1) * S::STAGE);
-        if (st > 0) dq_update(st - 1, smem + S::OFF_DS + ((st - 1) & 1) * S::DS_BYTES);
-
-        // S = Q K^T and dP = dO V^T, rows = queries, one key column per lane.
-        f32x16 sc[2], dp[2];
-#pragma unroll
-        for (int qb = 0; qb < 2; qb++)
-#pragma unroll
-            for (int r = 0; r < 16; r++) sc[qb][r] = dp[qb][r] = 0.f;
-#pragma unroll
-        for (int s = 0; s < S::KSTEPS; s++)
-#pragma unroll
-            for (int qb = 0; qb < 2; qb++) {
-                const uint32_t ro = rowoff[s] + qb * 32 * D * 2;
-                sc[qb] = mfma32(lds_read_bf16x8(ql, ro), kf[s], sc[qb]);
-                dp[qb] = mfma32(lds_read_bf16x8(dol, ro), vf[s], dp[qb]);
-            }
-        // P = exp2(s * scale * log2 e - LSE2), dS = P (dP - D).  Rows >= N,
-        // keys >= N and (causal) keys after the query get a -inf exponent
-        // (P = 0); only steps that contain such pairs evaluate the mask.
-        const bool need_mask = kv0 + S::BN > N || qs + S::BM > N || (CAUSAL && qs < kv0 + S::BN - 1);
-        auto softmax = [&](auto masked) {
-            constexpr bool MASK = decltype(masked)::value;
-#pragma unroll
-            for (int qb = 0; qb < 2; qb++)
-#pragma unroll
-                for (int gq = 0; gq < 4; gq++) {
-                    const int qr = 32 * qb + 8 * gq + 4 * h;  // rows qr .. qr + 3 of the tile
-                    const f32x4 l2 = lds_read_f32x4(stage + S::ROWS, qr * 4);
-                    const f32x4 dl = lds_read_f32x4(stage + S::ROWS, (S::BM + qr) * 4);
-#pragma unroll
-                    for (int i = 0; i < 4; i++) {
-                        const int r = 4 * gq + i;
-                        float x = __builtin_fmaf(sc[qb][r], scale_log2, -l2[i]);
-                        if (MASK) {
-                            const int qi = qs + qr + i;
-                            const bool dead = key >= N || qi >= N || (CAUSAL && key > qi);
-                            x = dead ? -INFINITY : x;
-                        }
-                        const float p = exp2_hw(x);
-                        sc[qb][r] = p;
-                        dp[qb][r] = p * (dp[qb][r] - dl[i]);
-                    }
-                }
-        };
-        if (need_mask)
-            softmax(std::true_type{});
-        else
-            softmax(std::false_type{});
-        bf16x8 pf[4], dsf[4];
-#pragma unroll
-        for (int qb = 0; qb < 2; qb++) {
-            pf[2 * qb] = pack_half(sc[qb], 0);
-            pf[2 * qb + 1] = pack_half(sc[qb], 1);
-            dsf[2 * qb] = pack_half(dp[qb], 0);
-            dsf[2 * qb + 1] = pack_half(dp[qb], 1);
-        }
-        // dV^T += dO^T P,  dK^T += Q^T dS  (contraction over the tile's queries).
-#pragma unroll
-        for (int ks = 0; ks < 4; ks++)
-#pragma unroll
-            for (int db = 0; db < S::DBLK; db++) {
-                const uint32_t o0 = troff[db][0] + 16 * ks * D * 2;
-                const uint32_t o1 = troff[db][1] + 16 * ks * D * 2;
-                dva[db] = mfma32(join_bf16x8(lds_read_tr16(dol, o0), lds_read_tr16(dol, o1)), pf[ks], dva[db]);
-                dka[db] = mfma32(join_bf16x8(lds_read_tr16(ql, o0), lds_read_tr16(ql, o1)), dsf[ks], dka[db]);
-            }
-
-        {
-            // dS (bf16) -> LDS [BM queries][BN keys], natural key order.
-            char *dsl = smem + S::OFF_DS + (st & 1) * S::DS_BYTES;
-            const int kin = wave * 32 + col;  // key index within the workgroup
-#pragma unroll
-            for (int qb = 0; qb < 2; qb++)
-#pragma unroll
-                for (int r = 0; r < 16; r++) {
-                    const int qr = 32 * qb + 8 * (r >> 2) + 4 * h + (r & 3);
-                    const __bf16 x = (__bf16)dp[qb][r];
-                    *reinterpret_cast<uint16_t *>(dsl + tile_off(qr, kin >> 3, 128) + (kin & 7) * 2) =
-                        __builtin_bit_cast(uint16_t, x);
-                }
-        }
-        dma_barrier();  // next stage landed; this stage and dS are complete
-    }
-    if (n_steps > 0) dq_update(n_steps - 1, smem + S::OFF_DS + ((n_steps - 1) & 1) * S::DS_BYTES);
-
-    // dV = (dV^T)^T, dK = scale * (dK^T)^T: lane holds d = 32 db + 8 gq + 4 h + i of `key`.
-    if (key < N) {
-        float *dvr = dv + (((size_t)b * Hkv + g) * N + key) * D;
-        float *dkr = dk + (((size_t)b * Hkv + g) * N + key) * D;
-#pragma unroll
-        for (int db = 0; db < S::DBLK; db++)
-#pragma unroll
-            for (int gq = 0; gq < 4; gq++) {
-                const int dd = 32 * db + 8 * gq + 4 * h;
-                f32x4 a = {dva[db][4 * gq], dva[db][4 * gq + 1], dva[db][4 * gq + 2], dva[db][4 * gq + 3]};
-                f32x4 c = {dka[db][4 * gq] * scale, dka[db][4 * gq + 1] * scale,
-                           dka[db][4 * gq + 2] * scale, dka[db][4 * gq + 3] * scale};
-                *reinterpret_cast<f32x4 *>(dvr + dd) = a;
-                *reinterpret_cast<f32x4 *>(dkr + dd) = c;
-            }
-    }
-}
-
 // ------------------------------------------- dK/dV kernel, two waves per key slice
-// Deterministic mode.  One workgroup of 8 waves per (batch, kv head, 128 keys);
-// the 32 keys of slice p are shared by two waves (both on the same SIMD):
+// One workgroup of 8 waves per (batch, kv head, 128 keys); the 32 keys of
+// slice p are shared by two waves (both on the same SIMD):
 //   wave A (w = p):     S = Q K^T, P = exp2(S * c - LSE2), dV^T += dO^T P;
 //   wave B (w = p + 4): dP = dO V^T, then (after A publishes P through LDS)
 //                       dS = P (dP - D), dK^T += Q^T dS.
@@ -356,6 +105,10 @@ __global__ __launch_bounds__(256) void bwd_dkdv_atomic_kernel(
 // the exponent / elementwise phases of the other.  The Q, dO and row stages
 // live in separate LDS arrays per slot (step st uses slot st % 2), so reads of
 // one slot never wait for the copies into the other.
+// ATOMIC_DQ (the atomic-dQ mode) adds dQ += dS K: wave B stores dS^T to LDS
+// after the products of step st, and the four B waves add that step's dQ
+// tiles with fp32 atomics at the start of step st + 1 (before the mid-step
+// barrier, after which dS^T is overwritten).
 template <int D>
 struct DkdvSplitShape {
     static constexpr int BN = 128;   // keys per workgroup (32 per wave pair)
@@ -369,15 +122,19 @@ struct DkdvSplitShape {
     static constexpr int X_SLICE = 64 * 32 * 4;            // P exchange per slice: 64 lanes x 32 fp32
 };
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool ATOMIC_DQ>
 __global__ __launch_bounds__(512) void bwd_dkdv_split_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, const uint16_t *__restrict__ dout,
-    const float *__restrict__ lse2, const float *__restrict__ delta, float *__restrict__ dk,
-    float *__restrict__ dv, int Hq, int Hkv, int N, int BHkv, int KT, float scale,
-    float scale_log2)
+    const float *__restrict__ lse2, const float *__restrict__ delta, float *__restrict__ dq,
+    float *__restrict__ dk, float *__restrict__ dv, int Hq, int Hkv, int N, int BHkv, int KT,
+    float scale, float scale_log2)
 {
     using S = DkdvSplitShape<D>;
+    // Atomic mode only: the workgroup's K rows (B operand of dQ = dS K) and
+    // the step's dS^T [BN keys][BM queries] (A operand, transposing reads).
+    __shared__ __attribute__((aligned(16))) char k_lds[ATOMIC_DQ ? S::BN * D * 2 : 16];
+    __shared__ __attribute__((aligned(16))) char dst_lds[ATOMIC_DQ ? S::BN * S::BM * 2 : 16];
     __shared__ __attribute__((aligned(16))) char q_lds0[S::TILE];
     __shared__ __attribute__((aligned(16))) char q_lds1[S::TILE];
     __shared__ __attribute__((aligned(16))) char do_lds0[S::TILE];
@@ -452,6 +209,44 @@ __global__ __launch_bounds__(512) void bwd_dkdv_split_kernel(
         }
     };
 
+    // Atomic mode, B waves: dQ[BM x D] += dS[BM x BN] K[BN x D] for step st,
+    // whose dS^T the B waves left in dst_lds; the 2 * DBLK tiles of 32 x 32
+    // are spread over the four B waves, each tile added with fp32 atomics
+    // (lanes 0-31 and 32-63 cover 128 contiguous bytes of a dQ row each).
+    auto dq_update = [&](int st) {
+        const int hq = g * grp + st / steps_per_head;
+        const int qs = (first_qt + st % steps_per_head) * S::BM;
+        float *dqh = dq + ((size_t)b * Hq + hq) * N * D;
+        constexpr int TILES = 2 * S::DBLK;
+#pragma unroll
+        for (int tt = slice; tt < TILES; tt += 4) {
+            const int qb = tt / S::DBLK, db = tt % S::DBLK;
+            const uint32_t a0 = tr_off(8 * h, 32 * qb + 16 * (g16 & 1), lane, S::BM);
+            const uint32_t a1 = tr_off(8 * h + 4, 32 * qb + 16 * (g16 & 1), lane, S::BM);
+            const uint32_t b0 = tr_off(8 * h, 32 * db + 16 * (g16 & 1), lane, D);
+            const uint32_t b1 = tr_off(8 * h + 4, 32 * db + 16 * (g16 & 1), lane, D);
+            f32x16 c = {};
+#pragma unroll
+            for (int ks = 0; ks < S::BN / 16; ks++) {
+                const char *al = dst_lds + 16 * ks * S::BM * 2;
+                const char *bl = k_lds + 16 * ks * D * 2;
+                c = mfma32(join_bf16x8(lds_read_tr16(al, a0), lds_read_tr16(al, a1)),
+                           join_bf16x8(lds_read_tr16(bl, b0), lds_read_tr16(bl, b1)), c);
+            }
+            float *dqt = dqh + (size_t)(qs + 32 * qb + 4 * h) * D + 32 * db + col;
+            if (qs + S::BM <= N) {
+#pragma unroll
+                for (int r = 0; r < 16; r++)
+                    unsafeAtomicAdd(dqt + (8 * (r >> 2) + (r & 3)) * D, c[r] * scale);
+            } else {
+#pragma unroll
+                for (int r = 0; r < 16; r++)
+                    if (qs + 32 * qb + 4 * h + 8 * (r >> 2) + (r & 3) < N)
+                        unsafeAtomicAdd(dqt + (8 * (r >> 2) + (r & 3)) * D, c[r] * scale);
+            }
+        }
+    };
+
     auto step = [&](auto slot, int st) {
         constexpr int P = decltype(slot)::value;
         const int qs = (first_qt + st % steps_per_head) * S::BM;
@@ -459,6 +254,9 @@ __global__ __launch_bounds__(512) void bwd_dkdv_split_kernel(
         const char *dol = P ? do_lds1 : do_lds0;
         const char *rows = P ? rows1 : rows0;
         if (st + 1 < n_steps) issue(st + 1, std::integral_constant<int, 1 - P>{});
+        // Atomic mode: the B waves add the previous step's dS K into dQ first
+        // (no score registers live yet), while the A waves start on S.
+        if (ATOMIC_DQ && !wave_a && st > 0) dq_update(st - 1);
 
         // A: S = Q K^T.  B: dP = dO V^T.  (rows = queries, one key per lane)
         const char *rl = wave_a ? ql : dol;
@@ -514,7 +312,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_split_kernel(
             else
                 softmax(std::false_type{});
         }
-        lds_barrier();  // P of every slice published
+        lds_barrier();  // P of every slice published (and, atomic mode, dS^T consumed)
 
         bf16x8 bop[4];  // A: P, B: dS (B operands, key order of the accumulator rows)
         if (wave_a) {
@@ -537,6 +335,20 @@ __global__ __launch_bounds__(512) void bwd_dkdv_split_kernel(
                 bop[2 * qb] = pack_half(x[qb], 0);
                 bop[2 * qb + 1] = pack_half(x[qb], 1);
             }
+            if (ATOMIC_DQ) {
+                // dS^T row = this lane's key; bop[ks] holds queries
+                // 16 ks + 4 h + 0..3 and 16 ks + 8 + 4 h + 0..3: the two
+                // halves of chunks 2 ks and 2 ks + 1 selected by h.
+                const int kin = slice * 32 + col;
+#pragma unroll
+                for (int ks = 0; ks < 4; ks++) {
+                    const i16x8 w = __builtin_bit_cast(i16x8, bop[ks]);
+                    const i16x4 lo = __builtin_shufflevector(w, w, 0, 1, 2, 3);
+                    const i16x4 hi = __builtin_shufflevector(w, w, 4, 5, 6, 7);
+                    *reinterpret_cast<i16x4 *>(dst_lds + tile_off(kin, 2 * ks, S::BM) + 8 * h) = lo;
+                    *reinterpret_cast<i16x4 *>(dst_lds + tile_off(kin, 2 * ks + 1, S::BM) + 8 * h) = hi;
+                }
+            }
         }
         // A: dV^T += dO^T P.  B: dK^T += Q^T dS.
         const char *tl = wave_a ? dol : ql;
@@ -555,6 +367,12 @@ __global__ __launch_bounds__(512) void bwd_dkdv_split_kernel(
 
     // First copies while the K/V row loads are in flight; the barrier drains
     // both, and the loads are settled before the loop's copies start.
+    if (ATOMIC_DQ) {
+        DmaTile<S::BN, D, S::THREADS> ktile;
+        ktile.init(wave, lane);
+        ktile.issue(make_rsrc(k + ((size_t)b * Hkv + g) * N * D, (uint32_t)N * D * 2), kv0, N,
+                    k_lds, wave);
+    }
     if (n_steps > 0) issue(0, Slot0{});
     dma_barrier();
 #pragma unroll
@@ -565,6 +383,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_split_kernel(
         step(Slot1{}, st + 1);
     }
     if (st < n_steps) step(Slot0{}, st);
+    if (ATOMIC_DQ && !wave_a && n_steps > 0) dq_update(n_steps - 1);
 
     if (key < N) {
         float *out = (wave_a ? dv : dk) + (((size_t)b * Hkv + g) * N + key) * D;
@@ -780,13 +599,6 @@ __global__ __launch_bounds__(256, FA_DQ_MIN_WAVES) void bwd_dq_kernel(
 }
 
 // ------------------------------------------------------------------ launch
-template <typename K>
-static hipError_t set_lds(K kern, int bytes)
-{
-    return hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                               hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-}
-
 template <int D, bool CAUSAL>
 static hipError_t launch_bwd_t(const BwdArgs &a)
 {
@@ -804,26 +616,17 @@ static hipError_t launch_bwd_t(const BwdArgs &a)
         if (e != hipSuccess) return e;
     }
     {
-        using S = DkdvShape<D>;
+        using S = DkdvSplitShape<D>;
         const int KT = (a.N + S::BN - 1) / S::BN;
         const int BHkv = a.B * a.Hkv;
-        hipError_t e;
-        if (a.deterministic) {
-            using SS = DkdvSplitShape<D>;
-            auto kern = bwd_dkdv_split_kernel<D, CAUSAL>;
-            hipLaunchKernelGGL(kern, dim3(BHkv * KT), dim3(SS::THREADS), 0, a.stream,
-                               (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v,
-                               (const uint16_t *)a.dout, a.lse2, a.delta, a.dk, a.dv, a.Hq, a.Hkv,
-                               a.N, BHkv, KT, a.scale, scale_log2);
-        } else {
-            auto kern = bwd_dkdv_atomic_kernel<D, CAUSAL>;
-            if ((e = set_lds(kern, S::LDS_BYTES)) != hipSuccess) return e;
-            hipLaunchKernelGGL(kern, dim3(BHkv * KT), dim3(S::THREADS), S::LDS_BYTES, a.stream,
-                               (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v,
-                               (const uint16_t *)a.dout, a.lse2, a.delta, a.dq, a.dk, a.dv, a.Hq,
-                               a.Hkv, a.N, BHkv, KT, a.scale, scale_log2);
-        }
-        if ((e = hipGetLastError()) != hipSuccess) return e;
+        auto kern = a.deterministic ? bwd_dkdv_split_kernel<D, CAUSAL, false>
+                                    : bwd_dkdv_split_kernel<D, CAUSAL, true>;
+        hipLaunchKernelGGL(kern, dim3(BHkv * KT), dim3(S::THREADS), 0, a.stream,
+                           (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v,
+                           (const uint16_t *)a.dout, a.lse2, a.delta, a.dq, a.dk, a.dv, a.Hq,
+                           a.Hkv, a.N, BHkv, KT, a.scale, scale_log2);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
     }
     if (a.deterministic) {
         using S = DqShape<D>;
