@@ -153,15 +153,20 @@ __global__ __launch_bounds__(256, FA_FWD_MIN_WAVES) void fwd_kernel(
     };
 
     // S^T_t = K_t Q^T (raw scores).  k-step outer: two independent chains.
-    auto scores = [&](f32x16(&st)[S::NKB], auto slot) {
+    // piece(s) runs after k-step s's products (tile copies placed in their
+    // shadow).
+    auto scores_with = [&](f32x16(&st)[S::NKB], auto slot, auto piece) {
         const char *kl = decltype(slot)::value ? k_lds1 : k_lds0;
 #pragma unroll
-        for (int s = 0; s < S::KSTEPS; s++)
+        for (int s = 0; s < S::KSTEPS; s++) {
 #pragma unroll
             for (int kb = 0; kb < S::NKB; kb++)
                 st[kb] = mfma32(lds_read_bf16x8(kl, koff[s] + kb * 32 * D * 2), qf[s],
                                 s == 0 ? f32x16{} : st[kb]);
+            piece(s);
+        }
     };
+    auto scores = [&](f32x16(&st)[S::NKB], auto slot) { scores_with(st, slot, [](int) {}); };
     auto apply_mask = [&](f32x16(&st)[S::NKB], int t) {
 #pragma unroll
         for (int kb = 0; kb < S::NKB; kb++)
@@ -236,10 +241,26 @@ __global__ __launch_bounds__(256, FA_FWD_MIN_WAVES) void fwd_kernel(
         using Here = std::integral_constant<int, P>;
         using There = std::integral_constant<int, 1 - P>;
         dma_barrier();
-        if (NEXT) issue_v(t + 1, There{});
-        if (t + 2 < n_tiles) issue_k(t + 2, Here{});
         bf16x8 pf[S::KVSTEPS];
-        if (NEXT) scores(nxt, There{});
+        if constexpr (NEXT == 1) {
+            // Full steps: tiles t + 1 (V) and t + 2 (K) are whole; their
+            // copies go one per k-step between the score products.
+            constexpr int PW = S::KTile::PER_WAVE;
+            char *vdst = P ? v_lds0 : v_lds1;
+            char *kdst = P ? k_lds1 : k_lds0;
+            const bool knext = (t + 3) * S::BN <= N && t + 2 < n_tiles;  // whole tile
+            if (!knext && t + 2 < n_tiles) issue_k(t + 2, Here{});
+            scores_with(nxt, There{}, [&](int s) {
+                if (s < PW)
+                    kv_dma.issue_block(vrs, (t + 1) * S::BN, vdst, wave, s);
+                else if (s < 2 * PW && knext)
+                    kv_dma.issue_block(krs, (t + 2) * S::BN, kdst, wave, s - PW);
+            });
+        } else {
+            if (NEXT) issue_v(t + 1, There{});
+            if (t + 2 < n_tiles) issue_k(t + 2, Here{});
+            if (NEXT) scores(nxt, There{});
+        }
         exp_pack(cur, pf);
         pv(pf, Here{});
         if (NEXT == 2 && t + 1 >= n_full) apply_mask(nxt, t + 1);

@@ -90,6 +90,17 @@ __device__ __forceinline__ void lds_dma16_buf(const BufRsrc &rs, uint32_t voff, 
                  :: "{m0}"(m0), "v"(voff), "s"(rs.r), "s"(soff) : "memory");
 }
 
+// The same copy without a memory clobber: for copies placed between matrix
+// products (the step barriers, which carry the clobber, order them against
+// every LDS access of the slot they fill).
+__device__ __forceinline__ void lds_dma16_buf_nc(const BufRsrc &rs, uint32_t voff, uint32_t soff,
+                                                 lds_void_t *dst)
+{
+    const uint32_t m0 = (uint32_t)reinterpret_cast<uintptr_t>(dst);
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :: "{m0}"(m0), "v"(voff), "s"(rs.r), "s"(soff));
+}
+
 // HBM -> LDS staging of a [ROWS][D] bf16 tile without registers
 // (global_load_lds_dwordx4).  One wave instruction writes 1 KB of LDS: lane
 // L's 16 bytes land at base + 16 L, so each lane fetches the logical chunk the
@@ -138,6 +149,13 @@ struct DmaTile {
                 lds_dma16(src, (lds_void_t *)(lds + (wave * PER_WAVE + i) * 1024));
             }
         }
+    }
+    // Block i of a full tile (rows row0 .. row0 + ROWS - 1 all < N), alone.
+    __device__ __forceinline__ void issue_block(const BufRsrc &rs, int row0, char *lds, int wave,
+                                                int i) const
+    {
+        lds_dma16_buf_nc(rs, goff[i], (uint32_t)row0 * (D * 2),
+                         (lds_void_t *)(lds + (wave * PER_WAVE + i) * 1024));
     }
     // The same copy from a buffer resource over the head's rows (every
     // offset stays below N * D * 2 bytes).
