@@ -10,8 +10,8 @@
 // page, Key Contributions, item 2); P never goes through shared memory (the
 // guide's "Register-Level Softmax Streaming").
 //
-// gfx950 mapping (one workgroup = 4 waves = BM = 128 query rows of one head,
-// two workgroups per CU):
+// gfx950 mapping (one workgroup = 8 waves = BM = 256 query rows of one head,
+// one workgroup per CU, two waves per SIMD):
 //   * each wave owns 32 query rows; it computes S^T = K Q^T (keys x queries)
 //     with v_mfma_f32_32x32x16_bf16, so every lane holds one query column:
 //     row max and row sum are in-lane, plus one swap between the wave halves;
@@ -38,9 +38,9 @@ namespace fa {
 
 template <int D>
 struct FwdShape {
-    static constexpr int BM = 128;           // query rows per workgroup
+    static constexpr int BM = 256;           // query rows per workgroup (32 per wave)
     static constexpr int BN = 64;            // keys per tile
-    static constexpr int THREADS = 256;      // 4 waves
+    static constexpr int THREADS = 512;      // 8 waves: each K / V tile copied once per 256 rows
     static constexpr int KSTEPS = D / 16;    // k-steps of S^T = K Q^T
     static constexpr int DBLK = D / 32;      // 32-row blocks of O^T
     static constexpr int NKB = BN / 32;      // 32-key blocks of S^T
@@ -72,7 +72,7 @@ struct FwdShape {
 // VALU rate on gfx950 and the polynomial costs about seven full-rate
 // operations, so the default is none.
 template <int D, bool CAUSAL, int POLY>
-__global__ __launch_bounds__(256, FA_FWD_MIN_WAVES) void fwd_kernel(
+__global__ __launch_bounds__(512, FA_FWD_MIN_WAVES) void fwd_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, float *__restrict__ o, float *__restrict__ lse, int Hq,
     int Hkv, int N, int BH, int QT, float scale_log2, float tau)
