@@ -104,7 +104,8 @@ def gpu_bwd(fa, q, k, v, dout, o, lse, scale, causal, deterministic):
 
 # -------------------------------------------------------------- small sweep
 
-SWEEP = [(n, d, c) for n in (1, 2, 3, 17, 64, 127, 128, 129, 300) for d in (64, 128) for c in (False, True)]
+SWEEP = [(n, d, c) for n in (1, 2, 3, 17, 64, 127, 128, 129, 255, 256, 257, 300, 600)
+         for d in (64, 128) for c in (False, True)]
 
 
 def sweep_shape(N):
@@ -196,10 +197,11 @@ def test_planted_max_jump(fa, jump, causal):
 
 def sampled_rows(w, n_rows, seed):
     """Rows spread over every head, including the first and last row of each
-    head and rows at 64/128-row tile edges."""
+    head and rows at 64-, 128- and 256-row tile edges."""
     rng = np.random.default_rng(seed)
     BH = w.B * w.Hq
-    edges = np.array([0, 63, 64, 127, 128, w.N // 2, w.N - 129, w.N - 65, w.N - 1])
+    edges = np.array([0, 63, 64, 127, 128, 255, 256, w.N // 2, w.N - 257, w.N - 129, w.N - 65,
+                      w.N - 1])
     per = max(1, n_rows // BH)
     rows = []
     for bh in range(BH):
