@@ -14,7 +14,8 @@ The fp64 CPU oracle is timed on a bounded sample (16 heads' forward and
 backward) of the same workload as a reported baseline.
 
 "per_config" then times each of the five synthetic workloads on its own
-(forward; both backward modes where the workload has a backward): launches back
+(forward; both backward modes for the backward workload and for the
+long-context GQA shape): launches back
 to back after 0.3 s of untimed ones, an event pair around each launch, median
 and minimum reported.  --no-per-config skips it (profiling runs use that, so the
 kernel averages cover the step's launches only).
@@ -89,17 +90,17 @@ def time_launches(fn, reps, stream, warm_s=0.3):
 
 
 def per_config(fa, reps, dev, stream):
-    """Forward (and, for the backward workload, both backward modes) of each
-    synthetic workload, timed on its own."""
+    """Forward (and, for the backward workload and the long-context GQA shape,
+    both backward modes) of each synthetic workload, timed on its own."""
     import numpy as np
     import torch
     from synth import WORKLOADS, make_inputs
+    from dataclasses import replace
 
     def to_dev(bits):
         return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
 
-    rows = []
-    for w in WORKLOADS.values():
+    def one(w):
         x = make_inputs(w)
         q, k, v = to_dev(x["q"]), to_dev(x["k"]), to_dev(x["v"])
         B, Hq, Hkv, N, d = w.B, w.Hq, w.Hkv, w.N, w.d
@@ -138,9 +139,16 @@ def per_config(fa, reps, dev, stream):
 
                 name = "fa_bwd deterministic" if det else "fa_bwd atomic"
                 row["calls"].append(entry(name, w.bwd_flops(), time_launches(bwd, reps, stream)))
-        rows.append(row)
-        del x, q, k, v, o, lse
-    torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        return row
+
+    rows = []
+    for w in WORKLOADS.values():
+        # The long-context GQA shape also runs its backward (both modes): dO
+        # is drawn after V, so Q, K and V are the forward workload's own.
+        if w.name == "fwd_causal_gqa_n32768":
+            w = replace(w, backward=True)
+        rows.append(one(w))  # the workload's tensors are freed on return
     return rows
 
 
