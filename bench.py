@@ -283,7 +283,7 @@ def main():
     # dP is not counted).
     cz = "true" if w.causal else "false"
     if parts["fwd_ms_avg"] >= parts["bwd_deterministic_ms_avg"]:
-        rl_kernels = [f"fa::fwd_kernel<{d}, {cz}, 0>"]
+        rl_kernels = [f"fa::fwd_kernel<{d}, {cz}, 0, false>"]
         rl_flops, rl_ms = f_fwd, parts["fwd_ms_avg"]
     else:
         rl_kernels = [f"fa::bwd_pre_kernel<{d}>", f"fa::bwd_dkdv_split_kernel<{d}, {cz}, false>",

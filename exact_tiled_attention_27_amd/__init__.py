@@ -1,10 +1,11 @@
 """Exact tiled attention for AMD MI355X (gfx950): Python binding of libfa.so.
 
-The functions fa_fwd, fa_bwd, fa_bwd_workspace_bytes and fa_status_string
-mirror the C ABI in include/fa.h one for one; this module only marshals
-arguments (device pointers, sizes, the current HIP stream).  Every step of the
-computation runs in the library's HIP kernels; there is no fallback path, and
-importing this package fails if libfa.so has not been built.
+The functions fa_fwd, fa_fwd_splitkv, fa_fwd_splitkv_workspace_bytes, fa_bwd,
+fa_bwd_workspace_bytes and fa_status_string mirror the C ABI in include/fa.h
+one for one; this module only marshals arguments (device pointers, sizes, the
+current HIP stream).  Every step of the computation runs in the library's HIP
+kernels; there is no fallback path, and importing this package fails if
+libfa.so has not been built.
 
 Convenience wrappers attention_fwd / attention_bwd allocate the outputs with
 torch on the inputs' device and call the same entry points.
@@ -13,10 +14,13 @@ import ctypes
 import math
 import os
 
-__all__ = ["fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_status_string", "FAError",
-           "attention_fwd", "attention_bwd", "LIB_PATH", "STATUS"]
+__all__ = ["fa_fwd", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_bytes", "fa_bwd",
+           "fa_bwd_workspace_bytes", "fa_status_string", "FAError", "attention_fwd",
+           "attention_bwd", "LIB_PATH", "STATUS", "MAX_SPLITS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
+
+MAX_SPLITS = 64  # FA_MAX_SPLITS
 
 STATUS = {0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_UNSUPPORTED",
           4: "FA_ERR_ALIGN", 5: "FA_ERR_WORKSPACE", 6: "FA_ERR_HIP"}
@@ -36,6 +40,11 @@ _vp, _fp = ctypes.c_void_p, ctypes.c_void_p
 _i, _f, _sz = ctypes.c_int, ctypes.c_float, ctypes.c_size_t
 _lib.fa_fwd.argtypes = [_vp, _vp, _vp, _fp, _fp, _i, _i, _i, _i, _i, _f, _i, _vp]
 _lib.fa_fwd.restype = _i
+_lib.fa_fwd_splitkv.argtypes = [_vp, _vp, _vp, _fp, _fp, _i, _i, _i, _i, _i, _f, _i, _i, _vp,
+                                _sz, _vp]
+_lib.fa_fwd_splitkv.restype = _i
+_lib.fa_fwd_splitkv_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i]
+_lib.fa_fwd_splitkv_workspace_bytes.restype = _sz
 _lib.fa_bwd.argtypes = [_vp, _vp, _vp, _fp, _fp, _vp, _fp, _fp, _fp, _i, _i, _i, _i, _i, _f,
                         _i, _i, _vp, _sz, _vp]
 _lib.fa_bwd.restype = _i
@@ -80,6 +89,18 @@ def fa_fwd(q, k, v, o, lse, B, Hq, Hkv, N, d, scale, causal, stream=None) -> int
                        float(scale), int(bool(causal)), _stream(stream, q, o))
 
 
+def fa_fwd_splitkv(q, k, v, o, lse, B, Hq, Hkv, N, d, scale, causal, num_splits, workspace,
+                   workspace_bytes, stream=None) -> int:
+    """C ABI fa_fwd_splitkv.  Tensors (or integer device addresses) in, status out."""
+    return _lib.fa_fwd_splitkv(_addr(q), _addr(k), _addr(v), _addr(o), _addr(lse), B, Hq, Hkv,
+                               N, d, float(scale), int(bool(causal)), int(num_splits),
+                               _addr(workspace), int(workspace_bytes), _stream(stream, q, o))
+
+
+def fa_fwd_splitkv_workspace_bytes(B, Hq, Hkv, N, d, num_splits) -> int:
+    return int(_lib.fa_fwd_splitkv_workspace_bytes(B, Hq, Hkv, N, d, int(num_splits)))
+
+
 def fa_bwd_workspace_bytes(B, Hq, Hkv, N, d, deterministic) -> int:
     return int(_lib.fa_bwd_workspace_bytes(B, Hq, Hkv, N, d, int(bool(deterministic))))
 
@@ -105,8 +126,10 @@ def _check_inputs(*ts):
             raise ValueError("q/k/v/dout must be contiguous bfloat16 [B, H, N, d] tensors")
 
 
-def attention_fwd(q, k, v, scale=None, causal=False, o=None, lse=None, stream=None):
-    """Forward attention on device tensors.  Returns (o fp32, lse fp32)."""
+def attention_fwd(q, k, v, scale=None, causal=False, o=None, lse=None, stream=None,
+                  num_splits=1, workspace=None):
+    """Forward attention on device tensors.  Returns (o fp32, lse fp32).
+    num_splits > 1 runs the split-KV forward (fa_fwd_splitkv)."""
     import torch
     _check_inputs(q, k, v)
     B, Hq, Hkv, N, d = _dims(q, k)
@@ -115,9 +138,18 @@ def attention_fwd(q, k, v, scale=None, causal=False, o=None, lse=None, stream=No
         o = torch.empty((B, Hq, N, d), dtype=torch.float32, device=q.device)
     if lse is None:
         lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
-    st = fa_fwd(q, k, v, o, lse, B, Hq, Hkv, N, d, scale, causal, stream)
+    if num_splits == 1:
+        st = fa_fwd(q, k, v, o, lse, B, Hq, Hkv, N, d, scale, causal, stream)
+        if st:
+            raise FAError(st, "fa_fwd")
+        return o, lse
+    need = fa_fwd_splitkv_workspace_bytes(B, Hq, Hkv, N, d, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    st = fa_fwd_splitkv(q, k, v, o, lse, B, Hq, Hkv, N, d, scale, causal, num_splits, workspace,
+                        workspace.numel() * workspace.element_size(), stream)
     if st:
-        raise FAError(st, "fa_fwd")
+        raise FAError(st, "fa_fwd_splitkv")
     return o, lse
 
 

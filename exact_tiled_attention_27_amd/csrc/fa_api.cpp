@@ -91,7 +91,45 @@ int fa_fwd(const void *q, const void *k, const void *v, float *o, float *lse, in
         (lse && !aligned16(lse)))
         return FA_ERR_ALIGN;
     fa::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, N, d, scale, rescale_tau(), causal != 0,
-                  exp2_poly_share(), reinterpret_cast<hipStream_t>(stream)};
+                  exp2_poly_share(), 1, nullptr, nullptr, reinterpret_cast<hipStream_t>(stream)};
+    return hip_status(fa::launch_fwd(a));
+}
+
+size_t fa_fwd_splitkv_workspace_bytes(int B, int Hq, int Hkv, int N, int d, int num_splits)
+{
+    if (check_common(B, Hq, Hkv, N, d, 1.0f) != FA_OK) return 0;
+    if (num_splits < 1 || num_splits > FA_MAX_SPLITS) return 0;
+    if (num_splits == 1) return 0;
+    const size_t rows = (size_t)num_splits * B * Hq * (size_t)N;
+    return round256(rows * (size_t)d * sizeof(float)) + round256(rows * sizeof(float));
+}
+
+int fa_fwd_splitkv(const void *q, const void *k, const void *v, float *o, float *lse, int B,
+                   int Hq, int Hkv, int N, int d, float scale, int causal, int num_splits,
+                   void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (!q || !k || !v || !o) return FA_ERR_NULL;
+    int st = check_common(B, Hq, Hkv, N, d, scale);
+    if (st != FA_OK) return st;
+    if (num_splits < 1 || num_splits > FA_MAX_SPLITS) return FA_ERR_SHAPE;
+    // Workgroups: B * Hq * ceil(N / 256) query tiles times the chunks.
+    if ((int64_t)B * Hq * ((N + 255) / 256) * num_splits > INT32_MAX) return FA_ERR_SHAPE;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+        (lse && !aligned16(lse)))
+        return FA_ERR_ALIGN;
+    float *opart = nullptr, *lpart = nullptr;
+    if (num_splits > 1) {
+        const size_t need = fa_fwd_splitkv_workspace_bytes(B, Hq, Hkv, N, d, num_splits);
+        if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
+        if (!aligned16(workspace)) return FA_ERR_ALIGN;
+        const size_t rows = (size_t)num_splits * B * Hq * (size_t)N;
+        opart = reinterpret_cast<float *>(workspace);
+        lpart = reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) +
+                                          round256(rows * (size_t)d * sizeof(float)));
+    }
+    fa::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, N, d, scale, rescale_tau(), causal != 0,
+                  exp2_poly_share(), num_splits, opart, lpart,
+                  reinterpret_cast<hipStream_t>(stream)};
     return hip_status(fa::launch_fwd(a));
 }
 

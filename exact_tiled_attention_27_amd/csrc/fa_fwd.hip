@@ -71,11 +71,17 @@ struct FwdShape {
 // 4 one in four (score rows r % 4 == 3), 1 all.  v_exp_f32 issues at half the
 // VALU rate on gfx950 and the polynomial costs about seven full-rate
 // operations, so the default is none.
-template <int D, bool CAUSAL, int POLY>
+// SPLIT: the keys of each query tile are cut into n_splits chunks of whole
+// tiles, one workgroup per (query tile, chunk); a workgroup writes its
+// chunk's normalised partial O and partial LSE to opart / lpart
+// ([n_splits][B * Hq][N] rows) for fwd_merge_kernel.  A row with no valid key
+// in its chunk (causal) gets O = 0 and LSE = -inf there.
+template <int D, bool CAUSAL, int POLY, bool SPLIT>
 __global__ __launch_bounds__(512, FA_FWD_MIN_WAVES) void fwd_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, float *__restrict__ o, float *__restrict__ lse, int Hq,
-    int Hkv, int N, int BH, int QT, float scale_log2, float tau)
+    int Hkv, int N, int BH, int QT, float scale_log2, float tau, int n_splits,
+    float *__restrict__ opart, float *__restrict__ lpart)
 {
     using S = FwdShape<D>;
     __shared__ __attribute__((aligned(16))) char k_lds0[S::TILE_BYTES];
@@ -89,12 +95,48 @@ __global__ __launch_bounds__(512, FA_FWD_MIN_WAVES) void fwd_kernel(
     const int h = lane >> 5, col = lane & 31;
     const int g16 = lane >> 4;  // 16-lane group
 
-    int bh, qt;
-    xcd_tile_map(blockIdx.x, BH, QT, CAUSAL, bh, qt);
+    int bh, qt, split = 0;
+    if (SPLIT) {
+        int vt;  // (query tile, chunk) pairs, longest first when causal
+        xcd_tile_map(blockIdx.x, BH, QT * n_splits, CAUSAL, bh, vt);
+        qt = vt / n_splits;
+        split = vt % n_splits;
+    } else {
+        xcd_tile_map(blockIdx.x, BH, QT, CAUSAL, bh, qt);
+    }
     const int b = bh / Hq, hq = bh % Hq;
     const int g = hq / (Hq / Hkv);
     const int q0 = qt * S::BM;
     const int qrow = q0 + wave * 32 + col;  // the query column this lane owns
+
+    const int n_tiles_all = (N + S::BN - 1) / S::BN;
+    const int n_tiles_q = CAUSAL ? min(n_tiles_all, (min(q0 + S::BM, N) + S::BN - 1) / S::BN)
+                                 : n_tiles_all;
+    // This workgroup's key tiles [t_begin, n_tiles): all of them, or its chunk.
+    int t_begin = 0, n_tiles = n_tiles_q;
+    if (SPLIT) {
+        const int per = (n_tiles_q + n_splits - 1) / n_splits;
+        t_begin = min(split * per, n_tiles_q);
+        n_tiles = min(t_begin + per, n_tiles_q);
+        if (t_begin >= n_tiles) {
+            // Empty chunk (more chunks than tiles): O = 0, LSE = -inf.
+            if (qrow < N) {
+                const size_t prow = ((size_t)split * BH + bh) * N + qrow;
+                float *orow = opart + prow * D;
+                const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int db = 0; db < S::DBLK; db++)
+#pragma unroll
+                    for (int gq = 0; gq < 4; gq++)
+                        *reinterpret_cast<f32x4 *>(orow + db * 32 + 8 * gq + 4 * h) = z;
+                if (h == 0) lpart[prow] = -INFINITY;
+            }
+            return;
+        }
+    }
+    // Tiles every key of which is < N and (causal) <= q0 need no mask (and,
+    // split, lie in the chunk).
+    const int n_full = min(n_tiles, CAUSAL ? min(N / S::BN, (q0 + 1) / S::BN) : N / S::BN);
 
     const uint16_t *qh = q + ((size_t)b * Hq + hq) * N * D;
     const uint16_t *kh = k + ((size_t)b * Hkv + g) * N * D;
@@ -129,11 +171,6 @@ __global__ __launch_bounds__(512, FA_FWD_MIN_WAVES) void fwd_kernel(
     float m_ref = -INFINITY;  // reference maximum (base-2 domain) the exponent subtracts
     float l_part = 0.f;       // this lane's part of the row sum
 
-    const int n_tiles_all = (N + S::BN - 1) / S::BN;
-    const int n_tiles = CAUSAL ? min(n_tiles_all, (min(q0 + S::BM, N) + S::BN - 1) / S::BN)
-                               : n_tiles_all;
-    // Tiles every key of which is < N and (causal) <= q0 need no mask.
-    const int n_full = CAUSAL ? min(N / S::BN, (q0 + 1) / S::BN) : N / S::BN;
 
     // K and V tiles have one shape, so one set of per-lane copy offsets.
     typename S::KTile kv_dma;
@@ -274,20 +311,20 @@ __global__ __launch_bounds__(512, FA_FWD_MIN_WAVES) void fwd_kernel(
     // barrier drains both; the loads are settled right after it, so none is
     // still counted when the loop's copies start); S_0.
     f32x16 sa[S::NKB], sb[S::NKB];
-    issue_k(0, Slot0{});
-    issue_v(0, Slot0{});
-    if (n_tiles > 1) issue_k(1, Slot1{});
+    issue_k(t_begin, Slot0{});
+    issue_v(t_begin, Slot0{});
+    if (t_begin + 1 < n_tiles) issue_k(t_begin + 1, Slot1{});
     dma_barrier();
 #pragma unroll
     for (int s = 0; s < S::KSTEPS; s++) settle(qf[s]);
     scores(sa, Slot0{});
-    if (n_full == 0) apply_mask(sa, 0);
+    if (n_full <= t_begin) apply_mask(sa, t_begin);
     row_max_rescale(sa);
 
     // Unrolled by two: the score registers and LDS slots alternate statically.
     // Steps whose next tile is unmasked first, then the (at most a few)
     // diagonal and tail tiles.
-    int t = 0;
+    int t = t_begin;
     for (; t + 2 < n_full; t += 2) {
         step(Full{}, Slot0{}, sa, sb, t);
         step(Full{}, Slot1{}, sb, sa, t + 1);
@@ -305,6 +342,23 @@ __global__ __launch_bounds__(512, FA_FWD_MIN_WAVES) void fwd_kernel(
 
     // Epilogue: O = O / l, LSE = (m + log2 l) * ln 2.
     const float l_tot = halves_sum(l_part);
+    if (SPLIT) {
+        if (qrow < N) {
+            const size_t prow = ((size_t)split * BH + bh) * N + qrow;
+            float *orow = opart + prow * D;
+            const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;  // no valid key: O = 0
+#pragma unroll
+            for (int db = 0; db < S::DBLK; db++)
+#pragma unroll
+                for (int gq = 0; gq < 4; gq++) {
+                    f32x4 val = {acc[db][4 * gq] * inv, acc[db][4 * gq + 1] * inv,
+                                 acc[db][4 * gq + 2] * inv, acc[db][4 * gq + 3] * inv};
+                    *reinterpret_cast<f32x4 *>(orow + db * 32 + 8 * gq + 4 * h) = val;
+                }
+            if (h == 0) lpart[prow] = l_tot > 0.f ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
+        }
+        return;
+    }
     const float inv = 1.f / l_tot;
     if (qrow < N) {
         float *orow = o + (((size_t)b * Hq + hq) * N + qrow) * D;
@@ -320,20 +374,64 @@ __global__ __launch_bounds__(512, FA_FWD_MIN_WAVES) void fwd_kernel(
     }
 }
 
+// Merge of the split-KV partial results, one row per D / 4 threads: with
+// M = max_s LSE_s and w_s = exp(LSE_s - M), O = sum_s w_s O_s / sum_s w_s and
+// LSE = M + ln sum_s w_s, the log-sum-exp over the union of the chunks' keys
+// (each O_s is normalised by its own chunk's sum).  Chunk 0 holds key 0,
+// valid for every row, so M is finite and sum_s w_s >= 1.
+template <int D>
+__global__ __launch_bounds__(256) void fwd_merge_kernel(const float *__restrict__ opart,
+                                                        const float *__restrict__ lpart,
+                                                        float *__restrict__ o,
+                                                        float *__restrict__ lse, size_t rows,
+                                                        int n_splits)
+{
+    constexpr int TPR = D / 4;  // threads per row, 4 values each
+    const size_t row = (size_t)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
+    const int part = threadIdx.x % TPR;
+    if (row >= rows) return;
+    float m = -INFINITY;
+    for (int s = 0; s < n_splits; s++) m = fmaxf(m, lpart[(size_t)s * rows + row]);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    float wsum = 0.f;
+    for (int s = 0; s < n_splits; s++) {
+        const float w = exp2_hw((lpart[(size_t)s * rows + row] - m) * kLog2e);  // -inf -> 0
+        const f32x4 x = *reinterpret_cast<const f32x4 *>(opart + ((size_t)s * rows + row) * D + 4 * part);
+        acc += w * x;
+        wsum += w;
+    }
+    *reinterpret_cast<f32x4 *>(o + row * D + 4 * part) = acc * (1.f / wsum);
+    if (lse && part == 0) lse[row] = m + logf(wsum);
+}
+
+template <int D, bool CAUSAL, bool SPLIT>
+static hipError_t launch_fwd_split(const FwdArgs &a)
+{
+    using S = FwdShape<D>;
+    const int QT = (a.N + S::BM - 1) / S::BM;
+    const int BH = a.B * a.Hq;
+    auto kern = a.poly == 1 ? fwd_kernel<D, CAUSAL, 1, SPLIT>
+              : a.poly == 4 ? fwd_kernel<D, CAUSAL, 4, SPLIT>
+                            : fwd_kernel<D, CAUSAL, 0, SPLIT>;
+    const int splits = SPLIT ? a.splits : 1;
+    hipLaunchKernelGGL(kern, dim3(BH * QT * splits), dim3(S::THREADS), 0, a.stream,
+                       (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v, a.o,
+                       a.lse, a.Hq, a.Hkv, a.N, BH, QT, a.scale * kLog2e, a.tau, splits, a.opart,
+                       a.lpart);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !SPLIT) return e;
+    const size_t rows = (size_t)BH * a.N;
+    constexpr int RPB = 256 / (D / 4);  // rows per merge block
+    hipLaunchKernelGGL(fwd_merge_kernel<D>, dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0,
+                       a.stream, a.opart, a.lpart, a.o, a.lse, rows, splits);
+    return hipGetLastError();
+}
+
 template <int D, bool CAUSAL>
 static hipError_t launch_fwd_t(const FwdArgs &a)
 {
-    using S = FwdShape<D>;
     (void)hipGetLastError();  // clear an error left by an earlier, unrelated call
-    const int QT = (a.N + S::BM - 1) / S::BM;
-    const int BH = a.B * a.Hq;
-    auto kern = a.poly == 1 ? fwd_kernel<D, CAUSAL, 1>
-              : a.poly == 4 ? fwd_kernel<D, CAUSAL, 4>
-                            : fwd_kernel<D, CAUSAL, 0>;
-    hipLaunchKernelGGL(kern, dim3(BH * QT), dim3(S::THREADS), 0, a.stream,
-                       (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v, a.o,
-                       a.lse, a.Hq, a.Hkv, a.N, BH, QT, a.scale * kLog2e, a.tau);
-    return hipGetLastError();
+    return a.splits > 1 ? launch_fwd_split<D, CAUSAL, true>(a) : launch_fwd_split<D, CAUSAL, false>(a);
 }
 
 hipError_t launch_fwd(const FwdArgs &a)

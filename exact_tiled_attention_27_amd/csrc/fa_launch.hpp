@@ -14,6 +14,9 @@ struct FwdArgs {
     float tau;     // rescale threshold in the base-2 exponent domain
     bool causal;
     int poly;      // exponentials on the FMA units: 0 none, 4 one in four, 1 all
+    int splits;    // key chunks per query tile (1: one pass, no partials)
+    float *opart;  // splits > 1: partial O, [splits][B * Hq][N][d] fp32
+    float *lpart;  // splits > 1: partial LSE, [splits][B * Hq][N] fp32
     hipStream_t stream;
 };
 

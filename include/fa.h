@@ -84,6 +84,39 @@ int fa_fwd(const void *q, const void *k, const void *v, float *o, float *lse,
            int B, int Hq, int Hkv, int N, int d, float scale, int causal, void *stream);
 
 /*
+ * Split-KV forward: the same result as fa_fwd (up to rounding), computed with
+ * the keys of every query tile cut into num_splits chunks that separate
+ * workgroups process, each writing a partial O normalised by its own row
+ * sums and a partial LSE; a merge pass then combines them per row as
+ * O = sum_s w_s O_s / sum_s w_s, LSE = M + ln sum_s w_s with
+ * w_s = exp(LSE_s - M), M = max_s LSE_s.  The combination is the identity of
+ * the online softmax (the running max and sum of the page "FlashAttention-4
+ * Guide: Kernel Pipelining on Blackwell", "The Asymmetric Hardware Scaling
+ * Wall") applied to whole chunks instead of single tiles.  It pays when
+ * B * Hq * ceil(N / 256) workgroups leave the chip's compute units idle
+ * (few heads, long sequences).
+ *   num_splits: 1 .. FA_MAX_SPLITS; 1 is fa_fwd itself (no workspace needed).
+ *   workspace / workspace_bytes: device scratch of at least
+ *     fa_fwd_splitkv_workspace_bytes(...) bytes, 16-byte aligned, owned by
+ *     the caller, contents ignored on entry: the partial O
+ *     ([num_splits][B * Hq][N][d] fp32) and partial LSE
+ *     ([num_splits][B * Hq][N] fp32), each rounded up to 256 bytes.
+ *   Other arguments and outputs as in fa_fwd; num_splits outside the range
+ *   returns FA_ERR_SHAPE.
+ * Returns an fa_status.
+ */
+#define FA_MAX_SPLITS 64
+int fa_fwd_splitkv(const void *q, const void *k, const void *v, float *o, float *lse,
+                   int B, int Hq, int Hkv, int N, int d, float scale, int causal,
+                   int num_splits, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Bytes of workspace fa_fwd_splitkv needs; 0 when num_splits == 1 or for an
+ * invalid shape or split count.
+ */
+size_t fa_fwd_splitkv_workspace_bytes(int B, int Hq, int Hkv, int N, int d, int num_splits);
+
+/*
  * Bytes of device workspace fa_bwd needs for this shape: the per-row
  * D_i = sum_c dO_ic O_ic and the base-2 LSE, two fp32 arrays [B, Hq, N']
  * with N' = N rounded up to a multiple of 64, each rounded up to 256 bytes.

@@ -26,7 +26,8 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert names == ["fa_bwd", "fa_bwd_workspace_bytes", "fa_fwd", "fa_status_string"]
+    assert names == ["fa_bwd", "fa_bwd_workspace_bytes", "fa_fwd", "fa_fwd_splitkv",
+                     "fa_fwd_splitkv_workspace_bytes", "fa_status_string"]
     out = subprocess.run(["nm", "-D", "--defined-only", fa.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\sT\s(\w+)$", out, flags=re.M))
@@ -60,6 +61,44 @@ def fwd(**kw):
 ])
 def test_fwd_rejects(kw, status):
     assert fwd(**kw) == status
+
+
+def fwd_split(**kw):
+    args = dict(q=A, k=A, v=A, o=A, lse=A, B=1, Hq=2, Hkv=2, N=128, d=64, scale=0.125,
+                causal=0, num_splits=4, workspace=A, workspace_bytes=1 << 30, stream=0)
+    args.update(kw)
+    return fa.fa_fwd_splitkv(**args)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(o=None), 1),
+    (dict(B=0), 2), (dict(Hq=3, Hkv=2), 2), (dict(scale=0.0), 2), (dict(N=1 << 23, d=128), 2),
+    (dict(num_splits=0), 2), (dict(num_splits=-1), 2), (dict(num_splits=fa.MAX_SPLITS + 1), 2),
+    # more workgroups than a 32-bit grid holds
+    (dict(B=1 << 14, Hq=1 << 10, Hkv=1, N=4096, num_splits=fa.MAX_SPLITS), 2),
+    (dict(d=96), 3),
+    (dict(q=MIS), 4), (dict(lse=MIS), 4), (dict(workspace=MIS), 4),
+    (dict(workspace=None), 5), (dict(workspace_bytes=0), 5), (dict(workspace_bytes=4096), 5),
+])
+def test_fwd_splitkv_rejects(kw, status):
+    assert fwd_split(**kw) == status
+
+
+def test_splitkv_workspace_bytes():
+    # partial O [S][B*Hq][N][d] and partial LSE [S][B*Hq][N], fp32, each to 256 B
+    rows = 4 * 2 * 2 * 1000
+    assert fa.fa_fwd_splitkv_workspace_bytes(2, 2, 1, 1000, 128, 4) == \
+        (rows * 128 * 4 + 255) // 256 * 256 + (rows * 4 + 255) // 256 * 256
+    assert fa.fa_fwd_splitkv_workspace_bytes(1, 2, 2, 3, 64, 2) == 2 * 2 * 3 * 64 * 4 + 256
+    assert fa.fa_fwd_splitkv_workspace_bytes(1, 2, 2, 128, 64, 1) == 0   # one pass, no partials
+    assert fa.fa_fwd_splitkv_workspace_bytes(1, 2, 2, 128, 64, 0) == 0
+    assert fa.fa_fwd_splitkv_workspace_bytes(1, 2, 2, 128, 64, fa.MAX_SPLITS + 1) == 0
+    assert fa.fa_fwd_splitkv_workspace_bytes(1, 2, 2, 128, 48, 2) == 0
+    need = fa.fa_fwd_splitkv_workspace_bytes(1, 2, 2, 128, 64, 4)
+    assert fwd_split(workspace_bytes=need - 1) == 5
+    assert fwd_split(workspace_bytes=need, o=MIS) == 4
+    # one split needs no workspace: the remaining checks still run
+    assert fwd_split(num_splits=1, workspace=None, workspace_bytes=0, v=MIS) == 4
 
 
 def bwd(**kw):

@@ -358,3 +358,68 @@ def test_long_context_gqa_backward(fa):
     again = gpu_bwd(fa, x["q"], x["k"], x["v"], x["dout"], o, lse, w.scale, w.causal, 1)
     for a, b_ in zip(again, det_result):
         assert np.array_equal(a.view(np.uint32), b_.view(np.uint32))
+
+
+# ---------------------------------------------------------- split-KV forward
+
+def gpu_fwd_split(fa, q, k, v, scale, causal, splits):
+    """fa_fwd_splitkv with a workspace of 0xFF bytes (NaN as fp32): a partial
+    the merge reads without its chunk having written it shows up as NaN."""
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    o = Guarded((B, Hq, N, d))
+    lse = Guarded((B, Hq, N))
+    need = fa.fa_fwd_splitkv_workspace_bytes(B, Hq, Hkv, N, d, splits)
+    ws = torch.full((max(need, 256),), 255, dtype=torch.uint8, device="cuda")
+    st = fa.fa_fwd_splitkv(dev(q), dev(k), dev(v), o.t, lse.t, B, Hq, Hkv, N, d, scale, causal,
+                           splits, ws, need)
+    assert st == 0, fa.fa_status_string(st)
+    return o.result("o"), lse.result("lse")
+
+
+# N = 3 and 64: more chunks than key tiles (empty chunks); causal: rows with no
+# valid key inside a chunk; 600: chunks of unequal length and a ragged tail.
+SPLIT_SWEEP = [(n, d, c, s) for n in (3, 64, 300, 600) for d in (64, 128) for c in (False, True)
+               for s in (2, 7)]
+
+
+@pytest.mark.parametrize("N,d,causal,splits", SPLIT_SWEEP)
+def test_fwd_splitkv_small(fa, N, d, causal, splits):
+    B, Hq, Hkv = sweep_shape(N)
+    note(f"fwd split-KV B={B} Hq={Hq} Hkv={Hkv} N={N} d={d} causal={causal} splits={splits}")
+    q, k, v = random_bf16((B, Hq, N, d), N), random_bf16((B, Hkv, N, d), N + 1), random_bf16((B, Hkv, N, d), N + 2)
+    scale = 1 / math.sqrt(d)
+    o, lse = gpu_fwd_split(fa, q, k, v, scale, causal, splits)
+    o_ref, lse_ref = oracle.fwd(q, k, v, scale, causal)
+    compare("o", o, o_ref)
+    compare_lse(lse, lse_ref)
+
+
+def test_fwd_splitkv_one_split_is_fa_fwd(fa):
+    """num_splits = 1 runs the single-pass forward: bitwise equal outputs."""
+    B, Hq, Hkv, N, d = 1, 4, 2, 300, 128
+    q, k, v = random_bf16((B, Hq, N, d), 1), random_bf16((B, Hkv, N, d), 2), random_bf16((B, Hkv, N, d), 3)
+    for causal in (False, True):
+        o1, l1 = gpu_fwd(fa, q, k, v, 0.1, causal)
+        o = Guarded((B, Hq, N, d))
+        lse = Guarded((B, Hq, N))
+        st = fa.fa_fwd_splitkv(dev(q), dev(k), dev(v), o.t, lse.t, B, Hq, Hkv, N, d, 0.1, causal,
+                               1, None, 0)
+        assert st == 0, fa.fa_status_string(st)
+        assert np.array_equal(o.result("o"), o1) and np.array_equal(lse.result("lse"), l1)
+
+
+@pytest.mark.parametrize("causal,splits", [(True, 4), (False, 3)])
+def test_fwd_splitkv_long_context(fa, causal, splits):
+    """Few heads, N = 16384: the shape split-KV is for (64 query tiles per head
+    of 256 rows); non-causal with 3 chunks of 86, 86 and 84 key tiles."""
+    B, Hq, Hkv, N, d = 1, 4, 2, 16384, 128
+    note(f"fwd split-KV long context causal={causal} splits={splits}")
+    w = replace(WORKLOADS["fwd_n4096"], B=B, Hq=Hq, Hkv=Hkv, N=N, causal=causal, seed=47)
+    x = make_inputs(w)
+    o, lse = gpu_fwd_split(fa, x["q"], x["k"], x["v"], w.scale, causal, splits)
+    assert np.isfinite(lse).all()
+    rows = sampled_rows(w, 512, w.seed)
+    o_ref, lse_ref = oracle.fwd_rows(x["q"], x["k"], x["v"], w.scale, causal, rows)
+    compare("o (sampled rows)", o.reshape(-1, d)[rows], o_ref)
+    compare_lse(lse.reshape(-1)[rows], lse_ref)
