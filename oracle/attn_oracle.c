@@ -19,7 +19,11 @@
  *     O_i  = (sum_j p_ij v_j) / l_i,   LSE_i = m_i + ln(l_i)
  *
  *   Causal masking keeps key j for query i iff j <= i (the simulator's
- *   "Apply causal mask inside tile" step keeps q_idx >= kv_idx).
+ *   "Apply causal mask inside tile" step keeps q_idx >= kv_idx).  A causal
+ *   sliding window of W >= 1 keys (the banded mask a score/mask hook of the
+ *   FlexAttention kind expresses; the guide's deployment section names such
+ *   custom masks) further drops keys j <= i - W: query i sees keys
+ *   max(0, i - W + 1) .. i.  W <= 0 means no window.
  *   Grouped-query attention: query head h reads key/value head
  *   h / (Hq / Hkv) (contiguous groups).
  *
@@ -68,8 +72,12 @@ static int check_shape(int B, int Hq, int Hkv, int N, int d)
     return 1;
 }
 
-/* Number of keys query i may attend to. */
-static int n_valid(int i, int N, int causal) { return causal ? i + 1 : N; }
+/* Keys query i may attend to: lo .. hi (inclusive). */
+static int key_hi(int i, int N, int causal) { return causal ? i : N - 1; }
+static int key_lo(int i, int causal, int window)
+{
+    return (causal && window > 0 && i - window + 1 > 0) ? i - window + 1 : 0;
+}
 
 /* Offset of row n of head h of batch b in a [B, H, N, d] tensor. */
 static size_t row_off(int b, int h, int H, int n, int N, int d)
@@ -101,13 +109,14 @@ static double scores_row(const uint16_t *qi, const uint16_t *kh, int n, int d,
  * may be NULL).  Used for whole tensors (all rows) and for sampled rows of
  * tensors too large to check in full.
  */
-int oracle_fwd_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v,
-                    int B, int Hq, int Hkv, int N, int d, float scale, int causal,
-                    const int64_t *rows, int64_t nrows, double *o_rows, double *lse_rows,
-                    int nthreads)
+int oracle_fwd_rows_w(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                      int B, int Hq, int Hkv, int N, int d, float scale, int causal, int window,
+                      const int64_t *rows, int64_t nrows, double *o_rows, double *lse_rows,
+                      int nthreads)
 {
     if (!q || !k || !v || !rows || nrows < 0) return ORACLE_BAD_ARGS;
     if (!check_shape(B, Hq, Hkv, N, d)) return ORACLE_BAD_ARGS;
+    if (window > 0 && !causal) return ORACLE_BAD_ARGS;
     const int64_t total = (int64_t)B * Hq * N;
     for (int64_t r = 0; r < nrows; r++)
         if (rows[r] < 0 || rows[r] >= total) return ORACLE_BAD_ARGS;
@@ -133,9 +142,11 @@ int oracle_fwd_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v,
             const int b = (int)(flat / ((int64_t)N * Hq));
             const int g = h / group;
             const uint16_t *qi = q + row_off(b, h, Hq, i, N, d);
-            const uint16_t *kh = k + row_off(b, g, Hkv, 0, N, d);
-            const uint16_t *vh = v + row_off(b, g, Hkv, 0, N, d);
-            const int n = n_valid(i, N, causal);
+            const int lo = key_lo(i, causal, window);
+            const int n = key_hi(i, N, causal) - lo + 1;
+            /* keys lo .. lo + n - 1, indexed 0 .. n - 1 below */
+            const uint16_t *kh = k + row_off(b, g, Hkv, lo, N, d);
+            const uint16_t *vh = v + row_off(b, g, Hkv, lo, N, d);
 
             const double m = scores_row(qi, kh, n, d, sc, s);
             double l = 0.0;
@@ -158,9 +169,19 @@ int oracle_fwd_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v,
     return failed ? ORACLE_NO_MEMORY : ORACLE_OK;
 }
 
+int oracle_fwd_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                    int B, int Hq, int Hkv, int N, int d, float scale, int causal,
+                    const int64_t *rows, int64_t nrows, double *o_rows, double *lse_rows,
+                    int nthreads)
+{
+    return oracle_fwd_rows_w(q, k, v, B, Hq, Hkv, N, d, scale, causal, 0, rows, nrows, o_rows,
+                             lse_rows, nthreads);
+}
+
 /* Whole forward: O [B,Hq,N,d], LSE [B,Hq,N] (LSE may be NULL). */
-int oracle_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, double *o, double *lse,
-               int B, int Hq, int Hkv, int N, int d, float scale, int causal, int nthreads)
+int oracle_fwd_w(const uint16_t *q, const uint16_t *k, const uint16_t *v, double *o, double *lse,
+                 int B, int Hq, int Hkv, int N, int d, float scale, int causal, int window,
+                 int nthreads)
 {
     if (!o) return ORACLE_BAD_ARGS;
     if (!check_shape(B, Hq, Hkv, N, d)) return ORACLE_BAD_ARGS;
@@ -168,10 +189,16 @@ int oracle_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, double *
     int64_t *rows = (int64_t *)malloc(sizeof(int64_t) * (size_t)total);
     if (!rows) return ORACLE_NO_MEMORY;
     for (int64_t r = 0; r < total; r++) rows[r] = r;
-    int st = oracle_fwd_rows(q, k, v, B, Hq, Hkv, N, d, scale, causal, rows, total, o, lse,
-                             nthreads);
+    int st = oracle_fwd_rows_w(q, k, v, B, Hq, Hkv, N, d, scale, causal, window, rows, total, o,
+                               lse, nthreads);
     free(rows);
     return st;
+}
+
+int oracle_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, double *o, double *lse,
+               int B, int Hq, int Hkv, int N, int d, float scale, int causal, int nthreads)
+{
+    return oracle_fwd_w(q, k, v, o, lse, B, Hq, Hkv, N, d, scale, causal, 0, nthreads);
 }
 
 /*
@@ -194,17 +221,19 @@ int oracle_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, double *
  * i >= row0 is the ordinary row result.  Outputs hold the tail only:
  * dq [ngroups, Hq/Hkv, N - row0, d], dk and dv [ngroups, N - row0, d], o and
  * lse likewise.  row0 = 0 is the full backward (and the only value allowed
- * without the causal mask).
+ * without the causal mask).  With a window, key j receives gradient from rows
+ * j .. j + W - 1 only, still all >= j.
  */
-int oracle_bwd_groups_tail(const uint16_t *q, const uint16_t *k, const uint16_t *v,
-                           const uint16_t *dout, int B, int Hq, int Hkv, int N, int d,
-                           float scale, int causal, int row0, const int64_t *groups,
-                           int64_t ngroups, double *dq, double *dk, double *dv, double *o,
-                           double *lse, int nthreads)
+int oracle_bwd_groups_tail_w(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                             const uint16_t *dout, int B, int Hq, int Hkv, int N, int d,
+                             float scale, int causal, int window, int row0,
+                             const int64_t *groups, int64_t ngroups, double *dq, double *dk,
+                             double *dv, double *o, double *lse, int nthreads)
 {
     if (!q || !k || !v || !dout || !groups || !dq || !dk || !dv || ngroups < 0)
         return ORACLE_BAD_ARGS;
     if (!check_shape(B, Hq, Hkv, N, d)) return ORACLE_BAD_ARGS;
+    if (window > 0 && !causal) return ORACLE_BAD_ARGS;
     if (row0 < 0 || row0 >= N || (!causal && row0 != 0)) return ORACLE_BAD_ARGS;
     for (int64_t t = 0; t < ngroups; t++)
         if (groups[t] < 0 || groups[t] >= (int64_t)B * Hkv) return ORACLE_BAD_ARGS;
@@ -251,9 +280,12 @@ int oracle_bwd_groups_tail(const uint16_t *q, const uint16_t *k, const uint16_t 
                 const int h = g * group + hl;
                 const uint16_t *qi = q + row_off(b, h, Hq, i, N, d);
                 const uint16_t *doi = dout + row_off(b, h, Hq, i, N, d);
-                const int n = n_valid(i, N, causal);
+                const int lo = key_lo(i, causal, window);
+                const int n = key_hi(i, N, causal) - lo + 1;
+                const uint16_t *khi = kh + (size_t)lo * d; /* keys lo .. lo + n - 1 */
+                const uint16_t *vhi = vh + (size_t)lo * d;
 
-                const double m = scores_row(qi, kh, n, d, sc, s);
+                const double m = scores_row(qi, khi, n, d, sc, s);
                 double l = 0.0;
                 for (int j = 0; j < n; j++) {
                     s[j] = exp(s[j] - m);
@@ -261,7 +293,7 @@ int oracle_bwd_groups_tail(const uint16_t *q, const uint16_t *k, const uint16_t 
                 }
                 for (int c = 0; c < d; c++) acc[c] = 0.0;
                 for (int j = 0; j < n; j++) {
-                    const uint16_t *vj = vh + (size_t)j * d;
+                    const uint16_t *vj = vhi + (size_t)j * d;
                     for (int c = 0; c < d; c++) acc[c] += s[j] * bf16_to_double(vj[c]);
                 }
                 double *oi = o_buf + (size_t)rr * d;
@@ -275,8 +307,8 @@ int oracle_bwd_groups_tail(const uint16_t *q, const uint16_t *k, const uint16_t 
                 /* dQ_i = scale * sum_j dS_ij k_j */
                 for (int c = 0; c < d; c++) acc[c] = 0.0;
                 for (int j = 0; j < n; j++) {
-                    const uint16_t *vj = vh + (size_t)j * d;
-                    const uint16_t *kj = kh + (size_t)j * d;
+                    const uint16_t *vj = vhi + (size_t)j * d;
+                    const uint16_t *kj = khi + (size_t)j * d;
                     double dp = 0.0;
                     for (int c = 0; c < d; c++) dp += bf16_to_double(doi[c]) * bf16_to_double(vj[c]);
                     const double P = s[j] / l;
@@ -308,8 +340,10 @@ int oracle_bwd_groups_tail(const uint16_t *q, const uint16_t *k, const uint16_t 
                 for (int c = 0; c < d; c++) acck[c] = accv[c] = 0.0;
                 for (int hl = 0; hl < group; hl++) {
                     const int h = g * group + hl;
-                    const int i0 = causal ? j : 0; /* queries that see key j (>= row0) */
-                    for (int i = i0; i < N; i++) {
+                    /* queries that see key j (>= row0): j .. j + W - 1 with a window */
+                    const int i0 = causal ? j : 0;
+                    const int i1 = (causal && window > 0 && j + window < N) ? j + window : N;
+                    for (int i = i0; i < i1; i++) {
                         const size_t rr = (size_t)hl * NT + (i - row0);
                         const uint16_t *qi = q + row_off(b, h, Hq, i, N, d);
                         const uint16_t *doi = dout + row_off(b, h, Hq, i, N, d);
@@ -345,11 +379,21 @@ int oracle_bwd_groups_tail(const uint16_t *q, const uint16_t *k, const uint16_t 
     return failed ? ORACLE_NO_MEMORY : ORACLE_OK;
 }
 
+int oracle_bwd_groups_tail(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                           const uint16_t *dout, int B, int Hq, int Hkv, int N, int d,
+                           float scale, int causal, int row0, const int64_t *groups,
+                           int64_t ngroups, double *dq, double *dk, double *dv, double *o,
+                           double *lse, int nthreads)
+{
+    return oracle_bwd_groups_tail_w(q, k, v, dout, B, Hq, Hkv, N, d, scale, causal, 0, row0,
+                                    groups, ngroups, dq, dk, dv, o, lse, nthreads);
+}
+
 int oracle_bwd_groups(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                       const uint16_t *dout, int B, int Hq, int Hkv, int N, int d, float scale,
                       int causal, const int64_t *groups, int64_t ngroups, double *dq, double *dk,
                       double *dv, double *o, double *lse, int nthreads)
 {
-    return oracle_bwd_groups_tail(q, k, v, dout, B, Hq, Hkv, N, d, scale, causal, 0, groups,
-                                  ngroups, dq, dk, dv, o, lse, nthreads);
+    return oracle_bwd_groups_tail_w(q, k, v, dout, B, Hq, Hkv, N, d, scale, causal, 0, 0, groups,
+                                    ngroups, dq, dk, dv, o, lse, nthreads);
 }
