@@ -1,8 +1,8 @@
 """Exact tiled attention for AMD MI355X (gfx950): Python binding of libfa.so.
 
-The functions fa_fwd, fa_fwd_splitkv, fa_fwd_splitkv_workspace_bytes, fa_bwd,
-fa_bwd_workspace_bytes and fa_status_string mirror the C ABI in include/fa.h
-one for one; this module only marshals arguments (device pointers, sizes, the
+The functions fa_fwd, fa_fwd_window, fa_fwd_splitkv,
+fa_fwd_splitkv_workspace_bytes, fa_bwd, fa_bwd_window, fa_bwd_workspace_bytes
+and fa_status_string mirror the C ABI in include/fa.h one for one; this module only marshals arguments (device pointers, sizes, the
 current HIP stream).  Every step of the computation runs in the library's HIP
 kernels; there is no fallback path, and importing this package fails if
 libfa.so has not been built.
@@ -14,9 +14,9 @@ import ctypes
 import math
 import os
 
-__all__ = ["fa_fwd", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_bytes", "fa_bwd",
-           "fa_bwd_workspace_bytes", "fa_status_string", "FAError", "attention_fwd",
-           "attention_bwd", "LIB_PATH", "STATUS", "MAX_SPLITS"]
+__all__ = ["fa_fwd", "fa_fwd_window", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_bytes",
+           "fa_bwd", "fa_bwd_window", "fa_bwd_workspace_bytes", "fa_status_string", "FAError",
+           "attention_fwd", "attention_bwd", "LIB_PATH", "STATUS", "MAX_SPLITS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
@@ -40,6 +40,11 @@ _vp, _fp = ctypes.c_void_p, ctypes.c_void_p
 _i, _f, _sz = ctypes.c_int, ctypes.c_float, ctypes.c_size_t
 _lib.fa_fwd.argtypes = [_vp, _vp, _vp, _fp, _fp, _i, _i, _i, _i, _i, _f, _i, _vp]
 _lib.fa_fwd.restype = _i
+_lib.fa_fwd_window.argtypes = [_vp, _vp, _vp, _fp, _fp, _i, _i, _i, _i, _i, _f, _i, _vp]
+_lib.fa_fwd_window.restype = _i
+_lib.fa_bwd_window.argtypes = [_vp, _vp, _vp, _fp, _fp, _vp, _fp, _fp, _fp, _i, _i, _i, _i, _i,
+                               _f, _i, _i, _vp, _sz, _vp]
+_lib.fa_bwd_window.restype = _i
 _lib.fa_fwd_splitkv.argtypes = [_vp, _vp, _vp, _fp, _fp, _i, _i, _i, _i, _i, _f, _i, _i, _vp,
                                 _sz, _vp]
 _lib.fa_fwd_splitkv.restype = _i
@@ -87,6 +92,21 @@ def fa_fwd(q, k, v, o, lse, B, Hq, Hkv, N, d, scale, causal, stream=None) -> int
     """C ABI fa_fwd.  Tensors (or integer device addresses) in, status out."""
     return _lib.fa_fwd(_addr(q), _addr(k), _addr(v), _addr(o), _addr(lse), B, Hq, Hkv, N, d,
                        float(scale), int(bool(causal)), _stream(stream, q, o))
+
+
+def fa_fwd_window(q, k, v, o, lse, B, Hq, Hkv, N, d, scale, window, stream=None) -> int:
+    """C ABI fa_fwd_window (causal sliding window).  Status out."""
+    return _lib.fa_fwd_window(_addr(q), _addr(k), _addr(v), _addr(o), _addr(lse), B, Hq, Hkv, N,
+                              d, float(scale), int(window), _stream(stream, q, o))
+
+
+def fa_bwd_window(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, N, d, scale, window,
+                  deterministic, workspace, workspace_bytes, stream=None) -> int:
+    """C ABI fa_bwd_window (causal sliding window).  Status out."""
+    return _lib.fa_bwd_window(_addr(q), _addr(k), _addr(v), _addr(o), _addr(lse), _addr(dout),
+                              _addr(dq), _addr(dk), _addr(dv), B, Hq, Hkv, N, d, float(scale),
+                              int(window), int(bool(deterministic)), _addr(workspace),
+                              int(workspace_bytes), _stream(stream, q, dq))
 
 
 def fa_fwd_splitkv(q, k, v, o, lse, B, Hq, Hkv, N, d, scale, causal, num_splits, workspace,

@@ -63,6 +63,48 @@ int exp2_poly_share()
     return 0;
 }
 
+// fa_fwd and fa_fwd_window: window 0 = none (then causal as given), else
+// causal with that window (>= 1, checked by the caller).
+int fwd_impl(const void *q, const void *k, const void *v, float *o, float *lse, int B, int Hq,
+             int Hkv, int N, int d, float scale, int causal, int window, void *stream)
+{
+    if (!q || !k || !v || !o) return FA_ERR_NULL;
+    int st = check_common(B, Hq, Hkv, N, d, scale);
+    if (st != FA_OK) return st;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+        (lse && !aligned16(lse)))
+        return FA_ERR_ALIGN;
+    fa::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, N, d, scale, rescale_tau(), causal != 0,
+                  exp2_poly_share(), window < N ? window : 0, 1, nullptr, nullptr,
+                  reinterpret_cast<hipStream_t>(stream)};
+    return hip_status(fa::launch_fwd(a));
+}
+
+// fa_bwd and fa_bwd_window: window as in fwd_impl.
+int bwd_impl(const void *q, const void *k, const void *v, const float *o, const float *lse,
+             const void *dout, float *dq, float *dk, float *dv, int B, int Hq, int Hkv, int N,
+             int d, float scale, int causal, int window, int deterministic, void *workspace,
+             size_t workspace_bytes, void *stream)
+{
+    if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL;
+    int st = check_common(B, Hq, Hkv, N, d, scale);
+    if (st != FA_OK) return st;
+    const void *ptrs[] = {q, k, v, o, lse, dout, dq, dk, dv};
+    for (const void *p : ptrs)
+        if (!aligned16(p)) return FA_ERR_ALIGN;
+    const size_t need = fa_bwd_workspace_bytes(B, Hq, Hkv, N, d, deterministic);
+    if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return FA_ERR_ALIGN;
+    const size_t rows = workspace_rows(B, Hq, N);
+    float *delta = reinterpret_cast<float *>(workspace);
+    float *lse2 = reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) +
+                                            round256(rows * sizeof(float)));
+    fa::BwdArgs a{q, k, v, dout, o, lse, dq, dk, dv, delta, lse2, B, Hq, Hkv, N, d, scale,
+                  causal != 0, deterministic != 0, window < N ? window : 0,
+                  reinterpret_cast<hipStream_t>(stream)};
+    return hip_status(fa::launch_bwd(a));
+}
+
 }  // namespace
 
 extern "C" {
@@ -84,15 +126,14 @@ const char *fa_status_string(int status)
 int fa_fwd(const void *q, const void *k, const void *v, float *o, float *lse, int B, int Hq,
            int Hkv, int N, int d, float scale, int causal, void *stream)
 {
-    if (!q || !k || !v || !o) return FA_ERR_NULL;
-    int st = check_common(B, Hq, Hkv, N, d, scale);
-    if (st != FA_OK) return st;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
-        (lse && !aligned16(lse)))
-        return FA_ERR_ALIGN;
-    fa::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, N, d, scale, rescale_tau(), causal != 0,
-                  exp2_poly_share(), 1, nullptr, nullptr, reinterpret_cast<hipStream_t>(stream)};
-    return hip_status(fa::launch_fwd(a));
+    return fwd_impl(q, k, v, o, lse, B, Hq, Hkv, N, d, scale, causal, 0, stream);
+}
+
+int fa_fwd_window(const void *q, const void *k, const void *v, float *o, float *lse, int B,
+                  int Hq, int Hkv, int N, int d, float scale, int window, void *stream)
+{
+    if (window < 1) return FA_ERR_SHAPE;
+    return fwd_impl(q, k, v, o, lse, B, Hq, Hkv, N, d, scale, 1, window, stream);
 }
 
 size_t fa_fwd_splitkv_workspace_bytes(int B, int Hq, int Hkv, int N, int d, int num_splits)
@@ -128,7 +169,7 @@ int fa_fwd_splitkv(const void *q, const void *k, const void *v, float *o, float 
                                           round256(rows * (size_t)d * sizeof(float)));
     }
     fa::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, N, d, scale, rescale_tau(), causal != 0,
-                  exp2_poly_share(), num_splits, opart, lpart,
+                  exp2_poly_share(), 0, num_splits, opart, lpart,
                   reinterpret_cast<hipStream_t>(stream)};
     return hip_status(fa::launch_fwd(a));
 }
@@ -145,22 +186,18 @@ int fa_bwd(const void *q, const void *k, const void *v, const float *o, const fl
            int d, float scale, int causal, int deterministic, void *workspace,
            size_t workspace_bytes, void *stream)
 {
-    if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL;
-    int st = check_common(B, Hq, Hkv, N, d, scale);
-    if (st != FA_OK) return st;
-    const void *ptrs[] = {q, k, v, o, lse, dout, dq, dk, dv};
-    for (const void *p : ptrs)
-        if (!aligned16(p)) return FA_ERR_ALIGN;
-    const size_t need = fa_bwd_workspace_bytes(B, Hq, Hkv, N, d, deterministic);
-    if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
-    if (!aligned16(workspace)) return FA_ERR_ALIGN;
-    const size_t rows = workspace_rows(B, Hq, N);
-    float *delta = reinterpret_cast<float *>(workspace);
-    float *lse2 = reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) +
-                                            round256(rows * sizeof(float)));
-    fa::BwdArgs a{q, k, v, dout, o, lse, dq, dk, dv, delta, lse2, B, Hq, Hkv, N, d, scale,
-                  causal != 0, deterministic != 0, reinterpret_cast<hipStream_t>(stream)};
-    return hip_status(fa::launch_bwd(a));
+    return bwd_impl(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, N, d, scale, causal, 0,
+                    deterministic, workspace, workspace_bytes, stream);
+}
+
+int fa_bwd_window(const void *q, const void *k, const void *v, const float *o, const float *lse,
+                  const void *dout, float *dq, float *dk, float *dv, int B, int Hq, int Hkv,
+                  int N, int d, float scale, int window, int deterministic, void *workspace,
+                  size_t workspace_bytes, void *stream)
+{
+    if (window < 1) return FA_ERR_SHAPE;
+    return bwd_impl(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, N, d, scale, 1, window,
+                    deterministic, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -128,7 +128,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_split_kernel(
     const uint16_t *__restrict__ v, const uint16_t *__restrict__ dout,
     const float *__restrict__ lse2, const float *__restrict__ delta, float *__restrict__ dq,
     float *__restrict__ dk, float *__restrict__ dv, int Hq, int Hkv, int N, int BHkv, int KT,
-    float scale, float scale_log2)
+    float scale, float scale_log2, int window)
 {
     using S = DkdvSplitShape<D>;
     // Atomic mode only: the workgroup's K rows (B operand of dQ = dS K) and
@@ -182,8 +182,11 @@ __global__ __launch_bounds__(512) void bwd_dkdv_split_kernel(
             troff[db][rho] = tr_off(8 * rho + 4 * h, 32 * db + 16 * (g16 & 1), lane, D);
     char *xchg = xchg_lds + slice * S::X_SLICE + lane * 16;  // + (qb*4 + gq) * 1024
 
+    // Query tiles that see the workgroup's keys: from the diagonal on
+    // (causal), up to key kv0 + BN - 1 + window - 1 (sliding window).
     const int first_qt = CAUSAL ? kv0 / S::BM : 0;
-    const int n_qt = (N + S::BM - 1) / S::BM;
+    const int n_qt_all = (N + S::BM - 1) / S::BM;
+    const int n_qt = CAUSAL ? min(n_qt_all, (kv0 + S::BN + window - 2) / S::BM + 1) : n_qt_all;
     const int steps_per_head = n_qt - first_qt;
     const int n_steps = grp * steps_per_head;
 
@@ -284,7 +287,8 @@ __global__ __launch_bounds__(512) void bwd_dkdv_split_kernel(
 
         if (wave_a) {
             // P = exp2(s * c - LSE2); masked pairs get a -inf exponent.
-            const bool need_mask = kv0 + S::BN > N || qs + S::BM > N || (CAUSAL && qs < kv0 + S::BN - 1);
+            const bool need_mask = kv0 + S::BN > N || qs + S::BM > N ||
+                                   (CAUSAL && (qs < kv0 + S::BN - 1 || qs + S::BM - 1 - kv0 >= window));
             auto softmax = [&](auto masked) {
                 constexpr bool MASK = decltype(masked)::value;
 #pragma unroll
@@ -298,7 +302,8 @@ __global__ __launch_bounds__(512) void bwd_dkdv_split_kernel(
                             float e = __builtin_fmaf(x[qb][4 * gq + i], scale_log2, -l2[i]);
                             if (MASK) {
                                 const int qi = qs + qr + i;
-                                const bool dead = key >= N || qi >= N || (CAUSAL && key > qi);
+                                const bool dead = key >= N || qi >= N ||
+                                                  (CAUSAL && (key > qi || qi - key >= window));
                                 e = dead ? -INFINITY : e;
                             }
                             x[qb][4 * gq + i] = exp2_hw(e);
@@ -418,7 +423,7 @@ __global__ __launch_bounds__(256, FA_DQ_MIN_WAVES) void bwd_dq_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, const uint16_t *__restrict__ dout,
     const float *__restrict__ lse2, const float *__restrict__ delta, float *__restrict__ dq,
-    int Hq, int Hkv, int N, int BH, int QT, float scale, float scale_log2)
+    int Hq, int Hkv, int N, int BH, int QT, float scale, float scale_log2, int window)
 {
     using S = DqShape<D>;
     __shared__ __attribute__((aligned(16))) char k_lds0[S::TILE];
@@ -478,6 +483,10 @@ __global__ __launch_bounds__(256, FA_DQ_MIN_WAVES) void bwd_dq_kernel(
                                : n_tiles_all;
     // Tiles every key of which is < N and (causal) <= q0 need no mask.
     const int n_full = CAUSAL ? min(N / S::BN, (q0 + 1) / S::BN) : N / S::BN;
+    // Causal sliding window: t_lo is the first tile any row sees, w_full the
+    // first one every row sees whole.
+    const int t_lo = CAUSAL ? max(0, q0 - window + 1) / S::BN : 0;
+    const int w_full = CAUSAL ? (max(0, q0 + S::BM - window) + S::BN - 1) / S::BN : 0;
 
     typename S::Tile tile;
     tile.init(wave, lane);
@@ -527,7 +536,7 @@ __global__ __launch_bounds__(256, FA_DQ_MIN_WAVES) void bwd_dq_kernel(
                 float x = __builtin_fmaf(st[r], scale_log2, -l2);
                 if (MASK) {
                     const int kk = key0 + kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                    const bool dead = kk >= N || (CAUSAL && kk > qrow);
+                    const bool dead = kk >= N || (CAUSAL && (kk > qrow || qrow - kk >= window));
                     x = dead ? -INFINITY : x;
                 }
                 dpt[r] = exp2_hw(x) * (dpt[r] - dl);
@@ -563,7 +572,7 @@ __global__ __launch_bounds__(256, FA_DQ_MIN_WAVES) void bwd_dq_kernel(
 
     // First copies while the Q / dO row loads are in flight; the barrier
     // drains both, and the loads are settled before the loop's copies start.
-    issue(0, Slot0{});
+    issue(t_lo, Slot0{});
     dma_barrier();
 #pragma unroll
     for (int s = 0; s < S::KSTEPS; s++) {
@@ -574,7 +583,11 @@ __global__ __launch_bounds__(256, FA_DQ_MIN_WAVES) void bwd_dq_kernel(
     settle(dl);
     // Unrolled by two so that LDS slots are compile-time constants; unmasked
     // tiles first, then the diagonal and tail tiles.
-    int t = 0;
+    int t = t_lo;
+    for (; t < w_full && t + 2 <= n_tiles; t += 2) {  // tiles the window cuts
+        step(std::true_type{}, Slot0{}, t);
+        step(std::true_type{}, Slot1{}, t + 1);
+    }
     for (; t + 2 <= n_full; t += 2) {
         step(std::false_type{}, Slot0{}, t);
         step(std::false_type{}, Slot1{}, t + 1);
@@ -624,7 +637,8 @@ static hipError_t launch_bwd_t(const BwdArgs &a)
         hipLaunchKernelGGL(kern, dim3(BHkv * KT), dim3(S::THREADS), 0, a.stream,
                            (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v,
                            (const uint16_t *)a.dout, a.lse2, a.delta, a.dq, a.dk, a.dv, a.Hq,
-                           a.Hkv, a.N, BHkv, KT, a.scale, scale_log2);
+                           a.Hkv, a.N, BHkv, KT, a.scale, scale_log2,
+                           a.window > 0 ? a.window : kNoWindow);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -636,7 +650,7 @@ static hipError_t launch_bwd_t(const BwdArgs &a)
         hipLaunchKernelGGL(kern, dim3(BH * QT), dim3(S::THREADS), 0, a.stream,
                            (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v,
                            (const uint16_t *)a.dout, a.lse2, a.delta, a.dq, a.Hq, a.Hkv, a.N, BH,
-                           QT, a.scale, scale_log2);
+                           QT, a.scale, scale_log2, a.window > 0 ? a.window : kNoWindow);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     return hipSuccess;

@@ -80,7 +80,7 @@ template <int D, bool CAUSAL, int POLY, bool SPLIT>
 __global__ __launch_bounds__(512, FA_FWD_MIN_WAVES) void fwd_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, float *__restrict__ o, float *__restrict__ lse, int Hq,
-    int Hkv, int N, int BH, int QT, float scale_log2, float tau, int n_splits,
+    int Hkv, int N, int BH, int QT, float scale_log2, float tau, int window, int n_splits,
     float *__restrict__ opart, float *__restrict__ lpart)
 {
     using S = FwdShape<D>;
@@ -112,11 +112,16 @@ __global__ __launch_bounds__(512, FA_FWD_MIN_WAVES) void fwd_kernel(
     const int n_tiles_all = (N + S::BN - 1) / S::BN;
     const int n_tiles_q = CAUSAL ? min(n_tiles_all, (min(q0 + S::BM, N) + S::BN - 1) / S::BN)
                                  : n_tiles_all;
+    // Causal sliding window (window >= 1; at least N means none): query i
+    // sees keys i - window + 1 .. i.  t_lo: the first tile any row of the
+    // workgroup sees; w_full: the first tile every row sees whole.
+    const int t_lo = CAUSAL ? max(0, q0 - window + 1) / S::BN : 0;
+    const int w_full = CAUSAL ? (max(0, q0 + S::BM - window) + S::BN - 1) / S::BN : 0;
     // This workgroup's key tiles [t_begin, n_tiles): all of them, or its chunk.
-    int t_begin = 0, n_tiles = n_tiles_q;
+    int t_begin = t_lo, n_tiles = n_tiles_q;
     if (SPLIT) {
-        const int per = (n_tiles_q + n_splits - 1) / n_splits;
-        t_begin = min(split * per, n_tiles_q);
+        const int per = (n_tiles_q - t_lo + n_splits - 1) / n_splits;
+        t_begin = min(t_lo + split * per, n_tiles_q);
         n_tiles = min(t_begin + per, n_tiles_q);
         if (t_begin >= n_tiles) {
             // Empty chunk (more chunks than tiles): O = 0, LSE = -inf.
@@ -210,7 +215,7 @@ __global__ __launch_bounds__(512, FA_FWD_MIN_WAVES) void fwd_kernel(
 #pragma unroll
             for (int r = 0; r < 16; r++) {
                 const int key = t * S::BN + kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                const bool dead = key >= N || (CAUSAL && key > qrow);
+                const bool dead = key >= N || (CAUSAL && (key > qrow || qrow - key >= window));
                 st[kb][r] = dead ? -INFINITY : st[kb][r];
             }
     };
@@ -300,7 +305,7 @@ __global__ __launch_bounds__(512, FA_FWD_MIN_WAVES) void fwd_kernel(
         }
         exp_pack(cur, pf);
         pv(pf, Here{});
-        if (NEXT == 2 && t + 1 >= n_full) apply_mask(nxt, t + 1);
+        if (NEXT == 2 && (t + 1 >= n_full || t + 1 < w_full)) apply_mask(nxt, t + 1);
         if (NEXT) row_max_rescale(nxt);
     };
     using Last = std::integral_constant<int, 0>;
@@ -318,13 +323,18 @@ __global__ __launch_bounds__(512, FA_FWD_MIN_WAVES) void fwd_kernel(
 #pragma unroll
     for (int s = 0; s < S::KSTEPS; s++) settle(qf[s]);
     scores(sa, Slot0{});
-    if (n_full <= t_begin) apply_mask(sa, t_begin);
+    if (n_full <= t_begin || t_begin < w_full) apply_mask(sa, t_begin);
     row_max_rescale(sa);
 
     // Unrolled by two: the score registers and LDS slots alternate statically.
     // Steps whose next tile is unmasked first, then the (at most a few)
     // diagonal and tail tiles.
     int t = t_begin;
+    // Sliding window: leading tiles the window cuts for some rows.
+    for (; t + 2 < n_tiles && t + 1 < w_full; t += 2) {
+        step(Any{}, Slot0{}, sa, sb, t);
+        step(Any{}, Slot1{}, sb, sa, t + 1);
+    }
     for (; t + 2 < n_full; t += 2) {
         step(Full{}, Slot0{}, sa, sb, t);
         step(Full{}, Slot1{}, sb, sa, t + 1);
@@ -416,8 +426,8 @@ static hipError_t launch_fwd_split(const FwdArgs &a)
     const int splits = SPLIT ? a.splits : 1;
     hipLaunchKernelGGL(kern, dim3(BH * QT * splits), dim3(S::THREADS), 0, a.stream,
                        (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v, a.o,
-                       a.lse, a.Hq, a.Hkv, a.N, BH, QT, a.scale * kLog2e, a.tau, splits, a.opart,
-                       a.lpart);
+                       a.lse, a.Hq, a.Hkv, a.N, BH, QT, a.scale * kLog2e, a.tau,
+                       a.window > 0 ? a.window : kNoWindow, splits, a.opart, a.lpart);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !SPLIT) return e;
     const size_t rows = (size_t)BH * a.N;

@@ -14,6 +14,7 @@ struct FwdArgs {
     float tau;     // rescale threshold in the base-2 exponent domain
     bool causal;
     int poly;      // exponentials on the FMA units: 0 none, 4 one in four, 1 all
+    int window;    // causal sliding window in keys (0: none)
     int splits;    // key chunks per query tile (1: one pass, no partials)
     float *opart;  // splits > 1: partial O, [splits][B * Hq][N][d] fp32
     float *lpart;  // splits > 1: partial LSE, [splits][B * Hq][N] fp32
@@ -29,6 +30,7 @@ struct BwdArgs {
     int B, Hq, Hkv, N, d;
     float scale;
     bool causal, deterministic;
+    int window;    // causal sliding window in keys (0: none)
     hipStream_t stream;
 };
 
@@ -37,5 +39,9 @@ hipError_t launch_bwd(const BwdArgs &a);
 
 // Rescale threshold: log2(256) = 8 (conditional rescaling).
 constexpr float kRescaleTau = 8.0f;
+
+// Window value the kernels receive when there is none: wider than any
+// sequence, and small enough that q0 + 256 - kNoWindow cannot overflow.
+constexpr int kNoWindow = 1 << 30;
 
 }  // namespace fa

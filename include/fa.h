@@ -84,6 +84,20 @@ int fa_fwd(const void *q, const void *k, const void *v, float *o, float *lse,
            int B, int Hq, int Hkv, int N, int d, float scale, int causal, void *stream);
 
 /*
+ * Causal sliding-window forward: query i attends to keys
+ * max(0, i - window + 1) .. i only, the banded mask of local attention (the
+ * page "FlashAttention-4 Guide: Kernel Pipelining on Blackwell", section
+ * "Production Deployment Guide", points to custom masks of this kind; the
+ * pages give no formula, so the band is the reading stated here).  Key tiles
+ * wholly outside the band are skipped.  window >= 1 (window >= N is plain
+ * causal attention); otherwise FA_ERR_SHAPE.  Other arguments and outputs as
+ * in fa_fwd; the LSE runs over the row's band.
+ * Returns an fa_status.
+ */
+int fa_fwd_window(const void *q, const void *k, const void *v, float *o, float *lse,
+                  int B, int Hq, int Hkv, int N, int d, float scale, int window, void *stream);
+
+/*
  * Split-KV forward: the same result as fa_fwd (up to rounding), computed with
  * the keys of every query tile cut into num_splits chunks that separate
  * workgroups process, each writing a partial O normalised by its own row
@@ -143,6 +157,17 @@ int fa_bwd(const void *q, const void *k, const void *v, const float *o, const fl
            const void *dout, float *dq, float *dk, float *dv,
            int B, int Hq, int Hkv, int N, int d, float scale, int causal, int deterministic,
            void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Backward of fa_fwd_window (same band; o and lse from fa_fwd_window with the
+ * same window).  Arguments, workspace (fa_bwd_workspace_bytes) and modes as
+ * in fa_bwd; window >= 1, otherwise FA_ERR_SHAPE.
+ * Returns an fa_status.
+ */
+int fa_bwd_window(const void *q, const void *k, const void *v, const float *o, const float *lse,
+                  const void *dout, float *dq, float *dk, float *dv,
+                  int B, int Hq, int Hkv, int N, int d, float scale, int window,
+                  int deterministic, void *workspace, size_t workspace_bytes, void *stream);
 
 /* Static, human-readable name of a status code (never NULL). */
 const char *fa_status_string(int status);

@@ -26,8 +26,9 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert names == ["fa_bwd", "fa_bwd_workspace_bytes", "fa_fwd", "fa_fwd_splitkv",
-                     "fa_fwd_splitkv_workspace_bytes", "fa_status_string"]
+    assert names == ["fa_bwd", "fa_bwd_window", "fa_bwd_workspace_bytes", "fa_fwd",
+                     "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_bytes", "fa_fwd_window",
+                     "fa_status_string"]
     out = subprocess.run(["nm", "-D", "--defined-only", fa.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\sT\s(\w+)$", out, flags=re.M))
@@ -61,6 +62,31 @@ def fwd(**kw):
 ])
 def test_fwd_rejects(kw, status):
     assert fwd(**kw) == status
+
+
+@pytest.mark.parametrize("window", [0, -1, -(1 << 31)])
+def test_window_rejects_non_positive(window):
+    args = dict(q=A, k=A, v=A, o=A, lse=A, B=1, Hq=2, Hkv=2, N=128, d=64, scale=0.125,
+                window=window, stream=0)
+    assert fa.fa_fwd_window(**args) == 2
+    bargs = dict(q=A, k=A, v=A, o=A, lse=A, dout=A, dq=A, dk=A, dv=A, B=1, Hq=2, Hkv=2, N=128,
+                 d=64, scale=0.125, window=window, deterministic=1, workspace=A,
+                 workspace_bytes=1 << 20, stream=0)
+    assert fa.fa_bwd_window(**bargs) == 2
+
+
+def test_window_validates_like_fa_fwd():
+    args = dict(q=A, k=A, v=A, o=A, lse=A, B=1, Hq=2, Hkv=2, N=128, d=64, scale=0.125,
+                window=16, stream=0)
+    assert fa.fa_fwd_window(**dict(args, q=None)) == 1
+    assert fa.fa_fwd_window(**dict(args, d=80)) == 3
+    assert fa.fa_fwd_window(**dict(args, o=MIS)) == 4
+    bargs = dict(q=A, k=A, v=A, o=A, lse=A, dout=A, dq=A, dk=A, dv=A, B=1, Hq=2, Hkv=2, N=128,
+                 d=64, scale=0.125, window=16, deterministic=0, workspace=A,
+                 workspace_bytes=1 << 20, stream=0)
+    assert fa.fa_bwd_window(**dict(bargs, dk=None)) == 1
+    assert fa.fa_bwd_window(**dict(bargs, workspace_bytes=16)) == 5
+    assert fa.fa_bwd_window(**dict(bargs, dv=MIS)) == 4
 
 
 def fwd_split(**kw):

@@ -2,9 +2,9 @@
 
 Bar (fp32 outputs O, dQ, dK, dV): max |err| <= 1e-2 and mean |err| <= 1e-3 over
 every compared element; LSE: |err| <= 1e-3 * max(1, |LSE_ref|).  One derived
-exception: with N < 64 an element of dV/dK/dQ sums only a handful of terms, so
-the bf16 rounding of P and dS (relative error up to 2^-9) does not average out;
-there the mean bar is 2e-3 (rounding P alone, emulated in numpy, already gives
+exception: with N < 64 (or a sliding window under 64 keys) an element of
+dV/dK/dQ sums only a handful of terms, so the bf16 rounding of P and dS
+(relative error up to 2^-9) does not average out; there the mean bar is 2e-3 (rounding P alone, emulated in numpy, already gives
 mean 1.25e-3 at N = 3, d = 128, GQA 2:1, and the kernel matches that emulation).
 
 Every output buffer is NaN-poisoned before the call and sits between NaN guard
@@ -423,3 +423,83 @@ def test_fwd_splitkv_long_context(fa, causal, splits):
     o_ref, lse_ref = oracle.fwd_rows(x["q"], x["k"], x["v"], w.scale, causal, rows)
     compare("o (sampled rows)", o.reshape(-1, d)[rows], o_ref)
     compare_lse(lse.reshape(-1)[rows], lse_ref)
+
+
+# ------------------------------------------------------ causal sliding window
+
+def gpu_fwd_window(fa, q, k, v, scale, window):
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    o = Guarded((B, Hq, N, d))
+    lse = Guarded((B, Hq, N))
+    st = fa.fa_fwd_window(dev(q), dev(k), dev(v), o.t, lse.t, B, Hq, Hkv, N, d, scale, window)
+    assert st == 0, fa.fa_status_string(st)
+    return o.result("o"), lse.result("lse")
+
+
+def gpu_bwd_window(fa, q, k, v, dout, o, lse, scale, window, deterministic):
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    dq, dk, dv = Guarded((B, Hq, N, d)), Guarded((B, Hkv, N, d)), Guarded((B, Hkv, N, d))
+    need = fa.fa_bwd_workspace_bytes(B, Hq, Hkv, N, d, deterministic)
+    ws = torch.full((need,), 255, dtype=torch.uint8, device="cuda")
+    st = fa.fa_bwd_window(dev(q), dev(k), dev(v), torch.from_numpy(o).cuda(),
+                          torch.from_numpy(lse).cuda(), dev(dout), dq.t, dk.t, dv.t, B, Hq, Hkv,
+                          N, d, scale, window, deterministic, ws, need)
+    assert st == 0, fa.fa_status_string(st)
+    return dq.result("dq"), dk.result("dk"), dv.result("dv")
+
+
+# Windows of one key, under one key tile, across tile edges, over the 256-row
+# query tile, and wider than N (plain causal).
+@pytest.mark.parametrize("N,d,window", [(n, d, w) for n in (3, 64, 129, 300, 600) for d in (64, 128)
+                                        for w in (1, 17, 64, 200, 1000)])
+def test_fwd_window_small(fa, N, d, window):
+    B, Hq, Hkv = sweep_shape(N)
+    note(f"fwd window B={B} Hq={Hq} Hkv={Hkv} N={N} d={d} window={window}")
+    q, k, v = random_bf16((B, Hq, N, d), N + 7), random_bf16((B, Hkv, N, d), N + 8), random_bf16((B, Hkv, N, d), N + 9)
+    scale = 1 / math.sqrt(d)
+    o, lse = gpu_fwd_window(fa, q, k, v, scale, window)
+    o_ref, lse_ref = oracle.fwd(q, k, v, scale, True, window=window)
+    compare("o", o, o_ref)
+    compare_lse(lse, lse_ref)
+
+
+@pytest.mark.parametrize("deterministic", [0, 1])
+@pytest.mark.parametrize("N,d,window", [(n, d, w) for n in (64, 300, 600) for d in (64, 128)
+                                        for w in (1, 40, 256)])
+def test_bwd_window_small(fa, N, d, window, deterministic):
+    B, Hq, Hkv = sweep_shape(N)
+    note(f"bwd window B={B} Hq={Hq} Hkv={Hkv} N={N} d={d} window={window} det={deterministic}")
+    q, k, v = random_bf16((B, Hq, N, d), N + 17), random_bf16((B, Hkv, N, d), N + 18), random_bf16((B, Hkv, N, d), N + 19)
+    dout = random_bf16((B, Hq, N, d), N + 20)
+    scale = 1 / math.sqrt(d)
+    o, lse = gpu_fwd_window(fa, q, k, v, scale, window)
+    dq, dk, dv = gpu_bwd_window(fa, q, k, v, dout, o, lse, scale, window, deterministic)
+    r = oracle.bwd(q, k, v, dout, scale, True, window=window)
+    bar = MEAN_ABS_FEW_TERMS if window < 64 else MEAN_ABS
+    compare("dq", dq, r["dq"], bar)
+    compare("dk", dk, r["dk"], bar)
+    compare("dv", dv, r["dv"], bar)
+
+
+@pytest.mark.parametrize("deterministic", [0, 1])
+def test_window_long_context_gqa(fa, deterministic):
+    """N = 8192, GQA 2:1, window 1024: forward on sampled rows, backward on
+    every element of two KV groups (the oracle's cost grows with N * window)."""
+    B, Hq, Hkv, N, d, W = 1, 4, 2, 8192, 128, 1024
+    note(f"window long context det={deterministic}")
+    w = replace(WORKLOADS["fwd_n4096"], B=B, Hq=Hq, Hkv=Hkv, N=N, causal=True, seed=48,
+                backward=True)
+    x = make_inputs(w)
+    o, lse = gpu_fwd_window(fa, x["q"], x["k"], x["v"], w.scale, W)
+    rows = sampled_rows(w, 256, w.seed)
+    o_ref, lse_ref = oracle.fwd_rows(x["q"], x["k"], x["v"], w.scale, True, rows, window=W)
+    compare("o (sampled rows)", o.reshape(-1, d)[rows], o_ref)
+    compare_lse(lse.reshape(-1)[rows], lse_ref)
+    dq, dk, dv = gpu_bwd_window(fa, x["q"], x["k"], x["v"], x["dout"], o, lse, w.scale, W,
+                                deterministic)
+    r = oracle.bwd_groups(x["q"], x["k"], x["v"], x["dout"], w.scale, True, [0, 1], window=W)
+    compare("dq", dq.reshape(2, 2, N, d), r["dq"])
+    compare("dk", dk.reshape(2, N, d), r["dk"])
+    compare("dv", dv.reshape(2, N, d), r["dv"])
