@@ -503,3 +503,16 @@ def test_window_long_context_gqa(fa, deterministic):
     compare("dq", dq.reshape(2, 2, N, d), r["dq"])
     compare("dk", dk.reshape(2, N, d), r["dk"])
     compare("dv", dv.reshape(2, N, d), r["dv"])
+
+
+def test_attention_fwd_wrapper_splits(fa):
+    """The convenience wrapper's split-KV path (workspace allocated by the
+    wrapper) against the oracle."""
+    B, Hq, Hkv, N, d = 1, 2, 1, 700, 64
+    q, k, v = random_bf16((B, Hq, N, d), 71), random_bf16((B, Hkv, N, d), 72), random_bf16((B, Hkv, N, d), 73)
+    for causal in (False, True):
+        o, lse = fa.attention_fwd(dev(q), dev(k), dev(v), scale=0.2, causal=causal, num_splits=5)
+        torch.cuda.synchronize()
+        o_ref, lse_ref = oracle.fwd(q, k, v, 0.2, causal)
+        compare("o", o.cpu().numpy(), o_ref)
+        compare_lse(lse.cpu().numpy(), lse_ref)
