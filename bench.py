@@ -35,29 +35,24 @@ PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
 
-def kernel_source_sha256():
-    """Hash of the kernel sources, to tell whether stored counters still apply."""
+def library_sha256():
+    """Hash of the libfa.so this process loads, to tell whether the stored
+    counters were taken with the same compiled kernels."""
     import hashlib
-    h = hashlib.sha256()
-    d = os.path.join(ROOT, "exact_tiled_attention_27_amd", "csrc")
-    for f in sorted(os.listdir(d)):
-        if f.endswith((".hip", ".hpp", ".cpp")):
-            h.update(f.encode())
-            with open(os.path.join(d, f), "rb") as fh:
-                h.update(fh.read())
-    return h.hexdigest()
+    with open(os.path.join(ROOT, "exact_tiled_attention_27_amd", "libfa.so"), "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()
 
 
 def measured_traffic(kernels, workload):
     """HBM bytes per launch (read + write) of `kernels` from the rocprofv3
     FETCH_SIZE / WRITE_SIZE passes stored in profiles/, or None when they were
-    taken on another workload or before the kernel sources last changed."""
+    taken on another workload or with another build of the library."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("workload") != workload or t.get("source_sha256") != kernel_source_sha256():
+    if t.get("workload") != workload or t.get("library_sha256") != library_sha256():
         return None
     try:
         return sum(t["kernels"][k]["read_bytes"] + t["kernels"][k]["write_bytes"] for k in kernels)

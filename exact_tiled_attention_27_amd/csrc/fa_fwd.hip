@@ -47,22 +47,22 @@ struct FwdShape {
     static constexpr int KVSTEPS = BN / 16;  // k-steps of O^T += V^T P^T
     using KTile = DmaTile<BN, D, THREADS>;  // row-major K (and V) tile
     // LDS: two K slots and two V slots (tile t uses slot t % 2 of each), four
-    // separate arrays.  A read from one array after a copy into another needs
-    // no wait for that copy; the compiler only proves that for distinct
-    // arrays, and would otherwise drain every copy just issued before the
-    // first transposing read of the step.
+    // separate arrays addressed with compile-time slot numbers.  The tile
+    // copies are inline-asm buffer loads the compiler does not track; the
+    // step barrier waits for them.
     static constexpr int TILE_BYTES = KTile::BYTES;
 };
 
 // Software pipeline of one wave (tile t, with S_t already computed, masked,
 // and its row maximum folded into the reference m):
 //   1. barrier: V_t and K_{t+1} are in LDS, every wave is done with K_t and
-//      V_{t-1}; start the copies of V_{t+1} and K_{t+2} into the freed slots;
+//      V_{t-1}; start the copies of V_{t+1} and K_{t+2} into the freed slots
+//      (in mask-free steps, one copy per k-step between the score products);
 //   2. one straight-line block: S_{t+1} = K_{t+1} Q^T on the matrix cores,
 //      P_t = exp2(S_t * c - m) with its row sum and bf16 packing on the vector
 //      ALUs, then O^T += V_t^T P_t^T;
-//   3. mask S_{t+1} (diagonal or tail tiles only), take its row maximum and,
-//      rarely, rescale O and l.
+//   3. mask S_{t+1} (diagonal, tail and sliding-window edge tiles only), take
+//      its row maximum and, rarely, rescale O and l.
 // The exponentials of one tile thus overlap the score products of the next
 // (the overlap the FlashAttention-4 guide obtains with separate softmax and
 // MMA warps), inside each wave and without extra barriers.
@@ -76,6 +76,8 @@ struct FwdShape {
 // chunk's normalised partial O and partial LSE to opart / lpart
 // ([n_splits][B * Hq][N] rows) for fwd_merge_kernel.  A row with no valid key
 // in its chunk (causal) gets O = 0 and LSE = -inf there.
+// window (causal only): query i sees keys i - window + 1 .. i; tiles before
+// the workgroup's first such key are skipped (kNoWindow when there is none).
 template <int D, bool CAUSAL, int POLY, bool SPLIT>
 __global__ __launch_bounds__(512, FA_FWD_MIN_WAVES) void fwd_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,

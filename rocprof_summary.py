@@ -12,8 +12,9 @@
       conflicts, transcendental share) from --pmc passes
 
 Only the attention kernels (names in namespace fa::) and the calibration copy
-are reported.  The JSON written by `traffic` carries a hash of the kernel
-sources; bench.py reports the stored traffic only while that hash matches.
+are reported.  The JSON written by `traffic` carries a hash of the built
+library (libfa.so); bench.py reports the stored traffic only while that hash
+matches the library it loads.
 """
 import argparse
 import collections
@@ -84,16 +85,13 @@ def cmd_stats(a):
     write(a.out, out)
 
 
-def source_sha256():
+def library_sha256():
+    """Hash of the built libfa.so the counters were taken with.  The build is
+    deterministic, and comments do not reach the binary, so the stored
+    traffic stays valid exactly as long as the compiled kernels do."""
     import hashlib
-    h = hashlib.sha256()
-    d = os.path.join(ROOT, "exact_tiled_attention_27_amd", "csrc")
-    for f in sorted(os.listdir(d)):
-        if f.endswith((".hip", ".hpp", ".cpp")):
-            h.update(f.encode())
-            with open(os.path.join(d, f), "rb") as fh:
-                h.update(fh.read())
-    return h.hexdigest()
+    with open(os.path.join(ROOT, "exact_tiled_attention_27_amd", "libfa.so"), "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()
 
 
 def cmd_traffic(a):
@@ -111,7 +109,7 @@ def cmd_traffic(a):
             continue
         res[k] = {"read_bytes": mean(fk) * 1024 * ff, "write_bytes": mean(wk) * 1024 * wf,
                   "launches": min(len(fk), len(wk))}
-    js = {"workload": a.workload, "source_sha256": source_sha256(),
+    js = {"workload": a.workload, "library_sha256": library_sha256(),
           "calibration": {"kernel": COPY_KERNEL, "bytes_read_and_written": COPY_BYTES,
                           "fetch_size_kib": f_copy, "write_size_kib": w_copy,
                           "fetch_factor": ff, "write_factor": wf},
