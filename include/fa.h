@@ -36,12 +36,13 @@
  *     without any host synchronisation.  Argument errors return before any
  *     work is enqueued.  A launch failure returns FA_ERR_HIP; faults during
  *     execution surface at the caller's next synchronisation.
- *   - The environment variable FA_EXP2_POLY, read on every fa_fwd call,
+ *   - The environment variable FA_EXP2_POLY, read on every forward call
+ *     (fa_fwd, fa_fwd_window, fa_fwd_splitkv),
  *     moves forward exponentials from the transcendental unit to a cubic
  *     polynomial on the FMA units (page "FlashAttention-4", Key Contributions
  *     item 2): "1" all of them, "4" one in four; unset or any other value,
  *     none (the default, and the faster choice on this chip).
- *   - The environment variable FA_RESCALE_TAU, read on every fa_fwd call,
+ *   - The environment variable FA_RESCALE_TAU, read on every forward call,
  *     replaces the rescale threshold 8 by another finite value >= 0 (0:
  *     rescale whenever the running maximum grows); the result is the same
  *     up to rounding.
