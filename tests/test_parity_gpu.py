@@ -516,3 +516,50 @@ def test_attention_fwd_wrapper_splits(fa):
         o_ref, lse_ref = oracle.fwd(q, k, v, 0.2, causal)
         compare("o", o.cpu().numpy(), o_ref)
         compare_lse(lse.cpu().numpy(), lse_ref)
+
+
+@pytest.mark.parametrize("jump", [8.125, 40.0, -30.0])
+@pytest.mark.parametrize("mode", ["window", "split"])
+def test_planted_max_jump_window_and_split(fa, jump, mode):
+    """The planted jump at key 160 through the sliding-window forward (window
+    100: rows 160-259 see the jump inside their band, whose first tiles hold
+    no valid key for many rows) and through the split-KV forward (3 chunks:
+    the jump lands in a chunk of its own for the later rows)."""
+    B, H, N, d = 1, 2, 320, 64
+    note(f"planted jump {jump} via {mode}")
+    rng = np.random.default_rng(9)
+    qf = np.zeros((B, H, N, d), np.float32)
+    qf[..., 0] = 1.0
+    kf = rng.uniform(-0.25, 0.25, size=(B, H, N, d)).astype(np.float32)
+    kf[..., 0] = 0.0
+    kf[..., 160:, 0] = jump
+    q, k = f32_to_bf16_bits(qf), f32_to_bf16_bits(kf)
+    v = random_bf16((B, H, N, d), 10)
+    scale = float(np.float32(math.log(2.0)))
+    if mode == "window":
+        o, lse = gpu_fwd_window(fa, q, k, v, scale, 100)
+        o_ref, lse_ref = oracle.fwd(q, k, v, scale, True, window=100)
+    else:
+        o, lse = gpu_fwd_split(fa, q, k, v, scale, True, 3)
+        o_ref, lse_ref = oracle.fwd(q, k, v, scale, True)
+    compare("o", o, o_ref)
+    compare_lse(lse, lse_ref)
+
+
+@pytest.mark.parametrize("env,val", [("FA_EXP2_POLY", "1"), ("FA_EXP2_POLY", "4"),
+                                     ("FA_RESCALE_TAU", "0")])
+def test_window_and_split_under_switches(fa, monkeypatch, env, val):
+    """The forward switches apply to the window and split-KV entry points too."""
+    monkeypatch.setenv(env, val)
+    B, Hq, Hkv, N, d = 2, 4, 2, 300, 128
+    note(f"window/split with {env}={val}")
+    q, k, v = random_bf16((B, Hq, N, d), 81), random_bf16((B, Hkv, N, d), 82), random_bf16((B, Hkv, N, d), 83)
+    scale = 1 / math.sqrt(d)
+    o, lse = gpu_fwd_window(fa, q, k, v, scale, 70)
+    o_ref, lse_ref = oracle.fwd(q, k, v, scale, True, window=70)
+    compare("o window", o, o_ref)
+    compare_lse(lse, lse_ref)
+    o, lse = gpu_fwd_split(fa, q, k, v, scale, False, 3)
+    o_ref, lse_ref = oracle.fwd(q, k, v, scale, False)
+    compare("o split", o, o_ref)
+    compare_lse(lse, lse_ref)
