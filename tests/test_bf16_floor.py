@@ -1,0 +1,33 @@
+"""The bf16-operand floor emulation (tests/bf16_floor.py), pinned on the CPU:
+without rounding it reproduces the oracle's gradients, and on the causal GQA
+input of the smoke check the rounding of P alone already moves dV by more than
+the 1e-2 bar (the case the floor-aware bar exists for)."""
+import math
+
+import numpy as np
+
+import oracle
+from bf16_floor import backward_bars, backward_emulation
+from synth import random_bf16
+
+
+def test_unrounded_emulation_is_the_oracle():
+    B, Hq, Hkv, N, d = 1, 4, 2, 37, 32
+    q, k, v = random_bf16((B, Hq, N, d), 51), random_bf16((B, Hkv, N, d), 52), random_bf16((B, Hkv, N, d), 53)
+    do = random_bf16((B, Hq, N, d), 54)
+    for causal, window in ((False, 0), (True, 0), (True, 9)):
+        ref = oracle.bwd(q, k, v, do, 0.2, causal, window=window)
+        emu = backward_emulation(q, k, v, do, 0.2, causal, window, round_operands=False)
+        for name in ("dq", "dk", "dv"):
+            np.testing.assert_allclose(emu[name], ref[name], rtol=1e-10, atol=1e-12)
+
+
+def test_floor_exceeds_bar_on_the_smoke_input():
+    B, Hq, Hkv, N, d = 1, 4, 2, 200, 128
+    scale = 1.0 / math.sqrt(d)
+    q, k, v = random_bf16((B, Hq, N, d), 1), random_bf16((B, Hkv, N, d), 2), random_bf16((B, Hkv, N, d), 3)
+    do = random_bf16((B, Hq, N, d), 4)
+    ref = oracle.bwd(q, k, v, do, scale, True)
+    bars, floors = backward_bars(q, k, v, do, scale, True, ref)
+    assert floors["dv"] > 1e-2 and bars["dv"] == 1.25 * floors["dv"]
+    assert floors["dk"] < 1e-2 and bars["dk"] == 1e-2
