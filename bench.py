@@ -122,7 +122,7 @@ def per_config(fa, reps, dev, stream):
             dq = torch.empty((B, Hq, N, d), dtype=torch.float32, device=dev)
             dk = torch.empty((B, Hkv, N, d), dtype=torch.float32, device=dev)
             dv = torch.empty_like(dk)
-            for det in (1, 0):
+            for det in (fa.BWD_SEPARATE, fa.BWD_ATOMIC, fa.BWD_ORDERED):
                 wsb = fa.fa_bwd_workspace_bytes(B, Hq, Hkv, N, d, det)
                 ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
 
@@ -132,7 +132,8 @@ def per_config(fa, reps, dev, stream):
                     if st:
                         raise fa.FAError(st, "fa_bwd")
 
-                name = "fa_bwd deterministic" if det else "fa_bwd atomic"
+                name = {fa.BWD_SEPARATE: "fa_bwd deterministic", fa.BWD_ATOMIC: "fa_bwd atomic",
+                        fa.BWD_ORDERED: "fa_bwd ordered"}[det]
                 row["calls"].append(entry(name, w.bwd_flops(), time_launches(bwd, reps, stream)))
         torch.cuda.synchronize()
         return row

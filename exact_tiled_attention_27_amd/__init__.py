@@ -16,11 +16,16 @@ import os
 
 __all__ = ["fa_fwd", "fa_fwd_window", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_bytes",
            "fa_bwd", "fa_bwd_window", "fa_bwd_workspace_bytes", "fa_status_string", "FAError",
-           "attention_fwd", "attention_bwd", "LIB_PATH", "STATUS", "MAX_SPLITS"]
+           "attention_fwd", "attention_bwd", "LIB_PATH", "STATUS", "MAX_SPLITS",
+           "BWD_ATOMIC", "BWD_SEPARATE", "BWD_ORDERED"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
 MAX_SPLITS = 64  # FA_MAX_SPLITS
+
+# dQ modes of fa_bwd's `deterministic` argument (FA_BWD_ATOMIC, FA_BWD_SEPARATE,
+# FA_BWD_ORDERED); False and True select the first two.
+BWD_ATOMIC, BWD_SEPARATE, BWD_ORDERED = 0, 1, 2
 
 STATUS = {0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_UNSUPPORTED",
           4: "FA_ERR_ALIGN", 5: "FA_ERR_WORKSPACE", 6: "FA_ERR_HIP"}
@@ -105,7 +110,7 @@ def fa_bwd_window(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, N, d, scale, wi
     """C ABI fa_bwd_window (causal sliding window).  Status out."""
     return _lib.fa_bwd_window(_addr(q), _addr(k), _addr(v), _addr(o), _addr(lse), _addr(dout),
                               _addr(dq), _addr(dk), _addr(dv), B, Hq, Hkv, N, d, float(scale),
-                              int(window), int(bool(deterministic)), _addr(workspace),
+                              int(window), int(deterministic), _addr(workspace),
                               int(workspace_bytes), _stream(stream, q, dq))
 
 
@@ -122,7 +127,7 @@ def fa_fwd_splitkv_workspace_bytes(B, Hq, Hkv, N, d, num_splits) -> int:
 
 
 def fa_bwd_workspace_bytes(B, Hq, Hkv, N, d, deterministic) -> int:
-    return int(_lib.fa_bwd_workspace_bytes(B, Hq, Hkv, N, d, int(bool(deterministic))))
+    return int(_lib.fa_bwd_workspace_bytes(B, Hq, Hkv, N, d, int(deterministic)))
 
 
 def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, N, d, scale, causal, deterministic,
@@ -130,7 +135,7 @@ def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, N, d, scale, causal, d
     """C ABI fa_bwd.  Tensors (or integer device addresses) in, status out."""
     return _lib.fa_bwd(_addr(q), _addr(k), _addr(v), _addr(o), _addr(lse), _addr(dout),
                        _addr(dq), _addr(dk), _addr(dv), B, Hq, Hkv, N, d, float(scale),
-                       int(bool(causal)), int(bool(deterministic)), _addr(workspace),
+                       int(bool(causal)), int(deterministic), _addr(workspace),
                        int(workspace_bytes), _stream(stream, q, dq))
 
 
@@ -175,7 +180,8 @@ def attention_fwd(q, k, v, scale=None, causal=False, o=None, lse=None, stream=No
 
 def attention_bwd(q, k, v, o, lse, dout, scale=None, causal=False, deterministic=False,
                   dq=None, dk=None, dv=None, workspace=None, stream=None):
-    """Backward attention on device tensors.  Returns (dq, dk, dv) fp32."""
+    """Backward attention on device tensors.  Returns (dq, dk, dv) fp32.
+    deterministic: BWD_ATOMIC (False), BWD_SEPARATE (True) or BWD_ORDERED."""
     import torch
     _check_inputs(q, k, v, dout)
     B, Hq, Hkv, N, d = _dims(q, k)

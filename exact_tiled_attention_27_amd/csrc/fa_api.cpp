@@ -80,7 +80,8 @@ int fwd_impl(const void *q, const void *k, const void *v, float *o, float *lse, 
     return hip_status(fa::launch_fwd(a));
 }
 
-// fa_bwd and fa_bwd_window: window as in fwd_impl.
+// fa_bwd and fa_bwd_window: window as in fwd_impl; deterministic is the dQ
+// mode (FA_BWD_ATOMIC, FA_BWD_SEPARATE or FA_BWD_ORDERED).
 int bwd_impl(const void *q, const void *k, const void *v, const float *o, const float *lse,
              const void *dout, float *dq, float *dk, float *dv, int B, int Hq, int Hkv, int N,
              int d, float scale, int causal, int window, int deterministic, void *workspace,
@@ -89,6 +90,7 @@ int bwd_impl(const void *q, const void *k, const void *v, const float *o, const 
     if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL;
     int st = check_common(B, Hq, Hkv, N, d, scale);
     if (st != FA_OK) return st;
+    if (deterministic < FA_BWD_ATOMIC || deterministic > FA_BWD_ORDERED) return FA_ERR_SHAPE;
     const void *ptrs[] = {q, k, v, o, lse, dout, dq, dk, dv};
     for (const void *p : ptrs)
         if (!aligned16(p)) return FA_ERR_ALIGN;
@@ -99,8 +101,12 @@ int bwd_impl(const void *q, const void *k, const void *v, const float *o, const 
     float *delta = reinterpret_cast<float *>(workspace);
     float *lse2 = reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) +
                                             round256(rows * sizeof(float)));
-    fa::BwdArgs a{q, k, v, dout, o, lse, dq, dk, dv, delta, lse2, B, Hq, Hkv, N, d, scale,
-                  causal != 0, deterministic != 0, window < N ? window : 0,
+    int *sync = deterministic == FA_BWD_ORDERED
+                    ? reinterpret_cast<int *>(reinterpret_cast<char *>(workspace) +
+                                              2 * round256(rows * sizeof(float)))
+                    : nullptr;
+    fa::BwdArgs a{q, k, v, dout, o, lse, dq, dk, dv, delta, lse2, sync, B, Hq, Hkv, N, d, scale,
+                  causal != 0, deterministic, window < N ? window : 0,
                   reinterpret_cast<hipStream_t>(stream)};
     return hip_status(fa::launch_bwd(a));
 }
@@ -114,7 +120,7 @@ const char *fa_status_string(int status)
     switch (status) {
     case FA_OK: return "FA_OK";
     case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
-    case FA_ERR_SHAPE: return "FA_ERR_SHAPE: invalid B/Hq/Hkv/N or scale";
+    case FA_ERR_SHAPE: return "FA_ERR_SHAPE: invalid B/Hq/Hkv/N, scale, window, split count or dQ mode";
     case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: head dimension must be 64 or 128";
     case FA_ERR_ALIGN: return "FA_ERR_ALIGN: pointers must be 16-byte aligned";
     case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing or too small";
@@ -176,9 +182,11 @@ int fa_fwd_splitkv(const void *q, const void *k, const void *v, float *o, float 
 
 size_t fa_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d, int deterministic)
 {
-    (void)deterministic;
     if (check_common(B, Hq, Hkv, N, d, 1.0f) != FA_OK) return 0;
-    return 2 * round256(workspace_rows(B, Hq, N) * sizeof(float));
+    if (deterministic < FA_BWD_ATOMIC || deterministic > FA_BWD_ORDERED) return 0;
+    const size_t rows_part = 2 * round256(workspace_rows(B, Hq, N) * sizeof(float));
+    if (deterministic != FA_BWD_ORDERED) return rows_part;
+    return rows_part + round256(fa::bwd_sync_words(B * Hq, N) * sizeof(int));
 }
 
 int fa_bwd(const void *q, const void *k, const void *v, const float *o, const float *lse,

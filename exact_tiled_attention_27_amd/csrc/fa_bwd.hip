@@ -56,8 +56,13 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t *__restrict
                                                       float *__restrict__ delta,
                                                       float *__restrict__ lse2,
                                                       float *__restrict__ dq, int BH, int N,
-                                                      int zero_dq)
+                                                      int zero_dq, int *__restrict__ sync,
+                                                      size_t n_sync)
 {
+    // Ordered mode: clear the ticket, timeout and turn counters (the grid
+    // has at least 8 threads per padded row, more than n_sync).
+    const size_t gid = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (sync && gid < n_sync) sync[gid] = 0;
     constexpr int TPR = D / 8;  // threads per row, 8 elements each
     const int NP = pad_rows(N);
     const size_t prow = (size_t)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;  // padded row
@@ -105,10 +110,26 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t *__restrict
 // the exponent / elementwise phases of the other.  The Q, dO and row stages
 // live in separate LDS arrays per slot (step st uses slot st % 2), so reads of
 // one slot never wait for the copies into the other.
-// ATOMIC_DQ (the atomic-dQ mode) adds dQ += dS K: wave B stores dS^T to LDS
-// after the products of step st, and the four B waves add that step's dQ
-// tiles with fp32 atomics at the start of step st + 1 (before the mid-step
-// barrier, after which dS^T is overwritten).
+// DQ selects what the kernel does for dQ: kDqNone (the deterministic mode's
+// separate pass computes it), kDqAtomic or kDqOrdered.  Both atomic modes add
+// dQ += dS K: wave B stores dS^T to LDS after the products of step st, and the
+// four B waves add that step's dQ tiles with fp32 atomics at the start of step
+// st + 1 (before the mid-step barrier, after which dS^T is overwritten).
+// kDqOrdered makes the adds into each 64-row dQ tile happen in ascending
+// key-block order, so the fp32 sums, and dQ's bits, are the same on every run:
+//   - Each workgroup draws a ticket from a counter at its start and takes
+//     the work item of that ticket (key block major).  A workgroup only ever
+//     waits for a smaller ticket, i.e. for a workgroup that has already
+//     started, so the waits cannot deadlock whatever order the hardware
+//     dispatches workgroups in.
+//   - Per (query head, 64-row tile, B wave) a turn counter in the workspace
+//     counts the key blocks that have added; key block kt adds when the
+//     counter equals its rank among the tile's key blocks, and raises it one
+//     step later, once the end-of-step wait has seen its atomics complete.
+//   - Every wait is bounded (kTurnTimeout ticks of the wall clock).  A wait
+//     that times out is counted in the workspace, makes every later wait of
+//     the launch give up at once, and the adds still happen: dQ is then the
+//     correct sum in an unspecified order, and the kernel always finishes.
 template <int D>
 struct DkdvSplitShape {
     static constexpr int BN = 128;   // keys per workgroup (32 per wave pair)
@@ -122,15 +143,51 @@ struct DkdvSplitShape {
     static constexpr int X_SLICE = 64 * 32 * 4;            // P exchange per slice: 64 lanes x 32 fp32
 };
 
-template <int D, bool CAUSAL, bool ATOMIC_DQ>
+constexpr int kDqNone = 0, kDqAtomic = 1, kDqOrdered = 2;
+
+// Longest wait for a turn: 2 s at the 100 MHz wall clock.
+constexpr long long kTurnTimeout = 200000000LL;
+
+// Waits (the whole wave) until *turn == want, bounded as described above.
+__device__ __forceinline__ void wait_turn(const int *turn, int want, int *sync, int lane)
+{
+    int seen = __builtin_amdgcn_readfirstlane(
+        __hip_atomic_load(turn, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    if (seen != want) {
+        const long long t0 = wall_clock64();
+        while (true) {
+            __builtin_amdgcn_s_sleep(2);
+            seen = __builtin_amdgcn_readfirstlane(
+                __hip_atomic_load(turn, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+            if (seen == want) break;
+            if (__builtin_amdgcn_readfirstlane(__hip_atomic_load(
+                    sync + kSyncTimeouts, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) != 0)
+                break;
+            if (wall_clock64() - t0 > kTurnTimeout) {
+                if (lane == 0)
+                    __hip_atomic_fetch_add(sync + kSyncTimeouts, 1, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+                break;
+            }
+        }
+    }
+    // The dQ adds that follow are issued only once the counter load has
+    // returned (the branch above needs its value); keep the compiler from
+    // moving them above the wait.
+    asm volatile("" ::: "memory");
+}
+
+template <int D, bool CAUSAL, int DQ>
 __global__ __launch_bounds__(512) void bwd_dkdv_split_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, const uint16_t *__restrict__ dout,
     const float *__restrict__ lse2, const float *__restrict__ delta, float *__restrict__ dq,
     float *__restrict__ dk, float *__restrict__ dv, int Hq, int Hkv, int N, int BHkv, int KT,
-    float scale, float scale_log2, int window)
+    float scale, float scale_log2, int window, int *__restrict__ sync)
 {
     using S = DkdvSplitShape<D>;
+    constexpr bool ATOMIC_DQ = DQ != kDqNone;
+    constexpr bool ORDERED = DQ == kDqOrdered;
     // Atomic mode only: the workgroup's K rows (B operand of dQ = dS K) and
     // the step's dS^T [BN keys][BM queries] (A operand, transposing reads).
     __shared__ __attribute__((aligned(16))) char k_lds[ATOMIC_DQ ? S::BN * D * 2 : 16];
@@ -151,7 +208,24 @@ __global__ __launch_bounds__(512) void bwd_dkdv_split_kernel(
     const int g16 = lane >> 4;
 
     int bg, kt;
-    xcd_tile_map(blockIdx.x, BHkv, KT, false, bg, kt);
+    if (ORDERED) {
+        __shared__ int ticket;
+        if (tid == 0)
+            ticket = __hip_atomic_fetch_add(sync + kSyncTicket, 1, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        const int hw = __builtin_amdgcn_readfirstlane(ticket);
+        if (hw >= BHkv * KT) {  // counter not cleared by the preprocess: give up
+            if (tid == 0)
+                __hip_atomic_fetch_add(sync + kSyncTimeouts, 1, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+            return;
+        }
+        kt = hw / BHkv;
+        bg = hw % BHkv;
+    } else {
+        xcd_tile_map(blockIdx.x, BHkv, KT, false, bg, kt);
+    }
     const int b = bg / Hkv, g = bg % Hkv;
     const int grp = Hq / Hkv;
     const int NP = pad_rows(N);
@@ -216,6 +290,30 @@ __global__ __launch_bounds__(512) void bwd_dkdv_split_kernel(
     // whose dS^T the B waves left in dst_lds; the 2 * DBLK tiles of 32 x 32
     // are spread over the four B waves, each tile added with fp32 atomics
     // (lanes 0-31 and 32-63 cover 128 contiguous bytes of a dQ row each).
+    // Ordered mode: this B wave's turn counter for step st's dQ tile, and the
+    // rank of key block kt among the key blocks that add into that tile
+    // (those whose query range, first_qt .. n_qt - 1 above, holds it).
+    auto turn_of = [&](int st) {
+        const int hq = g * grp + st / steps_per_head;
+        const int qt = first_qt + st % steps_per_head;
+        return sync + kSyncHead + (((size_t)b * Hq + hq) * (NP / S::BM) + qt) * 4 + slice;
+    };
+    auto rank_of = [&](int st) {
+        const int qt = first_qt + st % steps_per_head;
+        const int num = S::BM * qt - (S::BN - 2) - window;
+        return kt - (CAUSAL && num > 0 ? (num + S::BN - 1) / S::BN : 0);
+    };
+    // The dQ adds and the turn counters are device-scope atomics, performed
+    // at the device's coherence point, not in an XCD's L2: once the wave's
+    // adds have completed (vmcnt(0)), raising the counter orders them before
+    // every add issued after a wave has seen the raised value.  No L2
+    // write-back or invalidate is needed for that (an agent-scope
+    // release/acquire fence pair, which does both, made this mode five times
+    // slower).
+    auto release = [&](int st) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        if (lane == 0) __hip_atomic_fetch_add(turn_of(st), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
     auto dq_update = [&](int st) {
         const int hq = g * grp + st / steps_per_head;
         const int qs = (first_qt + st % steps_per_head) * S::BM;
@@ -237,6 +335,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_split_kernel(
                            join_bf16x8(lds_read_tr16(bl, b0), lds_read_tr16(bl, b1)), c);
             }
             float *dqt = dqh + (size_t)(qs + 32 * qb + 4 * h) * D + 32 * db + col;
+            if (ORDERED && tt == slice) wait_turn(turn_of(st), rank_of(st), sync, lane);
             if (qs + S::BM <= N) {
 #pragma unroll
                 for (int r = 0; r < 16; r++)
@@ -256,8 +355,12 @@ __global__ __launch_bounds__(512) void bwd_dkdv_split_kernel(
         const char *ql = P ? q_lds1 : q_lds0;
         const char *dol = P ? do_lds1 : do_lds0;
         const char *rows = P ? rows1 : rows0;
+        // Ordered mode: step st - 2's adds completed at the last end-of-step
+        // wait; publish them before this step's copies are in flight (the
+        // release waits for every outstanding memory operation of the wave).
+        if (ORDERED && !wave_a && st > 1) release(st - 2);
         if (st + 1 < n_steps) issue(st + 1, std::integral_constant<int, 1 - P>{});
-        // Atomic mode: the B waves add the previous step's dS K into dQ first
+        // Atomic modes: the B waves add the previous step's dS K into dQ first
         // (no score registers live yet), while the A waves start on S.
         if (ATOMIC_DQ && !wave_a && st > 0) dq_update(st - 1);
 
@@ -388,7 +491,11 @@ __global__ __launch_bounds__(512) void bwd_dkdv_split_kernel(
         step(Slot1{}, st + 1);
     }
     if (st < n_steps) step(Slot0{}, st);
-    if (ATOMIC_DQ && !wave_a && n_steps > 0) dq_update(n_steps - 1);
+    if (ATOMIC_DQ && !wave_a && n_steps > 0) {
+        if (ORDERED && n_steps > 1) release(n_steps - 2);
+        dq_update(n_steps - 1);
+        if (ORDERED) release(n_steps - 1);
+    }
 
     if (key < N) {
         float *out = (wave_a ? dv : dk) + (((size_t)b * Hkv + g) * N + key) * D;
@@ -624,7 +731,8 @@ static hipError_t launch_bwd_t(const BwdArgs &a)
         const unsigned grid = (unsigned)((rows + RPB - 1) / RPB);
         hipLaunchKernelGGL(bwd_pre_kernel<D>, dim3(grid), dim3(256), 0, a.stream,
                            (const uint16_t *)a.dout, a.o, a.lse, a.delta, a.lse2, a.dq, BH, a.N,
-                           a.deterministic ? 0 : 1);
+                           a.mode == kBwdSeparate ? 0 : 1, a.sync,
+                           a.mode == kBwdOrdered ? bwd_sync_words(BH, a.N) : (size_t)0);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -632,17 +740,19 @@ static hipError_t launch_bwd_t(const BwdArgs &a)
         using S = DkdvSplitShape<D>;
         const int KT = (a.N + S::BN - 1) / S::BN;
         const int BHkv = a.B * a.Hkv;
-        auto kern = a.deterministic ? bwd_dkdv_split_kernel<D, CAUSAL, false>
-                                    : bwd_dkdv_split_kernel<D, CAUSAL, true>;
+        auto kern = a.mode == kBwdSeparate  ? bwd_dkdv_split_kernel<D, CAUSAL, kDqNone>
+                    : a.mode == kBwdOrdered ? bwd_dkdv_split_kernel<D, CAUSAL, kDqOrdered>
+                                            : bwd_dkdv_split_kernel<D, CAUSAL, kDqAtomic>;
         hipLaunchKernelGGL(kern, dim3(BHkv * KT), dim3(S::THREADS), 0, a.stream,
                            (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v,
                            (const uint16_t *)a.dout, a.lse2, a.delta, a.dq, a.dk, a.dv, a.Hq,
                            a.Hkv, a.N, BHkv, KT, a.scale, scale_log2,
-                           a.window > 0 ? a.window : kNoWindow);
+                           a.window > 0 ? a.window : kNoWindow,
+                           a.mode == kBwdOrdered ? a.sync : nullptr);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    if (a.deterministic) {
+    if (a.mode == kBwdSeparate) {
         using S = DqShape<D>;
         const int QT = (a.N + S::BM - 1) / S::BM;
         auto kern = bwd_dq_kernel<D, CAUSAL>;

@@ -21,15 +21,27 @@ struct FwdArgs {
     hipStream_t stream;
 };
 
+// How the backward sums dQ: fp32 atomics from the dK/dV kernel; a separate
+// pass that owns each dQ row; or the dK/dV kernel's atomics in a fixed order.
+constexpr int kBwdAtomic = 0, kBwdSeparate = 1, kBwdOrdered = 2;
+
+// Ordered mode's int32 workspace block: the ticket counter, the count of
+// timed-out waits, then (from word kSyncHead on) the turn counters, four per
+// (batch, query head, 64-row tile of N rounded up to 64).
+constexpr int kSyncTicket = 0, kSyncTimeouts = 1, kSyncHead = 64;
+inline size_t bwd_sync_words(int BH, int N) { return kSyncHead + (size_t)BH * (((N + 63) & ~63) / 16); }
+
 struct BwdArgs {
     const void *q, *k, *v, *dout;
     const float *o, *lse;
     float *dq, *dk, *dv;
     float *delta;  // workspace: D_i = sum_c dO_ic O_ic, [B, Hq, N]
     float *lse2;   // workspace: LSE_i * log2(e), [B, Hq, N]
+    int *sync;     // workspace, ordered mode only: ticket, timeouts, turn counters
     int B, Hq, Hkv, N, d;
     float scale;
-    bool causal, deterministic;
+    bool causal;
+    int mode;      // kBwdAtomic, kBwdSeparate or kBwdOrdered
     int window;    // causal sliding window in keys (0: none)
     hipStream_t stream;
 };

@@ -12,10 +12,10 @@
  *   log2(256) = 8 in the base-2 exponent domain (page "FlashAttention-4",
  *   section "Key Contributions", item 2).
  *   Backward: dQ, dK, dV of the same function, with P recomputed from the
- *   saved log-sum-exp; dQ is summed either with global atomic adds or by a
- *   separate deterministic pass (page "FlashAttention-4", "Key Contributions"
- *   item 3 and "Limitations": the deterministic mode trades speed for
- *   reproducibility).
+ *   saved log-sum-exp; dQ is summed with global atomic adds, by a separate
+ *   deterministic pass, or with the atomic adds put in a fixed order (page
+ *   "FlashAttention-4", "Key Contributions" item 3 and "Limitations": the
+ *   deterministic mode trades speed for reproducibility).
  *
  * Conventions shared by every call:
  *   - Tensors are device pointers to dense row-major arrays laid out
@@ -64,8 +64,9 @@ extern "C" {
 typedef enum {
     FA_OK = 0,
     FA_ERR_NULL = 1,        /* a required pointer is NULL                       */
-    FA_ERR_SHAPE = 2,       /* B/Hq/Hkv/N < 1, Hq % Hkv != 0, N too large, or
-                               scale invalid                                   */
+    FA_ERR_SHAPE = 2,       /* B/Hq/Hkv/N < 1, Hq % Hkv != 0, N too large,
+                               scale invalid, or window, split count or dQ
+                               mode out of range                               */
     FA_ERR_UNSUPPORTED = 3, /* head dimension d not in {64, 128}                */
     FA_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned                 */
     FA_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required       */
@@ -132,10 +133,33 @@ int fa_fwd_splitkv(const void *q, const void *k, const void *v, float *o, float 
 size_t fa_fwd_splitkv_workspace_bytes(int B, int Hq, int Hkv, int N, int d, int num_splits);
 
 /*
- * Bytes of device workspace fa_bwd needs for this shape: the per-row
- * D_i = sum_c dO_ic O_ic and the base-2 LSE, two fp32 arrays [B, Hq, N']
- * with N' = N rounded up to a multiple of 64, each rounded up to 256 bytes.
- * Returns 0 for an invalid shape.
+ * dQ modes of fa_bwd (its `deterministic` argument).
+ *   FA_BWD_ATOMIC:   the dK/dV kernel adds each key block's dS K into dq with
+ *                    fp32 atomic adds in whatever order they land (bits may
+ *                    differ from run to run).
+ *   FA_BWD_SEPARATE: a separate pass owns each dq row and sums it in
+ *                    registers, no atomics (bitwise identical run to run).
+ *   FA_BWD_ORDERED:  the same atomic adds, made in ascending key-block order
+ *                    for every 64-row dq tile through turn counters in the
+ *                    workspace (bitwise identical run to run): the
+ *                    semaphore-ordered reduction the page "FlashAttention-4"
+ *                    names under "Limitations" for its deterministic mode.
+ */
+#define FA_BWD_ATOMIC 0
+#define FA_BWD_SEPARATE 1
+#define FA_BWD_ORDERED 2
+
+/*
+ * Bytes of device workspace fa_bwd needs for this shape and dQ mode: the
+ * per-row D_i = sum_c dO_ic O_ic and the base-2 LSE, two fp32 arrays
+ * [B, Hq, N'] with N' = N rounded up to a multiple of 64, each rounded up to
+ * 256 bytes; FA_BWD_ORDERED adds, right after them (at byte offset
+ * fa_bwd_workspace_bytes(..., FA_BWD_SEPARATE)), a block of int32 counters:
+ * 64 words, then 4 words per (batch, query head, 64 rows of N').  Word 1 of
+ * that block counts the waits for a turn that gave up after about 2 s; it is
+ * 0 after every call whose dq is bitwise reproducible (a non-zero count
+ * leaves dq the correct sum, added in an unspecified order).
+ * Returns 0 for an invalid shape or mode.
  */
 size_t fa_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d, int deterministic);
 
@@ -146,9 +170,9 @@ size_t fa_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d, int determin
  *   dout      bf16 [B, Hq, N, d], the gradient of the loss w.r.t. o (read)
  *   dq        fp32 [B, Hq,  N, d]  (written)
  *   dk, dv    fp32 [B, Hkv, N, d]  (written; summed over each group's heads)
- *   deterministic == 0: dq is accumulated with fp32 global atomic adds
- *     (bits may differ from run to run); != 0: a separate dq pass with no
- *     atomics (bitwise identical run to run on the same device and shape).
+ *   deterministic: the dQ mode, FA_BWD_ATOMIC (0), FA_BWD_SEPARATE (1)
+ *     or FA_BWD_ORDERED (2), above; any other value is FA_ERR_SHAPE.  The
+ *     reproducible modes repeat bit for bit on the same device and shape.
  *   workspace / workspace_bytes: device scratch of at least
  *     fa_bwd_workspace_bytes(...) bytes, 16-byte aligned, owned by the
  *     caller; its contents on entry are ignored.

@@ -184,3 +184,28 @@ def test_single_hip_runtime_in_process():
     out = subprocess.run(["python", "-c", code], capture_output=True, text=True, cwd=ROOT,
                          check=True).stdout.strip()
     assert out == "1"
+
+
+@pytest.mark.parametrize("mode", [-1, 3, 1 << 20])
+def test_bwd_rejects_unknown_dq_mode(mode):
+    assert fa.fa_bwd_workspace_bytes(1, 2, 2, 128, 64, mode) == 0
+    assert bwd(deterministic=mode) == 2
+    bargs = dict(q=A, k=A, v=A, o=A, lse=A, dout=A, dq=A, dk=A, dv=A, B=1, Hq=2, Hkv=2, N=128,
+                 d=64, scale=0.125, window=16, deterministic=mode, workspace=A,
+                 workspace_bytes=1 << 20, stream=0)
+    assert fa.fa_bwd_window(**bargs) == 2
+
+
+def test_bwd_ordered_workspace_bytes():
+    # D and LSE2 ([B*Hq][N'] fp32 each, N' = N rounded up to 64, each to 256 B),
+    # then 64 + 4 * B*Hq*N'/64 int32 counters, to 256 B
+    for B, Hq, Hkv, N, d in ((1, 2, 2, 128, 64), (2, 4, 2, 1000, 128), (1, 1, 1, 1, 64)):
+        npad = (N + 63) // 64 * 64
+        rows = (B * Hq * npad * 4 + 255) // 256 * 256
+        sync = ((64 + 4 * B * Hq * npad // 64) * 4 + 255) // 256 * 256
+        assert fa.fa_bwd_workspace_bytes(B, Hq, Hkv, N, d, fa.BWD_SEPARATE) == 2 * rows
+        assert fa.fa_bwd_workspace_bytes(B, Hq, Hkv, N, d, fa.BWD_ATOMIC) == 2 * rows
+        assert fa.fa_bwd_workspace_bytes(B, Hq, Hkv, N, d, fa.BWD_ORDERED) == 2 * rows + sync
+    need = fa.fa_bwd_workspace_bytes(1, 2, 2, 128, 64, fa.BWD_ORDERED)
+    assert bwd(deterministic=fa.BWD_ORDERED, workspace_bytes=need - 1) == 5
+    assert bwd(deterministic=fa.BWD_ORDERED, workspace_bytes=need, dq=MIS) == 4

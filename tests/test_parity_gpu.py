@@ -89,6 +89,32 @@ def gpu_fwd(fa, q, k, v, scale, causal):
     return o.result("o"), lse.result("lse")
 
 
+def check_ordered_counters(fa, ws, B, Hq, Hkv, N, d, causal, window):
+    """After an ordered-mode call: every workgroup drew one ticket, no wait
+    timed out, and each turn counter equals the number of key blocks (128
+    keys each) that add into its 64-row dQ tile: the blocks whose keys some
+    row of the tile sees (causal: key <= row, row - key < window)."""
+    torch.cuda.synchronize()
+    off = fa.fa_bwd_workspace_bytes(B, Hq, Hkv, N, d, fa.BWD_SEPARATE)
+    words = ws[off:].cpu().numpy().view(np.int32)
+    KT = (N + 127) // 128
+    assert words[0] == B * Hkv * KT, f"tickets {words[0]} != workgroups {B * Hkv * KT}"
+    assert words[1] == 0, f"{words[1]} turn waits timed out"
+    n_tiles = (N + 63) // 64
+    want = np.zeros(n_tiles, dtype=np.int64)
+    W = window if window else 1 << 40
+    for qt in range(n_tiles):
+        r0, r1 = 64 * qt, min(N, 64 * qt + 64) - 1
+        for kt in range(KT):
+            k0, k1 = 128 * kt, min(N, 128 * kt + 128) - 1
+            if not causal:
+                want[qt] += 1
+            elif k0 <= r1 and r0 - k1 < W:  # some (row, key) of the two blocks in the band
+                want[qt] += 1
+    turns = words[64:64 + B * Hq * n_tiles * 4].reshape(B * Hq, n_tiles, 4)
+    assert (turns == want[None, :, None]).all(), "turn counters"
+
+
 def gpu_bwd(fa, q, k, v, dout, o, lse, scale, causal, deterministic):
     B, Hq, N, d = q.shape
     Hkv = k.shape[1]
@@ -99,6 +125,8 @@ def gpu_bwd(fa, q, k, v, dout, o, lse, scale, causal, deterministic):
                    dev(dout), dq.t, dk.t, dv.t, B, Hq, Hkv, N, d, scale, causal, deterministic,
                    ws, need)
     assert st == 0, fa.fa_status_string(st)
+    if deterministic == fa.BWD_ORDERED:
+        check_ordered_counters(fa, ws, B, Hq, Hkv, N, d, causal, 0)
     return dq.result("dq"), dk.result("dk"), dv.result("dv")
 
 
@@ -124,8 +152,11 @@ def test_fwd_small(fa, N, d, causal):
     compare_lse(lse, lse_ref)
 
 
+MODES = [0, 1, 2]  # dQ modes: atomic, separate pass, ordered atomics
+
+
 @pytest.mark.parametrize("N,d,causal", SWEEP)
-@pytest.mark.parametrize("deterministic", [0, 1])
+@pytest.mark.parametrize("deterministic", MODES)
 def test_bwd_small(fa, N, d, causal, deterministic):
     B, Hq, Hkv = sweep_shape(N)
     note(f"bwd small B={B} Hq={Hq} Hkv={Hkv} N={N} d={d} causal={causal} det={deterministic}")
@@ -284,9 +315,9 @@ def test_workload_forward_exp2_polynomial(fa, monkeypatch, share):
 
 def test_workload_backward_both_modes(fa):
     """Full-size causal backward: one key/value group per batch compared element
-    by element with the oracle in both modes; the deterministic mode must repeat
-    bit for bit; exact identities sum_j dK_j = 0 and sum_j dV_j = sum_i dO_i
-    checked on every group."""
+    by element with the oracle in every dQ mode; the two reproducible modes must
+    repeat bit for bit; exact identities sum_j dK_j = 0 and sum_j dV_j =
+    sum_i dO_i checked on every group."""
     w = WORKLOADS["fwdbwd_causal_n8192"]
     note("workload backward fwdbwd_causal_n8192")
     x = make_inputs(w)
@@ -295,7 +326,7 @@ def test_workload_backward_both_modes(fa):
     ref = oracle.bwd_groups(x["q"], x["k"], x["v"], x["dout"], w.scale, w.causal, groups)
     grp = w.Hq // w.Hkv
     results = {}
-    for det in (0, 1):
+    for det in MODES:
         note(f"  deterministic={det}")
         dq, dk, dv = gpu_bwd(fa, x["q"], x["k"], x["v"], x["dout"], o, lse, w.scale, w.causal, det)
         results[det] = (dq, dk, dv)
@@ -313,20 +344,51 @@ def test_workload_backward_both_modes(fa):
         err = np.abs(dv.astype(np.float64).sum(2) - want)
         note(f"  max |sum_j dV_j - sum_i dO_i| = {float(err.max()):.2e}")
         assert (err <= 1e-3 * np.abs(dof).reshape(w.B, w.Hkv, -1, w.d).sum(2) + 1e-2).all()
-    note("  deterministic repeat")
-    again = gpu_bwd(fa, x["q"], x["k"], x["v"], x["dout"], o, lse, w.scale, w.causal, 1)
-    for a, b_ in zip(again, results[1]):
-        assert np.array_equal(a.view(np.uint32), b_.view(np.uint32))
+    for det in (1, 2):
+        note(f"  repeat deterministic={det}")
+        again = gpu_bwd(fa, x["q"], x["k"], x["v"], x["dout"], o, lse, w.scale, w.causal, det)
+        for a, b_ in zip(again, results[det]):
+            assert np.array_equal(a.view(np.uint32), b_.view(np.uint32))
     for a, b_ in zip(results[0], results[1]):
         assert float(np.abs(a - b_).max()) <= 5e-3
+    # dK and dV do not depend on the dQ mode: the same kernel computes them
+    for m in (0, 2):
+        for a, b_ in zip(results[m][1:], results[1][1:]):
+            assert np.array_equal(a.view(np.uint32), b_.view(np.uint32))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_ordered_mode_repeats_across_xcds(fa, causal):
+    """One key/value head (B1 Hq2 Hkv1 N4096 d128): its 32 key blocks run at
+    once on workgroups spread over every XCD and all add into the same dQ
+    tiles, the case where an ordering mistake would show.  Five ordered runs
+    must agree bit for bit; they match the separate-pass mode and the
+    oracle."""
+    B, Hq, Hkv, N, d = 1, 2, 1, 4096, 128
+    note(f"ordered repeats causal={causal}")
+    q, k, v = random_bf16((B, Hq, N, d), 71), random_bf16((B, Hkv, N, d), 72), random_bf16((B, Hkv, N, d), 73)
+    dout = random_bf16((B, Hq, N, d), 74)
+    scale = 1 / math.sqrt(d)
+    o, lse = gpu_fwd(fa, q, k, v, scale, causal)
+    runs = [gpu_bwd(fa, q, k, v, dout, o, lse, scale, causal, 2) for _ in range(5)]
+    for r in runs[1:]:
+        for a, b_ in zip(r, runs[0]):
+            assert np.array_equal(a.view(np.uint32), b_.view(np.uint32))
+    sep = gpu_bwd(fa, q, k, v, dout, o, lse, scale, causal, 1)
+    assert float(np.abs(runs[0][0] - sep[0]).max()) <= 5e-3
+    ref = oracle.bwd_groups(q, k, v, dout, scale, causal, [0])
+    compare("dq", runs[0][0].reshape(1, Hq, N, d), ref["dq"])
+    compare("dk", runs[0][1].reshape(1, N, d), ref["dk"])
+    compare("dv", runs[0][2].reshape(1, N, d), ref["dv"])
 
 
 def test_long_context_gqa_backward(fa):
     """Backward at the long-context GQA shape (B1 Hq32 Hkv8 N32768 d128,
-    causal), both modes.  Element by element against the oracle on the causal
-    tail block (rows and keys N-256 .. N-1 of the first and last KV group:
-    exact there, since a key only receives gradient from later rows); the
-    exact identities on every group; deterministic mode repeats bit for bit."""
+    causal), every dQ mode.  Element by element against the oracle on the
+    causal tail block (rows and keys N-256 .. N-1 of the first and last KV
+    group: exact there, since a key only receives gradient from later rows);
+    the exact identities on every group; the reproducible modes repeat bit for
+    bit."""
     w = replace(WORKLOADS["fwd_causal_gqa_n32768"], backward=True)
     note("long-context GQA backward")
     x = make_inputs(w)
@@ -338,8 +400,8 @@ def test_long_context_gqa_backward(fa):
     dof = (x["dout"].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     want_dv = dof.reshape(w.B, w.Hkv, grp, w.N, w.d).sum((2, 3))
     dv_bar = 1e-3 * np.abs(dof).reshape(w.B, w.Hkv, -1, w.d).sum(2) + 1e-2
-    det_result = None
-    for det in (0, 1):
+    det_result = {}
+    for det in MODES:
         note(f"  deterministic={det}")
         dq, dk, dv = gpu_bwd(fa, x["q"], x["k"], x["v"], x["dout"], o, lse, w.scale, w.causal, det)
         for t, gflat in enumerate(groups):
@@ -352,12 +414,14 @@ def test_long_context_gqa_backward(fa):
         assert (np.abs(dsum) <= 1e-3 * scale_k + 1e-3).all()
         assert (np.abs(dv.astype(np.float64).sum(2) - want_dv) <= dv_bar).all()
         if det:
-            det_result = (dq, dk, dv)
+            det_result[det] = (dq, dk, dv)
         del dq, dk, dv
-    note("  deterministic repeat")
-    again = gpu_bwd(fa, x["q"], x["k"], x["v"], x["dout"], o, lse, w.scale, w.causal, 1)
-    for a, b_ in zip(again, det_result):
-        assert np.array_equal(a.view(np.uint32), b_.view(np.uint32))
+    for det in (1, 2):
+        note(f"  repeat deterministic={det}")
+        again = gpu_bwd(fa, x["q"], x["k"], x["v"], x["dout"], o, lse, w.scale, w.causal, det)
+        for a, b_ in zip(again, det_result[det]):
+            assert np.array_equal(a.view(np.uint32), b_.view(np.uint32))
+        del again
 
 
 # ---------------------------------------------------------- split-KV forward
@@ -447,6 +511,8 @@ def gpu_bwd_window(fa, q, k, v, dout, o, lse, scale, window, deterministic):
                           torch.from_numpy(lse).cuda(), dev(dout), dq.t, dk.t, dv.t, B, Hq, Hkv,
                           N, d, scale, window, deterministic, ws, need)
     assert st == 0, fa.fa_status_string(st)
+    if deterministic == fa.BWD_ORDERED:
+        check_ordered_counters(fa, ws, B, Hq, Hkv, N, d, True, window)
     return dq.result("dq"), dk.result("dk"), dv.result("dv")
 
 
@@ -465,7 +531,7 @@ def test_fwd_window_small(fa, N, d, window):
     compare_lse(lse, lse_ref)
 
 
-@pytest.mark.parametrize("deterministic", [0, 1])
+@pytest.mark.parametrize("deterministic", MODES)
 @pytest.mark.parametrize("N,d,window", [(n, d, w) for n in (64, 300, 600) for d in (64, 128)
                                         for w in (1, 40, 256)])
 def test_bwd_window_small(fa, N, d, window, deterministic):
@@ -483,7 +549,7 @@ def test_bwd_window_small(fa, N, d, window, deterministic):
     compare("dv", dv, r["dv"], bar)
 
 
-@pytest.mark.parametrize("deterministic", [0, 1])
+@pytest.mark.parametrize("deterministic", MODES)
 def test_window_long_context_gqa(fa, deterministic):
     """N = 8192, GQA 2:1, window 1024: forward on sampled rows, backward on
     every element of two KV groups (the oracle's cost grows with N * window)."""
@@ -565,7 +631,7 @@ def test_window_and_split_under_switches(fa, monkeypatch, env, val):
     compare_lse(lse, lse_ref)
 
 
-@pytest.mark.parametrize("deterministic", [0, 1])
+@pytest.mark.parametrize("deterministic", MODES)
 def test_bf16_operand_floor_case(fa, deterministic):
     """Causal GQA input (the smoke check's) on which rounding P to bf16 alone
     moves dV by 1.03e-2: the gradients are held to 1.25 x that floor where it
