@@ -156,7 +156,8 @@ def parse():
     p.add_argument("--workload", default="fwd_n4096")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--atomic-reps", type=int, default=10,
-                   help="timed launches of the atomic-dQ backward reported under parts (0: skip)")
+                   help="timed launches of the atomic-dQ and ordered-dQ backward reported under "
+                        "parts (0: skip)")
     p.add_argument("--no-per-config", action="store_true",
                    help="skip timing each synthetic workload on its own")
     p.add_argument("--per-config-reps", type=int, default=10)
@@ -199,8 +200,8 @@ def main():
     dq = torch.empty((B, Hq, N, d), dtype=torch.float32, device=dev)
     dk = torch.empty((B, Hkv, N, d), dtype=torch.float32, device=dev)
     dv = torch.empty_like(dk)
-    ws_bytes = max(fa.fa_bwd_workspace_bytes(B, Hq, Hkv, N, d, 1),
-                   fa.fa_bwd_workspace_bytes(B, Hq, Hkv, N, d, 0))
+    ws_bytes = max(fa.fa_bwd_workspace_bytes(B, Hq, Hkv, N, d, m)
+                   for m in (fa.BWD_ATOMIC, fa.BWD_SEPARATE, fa.BWD_ORDERED))
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
@@ -259,18 +260,22 @@ def main():
     parts["fwd_frac_peak"] = parts["fwd_tflops"] / PEAK_BF16_TFLOPS
     parts["bwd_deterministic_frac_peak"] = parts["bwd_deterministic_tflops"] / PEAK_BF16_TFLOPS
 
-    if args.atomic_reps > 0:
+    # The other two dQ modes of the same backward, back to back after one
+    # untimed call each.
+    for mode, key in ((fa.BWD_ATOMIC, "atomic"), (fa.BWD_ORDERED, "ordered")):
+        if args.atomic_reps <= 0:
+            break
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        bwd(0)
+        bwd(mode)
         torch.cuda.synchronize()
         e0.record(stream)
         for _ in range(args.atomic_reps):
-            bwd(0)
+            bwd(mode)
         e1.record(stream)
         torch.cuda.synchronize()
         at_ms = e0.elapsed_time(e1) / args.atomic_reps
-        parts["bwd_atomic_ms_avg"] = at_ms
-        parts["bwd_atomic_tflops"] = f_bwd / (at_ms * 1e-3) / 1e12
+        parts[f"bwd_{key}_ms_avg"] = at_ms
+        parts[f"bwd_{key}_tflops"] = f_bwd / (at_ms * 1e-3) / 1e12
 
     # Roofline of the dominant launch.  fa_fwd is one kernel; fa_bwd
     # (deterministic) is a short preprocess kernel, the dK/dV kernel and the dQ
@@ -282,7 +287,7 @@ def main():
         rl_kernels = [f"fa::fwd_kernel<{d}, {cz}, 0, false>"]
         rl_flops, rl_ms = f_fwd, parts["fwd_ms_avg"]
     else:
-        rl_kernels = [f"fa::bwd_pre_kernel<{d}>", f"fa::bwd_dkdv_split_kernel<{d}, {cz}, false>",
+        rl_kernels = [f"fa::bwd_pre_kernel<{d}>", f"fa::bwd_dkdv_split_kernel<{d}, {cz}, 0>",
                       f"fa::bwd_dq_kernel<{d}, {cz}>"]
         rl_flops, rl_ms = f_bwd, parts["bwd_deterministic_ms_avg"]
     achieved = rl_flops / (rl_ms * 1e-3) / 1e12
