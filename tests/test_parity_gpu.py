@@ -651,3 +651,59 @@ def test_bf16_operand_floor_case(fa, deterministic):
         err = np.abs(got.astype(np.float64) - ref[name])
         note(f"  {name}: max_abs={err.max():.3e} (bar {bars[name]:.3e}) mean_abs={err.mean():.3e}")
         assert err.max() <= bars[name] and err.mean() <= MEAN_ABS, name
+
+
+# ------------------------------------------------------------- graph capture
+
+@pytest.mark.parametrize("mode", MODES)
+def test_graph_capture_replays(fa, mode):
+    """fa_fwd + fa_bwd captured into one HIP graph (every call only enqueues
+    kernels on the caller's stream: no allocation, no memset, no host sync).
+    Outputs are overwritten with NaN by eager kernels between replays; every
+    replay must reproduce the eager results: bit for bit, except dQ in the
+    unordered atomic mode (within 1e-5 of the eager dQ)."""
+    B, Hq, Hkv, N, d, causal = 1, 4, 2, 1000, 128, True
+    note(f"graph capture mode={mode}")
+    scale = 1 / math.sqrt(d)
+    q, k, v = dev(random_bf16((B, Hq, N, d), 81)), dev(random_bf16((B, Hkv, N, d), 82)), dev(random_bf16((B, Hkv, N, d), 83))
+    do = dev(random_bf16((B, Hq, N, d), 84))
+    o = torch.empty((B, Hq, N, d), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device="cuda")
+    dq, dk, dv = (torch.empty((B, h, N, d), dtype=torch.float32, device="cuda") for h in (Hq, Hkv, Hkv))
+    need = fa.fa_bwd_workspace_bytes(B, Hq, Hkv, N, d, mode)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    outs = (o, lse, dq, dk, dv)
+
+    def run():
+        st = fa.fa_fwd(q, k, v, o, lse, B, Hq, Hkv, N, d, scale, causal)
+        assert st == 0, fa.fa_status_string(st)
+        st = fa.fa_bwd(q, k, v, o, lse, do, dq, dk, dv, B, Hq, Hkv, N, d, scale, causal, mode,
+                       ws, need)
+        assert st == 0, fa.fa_status_string(st)
+
+    run()
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in outs]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for t in outs:
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, t, e in zip(("o", "lse", "dq", "dk", "dv"), outs, eager):
+            assert not torch.isnan(t).any(), f"replay {rep}: {name} not written"
+            if name == "dq" and mode == 0:
+                assert float((t - e).abs().max()) <= 1e-5, f"replay {rep}: dq"
+            else:
+                assert torch.equal(t.view(torch.int32), e.view(torch.int32)), f"replay {rep}: {name}"
+    del g
