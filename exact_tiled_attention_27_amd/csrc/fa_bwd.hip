@@ -39,6 +39,10 @@
 #include "fa_launch.hpp"
 #include "fa_tiles.hpp"
 
+#ifndef FA_DKDV_DEFER
+#define FA_DKDV_DEFER 1  // deterministic mode: wave B's dK products run one step late
+#endif
+
 #ifndef FA_DQ_MIN_WAVES
 #define FA_DQ_MIN_WAVES 2   // waves per SIMD the deterministic dQ kernel's registers must allow
 #endif
@@ -188,6 +192,13 @@ __global__ __launch_bounds__(512) void bwd_dkdv_split_kernel(
     using S = DkdvSplitShape<D>;
     constexpr bool ATOMIC_DQ = DQ != kDqNone;
     constexpr bool ORDERED = DQ == kDqOrdered;
+    // Deterministic mode: wave B's dK^T += Q^T dS of step st runs at the start
+    // of step st + 1, beside wave A's score products and exponentials, where
+    // B would otherwise wait at the mid-step barrier with the matrix core idle.
+    // Q tile st must then outlive step st, so the stages rotate over three
+    // slots (the atomic modes keep two: their K and dS^T arrays leave no room).
+    constexpr bool DEFER = !ATOMIC_DQ && FA_DKDV_DEFER;
+    constexpr int NSLOT = DEFER ? 3 : 2;
     // Atomic mode only: the workgroup's K rows (B operand of dQ = dS K) and
     // the step's dS^T [BN keys][BM queries] (A operand, transposing reads).
     __shared__ __attribute__((aligned(16))) char k_lds[ATOMIC_DQ ? S::BN * D * 2 : 16];
@@ -198,6 +209,9 @@ __global__ __launch_bounds__(512) void bwd_dkdv_split_kernel(
     __shared__ __attribute__((aligned(16))) char do_lds1[S::TILE];
     __shared__ __attribute__((aligned(16))) char rows0[S::ROWS_BYTES];
     __shared__ __attribute__((aligned(16))) char rows1[S::ROWS_BYTES];
+    __shared__ __attribute__((aligned(16))) char q_lds2[DEFER ? S::TILE : 16];
+    __shared__ __attribute__((aligned(16))) char do_lds2[DEFER ? S::TILE : 16];
+    __shared__ __attribute__((aligned(16))) char rows2[DEFER ? S::ROWS_BYTES : 16];
     __shared__ __attribute__((aligned(16))) char xchg_lds[4 * S::X_SLICE];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -274,11 +288,13 @@ __global__ __launch_bounds__(512) void bwd_dkdv_split_kernel(
         const int hq = g * grp + st / steps_per_head;
         const int qs = (first_qt + st % steps_per_head) * S::BM;
         const size_t ho = ((size_t)b * Hq + hq) * N;
-        qtile.issue(make_rsrc(q + ho * D, (uint32_t)N * D * 2), qs, N, P ? q_lds1 : q_lds0, wave);
-        qtile.issue(make_rsrc(dout + ho * D, (uint32_t)N * D * 2), qs, N, P ? do_lds1 : do_lds0, wave);
+        qtile.issue(make_rsrc(q + ho * D, (uint32_t)N * D * 2), qs, N,
+                    P == 0 ? q_lds0 : P == 1 ? q_lds1 : q_lds2, wave);
+        qtile.issue(make_rsrc(dout + ho * D, (uint32_t)N * D * 2), qs, N,
+                    P == 0 ? do_lds0 : P == 1 ? do_lds1 : do_lds2, wave);
         if (wave == 0) {
             const size_t hrow = ((size_t)b * Hq + hq) * NP;
-            lds_void_t *dst = (lds_void_t *)(P ? rows1 : rows0);
+            lds_void_t *dst = (lds_void_t *)(P == 0 ? rows0 : P == 1 ? rows1 : rows2);
             if (lane < 16)
                 lds_dma16_buf(make_rsrc(lse2 + hrow, (uint32_t)NP * 4), 16 * lane, qs * 4, dst);
             else if (lane < 32)
@@ -349,17 +365,38 @@ __global__ __launch_bounds__(512) void bwd_dkdv_split_kernel(
         }
     };
 
+    // A: dV^T += dO^T P.  B: dK^T += Q^T dS.  tl: the dO (A) or Q (B) tile,
+    // read transposed; bo: P or dS as B operands.
+    auto tr_products = [&](const char *tl, const bf16x8(&bo)[4]) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ks++)
+#pragma unroll
+            for (int db = 0; db < S::DBLK; db++) {
+                const uint32_t o0 = troff[db][0] + 16 * ks * D * 2;
+                const uint32_t o1 = troff[db][1] + 16 * ks * D * 2;
+                acc[db] = mfma32(join_bf16x8(lds_read_tr16(tl, o0), lds_read_tr16(tl, o1)), bo[ks], acc[db]);
+            }
+    };
+    bf16x8 bprev[4];  // deferred mode, B waves: the previous step's dS
+#pragma unroll
+    for (int i = 0; i < 4; i++) bprev[i] = bf16x8{};
+
     auto step = [&](auto slot, int st) {
         constexpr int P = decltype(slot)::value;
         const int qs = (first_qt + st % steps_per_head) * S::BM;
-        const char *ql = P ? q_lds1 : q_lds0;
-        const char *dol = P ? do_lds1 : do_lds0;
-        const char *rows = P ? rows1 : rows0;
+        constexpr int PN = (P + 1) % NSLOT;          // slot of step st + 1
+        constexpr int PP = (P + NSLOT - 1) % NSLOT;  // slot of step st - 1
+        const char *ql = P == 0 ? q_lds0 : P == 1 ? q_lds1 : q_lds2;
+        const char *dol = P == 0 ? do_lds0 : P == 1 ? do_lds1 : do_lds2;
+        const char *rows = P == 0 ? rows0 : P == 1 ? rows1 : rows2;
         // Ordered mode: step st - 2's adds completed at the last end-of-step
         // wait; publish them before this step's copies are in flight (the
         // release waits for every outstanding memory operation of the wave).
         if (ORDERED && !wave_a && st > 1) release(st - 2);
-        if (st + 1 < n_steps) issue(st + 1, std::integral_constant<int, 1 - P>{});
+        if (st + 1 < n_steps) issue(st + 1, std::integral_constant<int, PN>{});
+        // Deferred mode, B waves: dK^T += Q^T dS of step st - 1 (its Q tile
+        // is still in slot PP, its dS in bprev) while the A waves compute S.
+        if (DEFER && !wave_a && st > 0) tr_products(PP == 0 ? q_lds0 : PP == 1 ? q_lds1 : q_lds2, bprev);
         // Atomic modes: the B waves add the previous step's dS K into dQ first
         // (no score registers live yet), while the A waves start on S.
         if (ATOMIC_DQ && !wave_a && st > 0) dq_update(st - 1);
@@ -458,16 +495,12 @@ __global__ __launch_bounds__(512) void bwd_dkdv_split_kernel(
                 }
             }
         }
-        // A: dV^T += dO^T P.  B: dK^T += Q^T dS.
-        const char *tl = wave_a ? dol : ql;
+        if (DEFER && !wave_a) {
 #pragma unroll
-        for (int ks = 0; ks < 4; ks++)
-#pragma unroll
-            for (int db = 0; db < S::DBLK; db++) {
-                const uint32_t o0 = troff[db][0] + 16 * ks * D * 2;
-                const uint32_t o1 = troff[db][1] + 16 * ks * D * 2;
-                acc[db] = mfma32(join_bf16x8(lds_read_tr16(tl, o0), lds_read_tr16(tl, o1)), bop[ks], acc[db]);
-            }
+            for (int i = 0; i < 4; i++) bprev[i] = bop[i];
+        } else {
+            tr_products(wave_a ? dol : ql, bop);
+        }
         dma_barrier();  // next stage landed; this stage and the exchange are free
     };
     using Slot0 = std::integral_constant<int, 0>;
@@ -486,11 +519,31 @@ __global__ __launch_bounds__(512) void bwd_dkdv_split_kernel(
 #pragma unroll
     for (int s = 0; s < S::KSTEPS; s++) settle(kvf[s]);
     int st = 0;
-    for (; st + 2 <= n_steps; st += 2) {
-        step(Slot0{}, st);
-        step(Slot1{}, st + 1);
+    if constexpr (DEFER) {
+        using Slot2 = std::integral_constant<int, 2>;
+        for (; st + 3 <= n_steps; st += 3) {
+            step(Slot0{}, st);
+            step(Slot1{}, st + 1);
+            step(Slot2{}, st + 2);
+        }
+        // Then the last step's dK products (its Q tile is still in its slot).
+        if (st + 2 <= n_steps) {
+            step(Slot0{}, st);
+            step(Slot1{}, st + 1);
+            if (!wave_a) tr_products(q_lds1, bprev);
+        } else if (st + 1 <= n_steps) {
+            step(Slot0{}, st);
+            if (!wave_a) tr_products(q_lds0, bprev);
+        } else if (n_steps > 0 && !wave_a) {
+            tr_products(q_lds2, bprev);
+        }
+    } else {
+        for (; st + 2 <= n_steps; st += 2) {
+            step(Slot0{}, st);
+            step(Slot1{}, st + 1);
+        }
+        if (st < n_steps) step(Slot0{}, st);
     }
-    if (st < n_steps) step(Slot0{}, st);
     if (ATOMIC_DQ && !wave_a && n_steps > 0) {
         if (ORDERED && n_steps > 1) release(n_steps - 2);
         dq_update(n_steps - 1);
