@@ -10,8 +10,11 @@ Asymmetric Hardware Scaling Wall" (S = QK^T/sqrt(d), P = exp(S - m)/l,
 O = PV) and the simulator's validation harness, which equates the tiled result
 with softmax(QK^T * scale) V; the causal mask keeps key j for query i iff
 j <= i (the simulator's in-tile causal mask), and a causal sliding window of
-W keys (window=W > 0) keeps max(0, i - W + 1) <= j <= i.  The backward is the analytic
-gradient of that definition (the pages give no backward formulas).
+W keys (window=W > 0) keeps max(0, i - W + 1) <= j <= i.  With slopes (one
+per query head, float64 [Hq]) every score gets the linear position bias
+slopes[h] * (j - i) added after the scale (the ALiBi form of an additive score
+modification).  The backward is the analytic gradient of that definition (the
+pages give no backward formulas).
 
 Inputs are bf16 bit patterns held in numpy uint16 arrays, laid out
 [B, H, N, d].  Outputs are float64.
@@ -62,6 +65,13 @@ def _load():
                                              c_int, c_float, c_int, c_int, c_int, i64p, c_i64,
                                              f64p, f64p, f64p, f64p, f64p, c_int]
     lib.oracle_bwd_groups_tail_w.restype = c_int
+    lib.oracle_fwd_rows_b.argtypes = [u16p, u16p, u16p, c_int, c_int, c_int, c_int, c_int,
+                                      c_float, c_int, c_int, f64p, i64p, c_i64, f64p, f64p, c_int]
+    lib.oracle_fwd_rows_b.restype = c_int
+    lib.oracle_bwd_groups_tail_b.argtypes = [u16p, u16p, u16p, u16p, c_int, c_int, c_int, c_int,
+                                             c_int, c_float, c_int, c_int, f64p, c_int, i64p,
+                                             c_i64, f64p, f64p, f64p, f64p, f64p, c_int]
+    lib.oracle_bwd_groups_tail_b.restype = c_int
     _lib = lib
     return lib
 
@@ -99,23 +109,23 @@ def _shape(q, k, v):
     return B, Hq, Hkv, N, d
 
 
-def fwd(q, k, v, scale, causal, threads=None, window=0):
+def _slopes(slopes, Hq):
+    if slopes is None:
+        return None, None
+    a = np.ascontiguousarray(slopes, dtype=np.float64)
+    if a.shape != (Hq,):
+        raise ValueError(f"slopes must have shape ({Hq},), got {a.shape}")
+    return a, _ptr(a, ctypes.c_double)
+
+
+def fwd(q, k, v, scale, causal, threads=None, window=0, slopes=None):
     """Exact attention forward.  Returns (O [B,Hq,N,d] f64, LSE [B,Hq,N] f64)."""
-    lib = _load()
-    q, k, v = _u16(q, "q"), _u16(k, "k"), _u16(v, "v")
-    B, Hq, Hkv, N, d = _shape(q, k, v)
-    o = np.empty((B, Hq, N, d), np.float64)
-    lse = np.empty((B, Hq, N), np.float64)
-    st = lib.oracle_fwd_w(_ptr(q, ctypes.c_uint16), _ptr(k, ctypes.c_uint16),
-                          _ptr(v, ctypes.c_uint16), _ptr(o, ctypes.c_double),
-                          _ptr(lse, ctypes.c_double), B, Hq, Hkv, N, d, float(scale),
-                          int(bool(causal)), int(window), threads or default_threads())
-    if st:
-        raise RuntimeError(f"oracle_fwd failed with status {st}")
-    return o, lse
+    B, Hq, N, d = q.shape
+    o, lse = fwd_rows(q, k, v, scale, causal, np.arange(B * Hq * N), threads, window, slopes)
+    return o.reshape(B, Hq, N, d), lse.reshape(B, Hq, N)
 
 
-def fwd_rows(q, k, v, scale, causal, rows, threads=None, window=0):
+def fwd_rows(q, k, v, scale, causal, rows, threads=None, window=0, slopes=None):
     """Forward for selected query rows.  rows: flat indices (b*Hq + h)*N + i.
     Returns (O [n, d] f64, LSE [n] f64)."""
     lib = _load()
@@ -124,9 +134,10 @@ def fwd_rows(q, k, v, scale, causal, rows, threads=None, window=0):
     rows = np.ascontiguousarray(rows, dtype=np.int64)
     o = np.empty((rows.size, d), np.float64)
     lse = np.empty((rows.size,), np.float64)
-    st = lib.oracle_fwd_rows_w(_ptr(q, ctypes.c_uint16), _ptr(k, ctypes.c_uint16),
+    keep, sp = _slopes(slopes, Hq)
+    st = lib.oracle_fwd_rows_b(_ptr(q, ctypes.c_uint16), _ptr(k, ctypes.c_uint16),
                                _ptr(v, ctypes.c_uint16), B, Hq, Hkv, N, d, float(scale),
-                               int(bool(causal)), int(window), _ptr(rows, ctypes.c_int64),
+                               int(bool(causal)), int(window), sp, _ptr(rows, ctypes.c_int64),
                                rows.size, _ptr(o, ctypes.c_double), _ptr(lse, ctypes.c_double),
                                threads or default_threads())
     if st:
@@ -134,7 +145,7 @@ def fwd_rows(q, k, v, scale, causal, rows, threads=None, window=0):
     return o, lse
 
 
-def bwd_groups(q, k, v, dout, scale, causal, groups, threads=None, window=0):
+def bwd_groups(q, k, v, dout, scale, causal, groups, threads=None, window=0, slopes=None):
     """Backward for selected key/value groups (flat index b*Hkv + g).
 
     Returns dict with dq [G, Hq/Hkv, N, d], dk [G, N, d], dv [G, N, d],
@@ -153,10 +164,11 @@ def bwd_groups(q, k, v, dout, scale, causal, groups, threads=None, window=0):
         "o": np.empty((G, grp, N, d), np.float64),
         "lse": np.empty((G, grp, N), np.float64),
     }
-    st = lib.oracle_bwd_groups_tail_w(
+    keep, sp = _slopes(slopes, Hq)
+    st = lib.oracle_bwd_groups_tail_b(
         _ptr(q, ctypes.c_uint16), _ptr(k, ctypes.c_uint16), _ptr(v, ctypes.c_uint16),
         _ptr(dout, ctypes.c_uint16), B, Hq, Hkv, N, d, float(scale), int(bool(causal)),
-        int(window), 0, _ptr(groups, ctypes.c_int64), G, _ptr(out["dq"], ctypes.c_double),
+        int(window), sp, 0, _ptr(groups, ctypes.c_int64), G, _ptr(out["dq"], ctypes.c_double),
         _ptr(out["dk"], ctypes.c_double), _ptr(out["dv"], ctypes.c_double),
         _ptr(out["o"], ctypes.c_double), _ptr(out["lse"], ctypes.c_double),
         threads or default_threads())
@@ -165,7 +177,7 @@ def bwd_groups(q, k, v, dout, scale, causal, groups, threads=None, window=0):
     return out
 
 
-def bwd_groups_tail(q, k, v, dout, scale, row0, groups, threads=None, window=0):
+def bwd_groups_tail(q, k, v, dout, scale, row0, groups, threads=None, window=0, slopes=None):
     """Causal backward restricted to rows and keys row0 .. N-1 of the selected
     groups (exact there: a key only receives gradient from later rows).
 
@@ -185,9 +197,11 @@ def bwd_groups_tail(q, k, v, dout, scale, row0, groups, threads=None, window=0):
         "o": np.empty((G, grp, NT, d), np.float64),
         "lse": np.empty((G, grp, NT), np.float64),
     }
-    st = lib.oracle_bwd_groups_tail_w(
+    keep, sp = _slopes(slopes, Hq)
+    st = lib.oracle_bwd_groups_tail_b(
         _ptr(q, ctypes.c_uint16), _ptr(k, ctypes.c_uint16), _ptr(v, ctypes.c_uint16),
-        _ptr(dout, ctypes.c_uint16), B, Hq, Hkv, N, d, float(scale), 1, int(window), int(row0),
+        _ptr(dout, ctypes.c_uint16), B, Hq, Hkv, N, d, float(scale), 1, int(window), sp,
+        int(row0),
         _ptr(groups, ctypes.c_int64), G, _ptr(out["dq"], ctypes.c_double),
         _ptr(out["dk"], ctypes.c_double), _ptr(out["dv"], ctypes.c_double),
         _ptr(out["o"], ctypes.c_double), _ptr(out["lse"], ctypes.c_double),
@@ -197,11 +211,11 @@ def bwd_groups_tail(q, k, v, dout, scale, row0, groups, threads=None, window=0):
     return out
 
 
-def bwd(q, k, v, dout, scale, causal, threads=None, window=0):
+def bwd(q, k, v, dout, scale, causal, threads=None, window=0, slopes=None):
     """Whole backward.  Returns dict dq [B,Hq,N,d], dk/dv [B,Hkv,N,d], o, lse."""
     B, Hq, N, d = q.shape
     Hkv = k.shape[1]
-    r = bwd_groups(q, k, v, dout, scale, causal, np.arange(B * Hkv), threads, window)
+    r = bwd_groups(q, k, v, dout, scale, causal, np.arange(B * Hkv), threads, window, slopes)
     return {
         "dq": r["dq"].reshape(B, Hq, N, d),
         "dk": r["dk"].reshape(B, Hkv, N, d),

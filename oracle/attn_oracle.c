@@ -24,6 +24,13 @@
  *   FlexAttention kind expresses; the guide's deployment section names such
  *   custom masks) further drops keys j <= i - W: query i sees keys
  *   max(0, i - W + 1) .. i.  W <= 0 means no window.
+ *   Linear position bias (the `_b` entry points): with per-query-head slopes
+ *   a_h, every score gets a_h * (j - i) added after the scale,
+ *     s_ij = scale * sum_c q_ic k_jc + a_h * (j - i),
+ *   the additive score modification of the FlexAttention kind the guide's
+ *   deployment section points to (ALiBi form); softmax, O, LSE and the
+ *   gradients below are unchanged in form (the bias does not depend on Q, K
+ *   or V, so it only enters through s).  slopes == NULL means no bias.
  *   Grouped-query attention: query head h reads key/value head
  *   h / (Hq / Hkv) (contiguous groups).
  *
@@ -103,16 +110,32 @@ static double scores_row(const uint16_t *qi, const uint16_t *kh, int n, int d,
     return m;
 }
 
+/* The same with the linear position bias: the keys are lo .. lo + n - 1,
+ * s_ij = scale * (q_i . k_j) + slope * (j - i). */
+static double scores_row_bias(const uint16_t *qi, const uint16_t *kh, int n, int d, double sc,
+                              double slope, int lo, int i, double *s)
+{
+    double m = -INFINITY;
+    for (int j = 0; j < n; j++) {
+        const uint16_t *kj = kh + (size_t)j * d;
+        double dot = 0.0;
+        for (int c = 0; c < d; c++) dot += bf16_to_double(qi[c]) * bf16_to_double(kj[c]);
+        s[j] = sc * dot + slope * (double)(lo + j - i);
+        if (s[j] > m) m = s[j];
+    }
+    return m;
+}
+
 /*
  * Forward for an arbitrary list of query rows.  rows[r] is the flat index
  * (b * Hq + h) * N + i.  o_rows is [nrows, d], lse_rows is [nrows] (either
  * may be NULL).  Used for whole tensors (all rows) and for sampled rows of
  * tensors too large to check in full.
  */
-int oracle_fwd_rows_w(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+int oracle_fwd_rows_b(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                       int B, int Hq, int Hkv, int N, int d, float scale, int causal, int window,
-                      const int64_t *rows, int64_t nrows, double *o_rows, double *lse_rows,
-                      int nthreads)
+                      const double *slopes, const int64_t *rows, int64_t nrows, double *o_rows,
+                      double *lse_rows, int nthreads)
 {
     if (!q || !k || !v || !rows || nrows < 0) return ORACLE_BAD_ARGS;
     if (!check_shape(B, Hq, Hkv, N, d)) return ORACLE_BAD_ARGS;
@@ -148,7 +171,8 @@ int oracle_fwd_rows_w(const uint16_t *q, const uint16_t *k, const uint16_t *v,
             const uint16_t *kh = k + row_off(b, g, Hkv, lo, N, d);
             const uint16_t *vh = v + row_off(b, g, Hkv, lo, N, d);
 
-            const double m = scores_row(qi, kh, n, d, sc, s);
+            const double m = slopes ? scores_row_bias(qi, kh, n, d, sc, slopes[h], lo, i, s)
+                                    : scores_row(qi, kh, n, d, sc, s);
             double l = 0.0;
             for (int j = 0; j < n; j++) {
                 s[j] = exp(s[j] - m); /* p_ij */
@@ -167,6 +191,15 @@ int oracle_fwd_rows_w(const uint16_t *q, const uint16_t *k, const uint16_t *v,
         free(acc);
     }
     return failed ? ORACLE_NO_MEMORY : ORACLE_OK;
+}
+
+int oracle_fwd_rows_w(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                      int B, int Hq, int Hkv, int N, int d, float scale, int causal, int window,
+                      const int64_t *rows, int64_t nrows, double *o_rows, double *lse_rows,
+                      int nthreads)
+{
+    return oracle_fwd_rows_b(q, k, v, B, Hq, Hkv, N, d, scale, causal, window, NULL, rows, nrows,
+                             o_rows, lse_rows, nthreads);
 }
 
 int oracle_fwd_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v,
@@ -191,6 +224,23 @@ int oracle_fwd_w(const uint16_t *q, const uint16_t *k, const uint16_t *v, double
     for (int64_t r = 0; r < total; r++) rows[r] = r;
     int st = oracle_fwd_rows_w(q, k, v, B, Hq, Hkv, N, d, scale, causal, window, rows, total, o,
                                lse, nthreads);
+    free(rows);
+    return st;
+}
+
+/* Whole forward with the linear position bias (slopes [Hq]). */
+int oracle_fwd_b(const uint16_t *q, const uint16_t *k, const uint16_t *v, double *o, double *lse,
+                 int B, int Hq, int Hkv, int N, int d, float scale, int causal, int window,
+                 const double *slopes, int nthreads)
+{
+    if (!o || !slopes) return ORACLE_BAD_ARGS;
+    if (!check_shape(B, Hq, Hkv, N, d)) return ORACLE_BAD_ARGS;
+    const int64_t total = (int64_t)B * Hq * N;
+    int64_t *rows = (int64_t *)malloc(sizeof(int64_t) * (size_t)total);
+    if (!rows) return ORACLE_NO_MEMORY;
+    for (int64_t r = 0; r < total; r++) rows[r] = r;
+    int st = oracle_fwd_rows_b(q, k, v, B, Hq, Hkv, N, d, scale, causal, window, slopes, rows,
+                               total, o, lse, nthreads);
     free(rows);
     return st;
 }
@@ -224,11 +274,11 @@ int oracle_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, double *
  * without the causal mask).  With a window, key j receives gradient from rows
  * j .. j + W - 1 only, still all >= j.
  */
-int oracle_bwd_groups_tail_w(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+int oracle_bwd_groups_tail_b(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                              const uint16_t *dout, int B, int Hq, int Hkv, int N, int d,
-                             float scale, int causal, int window, int row0,
-                             const int64_t *groups, int64_t ngroups, double *dq, double *dk,
-                             double *dv, double *o, double *lse, int nthreads)
+                             float scale, int causal, int window, const double *slopes,
+                             int row0, const int64_t *groups, int64_t ngroups, double *dq,
+                             double *dk, double *dv, double *o, double *lse, int nthreads)
 {
     if (!q || !k || !v || !dout || !groups || !dq || !dk || !dv || ngroups < 0)
         return ORACLE_BAD_ARGS;
@@ -285,7 +335,8 @@ int oracle_bwd_groups_tail_w(const uint16_t *q, const uint16_t *k, const uint16_
                 const uint16_t *khi = kh + (size_t)lo * d; /* keys lo .. lo + n - 1 */
                 const uint16_t *vhi = vh + (size_t)lo * d;
 
-                const double m = scores_row(qi, khi, n, d, sc, s);
+                const double m = slopes ? scores_row_bias(qi, khi, n, d, sc, slopes[h], lo, i, s)
+                                        : scores_row(qi, khi, n, d, sc, s);
                 double l = 0.0;
                 for (int j = 0; j < n; j++) {
                     s[j] = exp(s[j] - m);
@@ -350,7 +401,8 @@ int oracle_bwd_groups_tail_w(const uint16_t *q, const uint16_t *k, const uint16_
                         double dot = 0.0, dp = 0.0;
                         for (int c = 0; c < d; c++) dot += bf16_to_double(qi[c]) * bf16_to_double(kj[c]);
                         for (int c = 0; c < d; c++) dp += bf16_to_double(doi[c]) * bf16_to_double(vj[c]);
-                        const double P = exp(sc * dot - m_buf[rr]) / l_buf[rr];
+                        const double sij = slopes ? sc * dot + slopes[h] * (double)(j - i) : sc * dot;
+                        const double P = exp(sij - m_buf[rr]) / l_buf[rr];
                         const double dS = P * (dp - D_buf[rr]);
                         for (int c = 0; c < d; c++) {
                             accv[c] += P * bf16_to_double(doi[c]);
@@ -377,6 +429,16 @@ int oracle_bwd_groups_tail_w(const uint16_t *q, const uint16_t *k, const uint16_
     free(D_buf);
     free(o_buf);
     return failed ? ORACLE_NO_MEMORY : ORACLE_OK;
+}
+
+int oracle_bwd_groups_tail_w(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                             const uint16_t *dout, int B, int Hq, int Hkv, int N, int d,
+                             float scale, int causal, int window, int row0,
+                             const int64_t *groups, int64_t ngroups, double *dq, double *dk,
+                             double *dv, double *o, double *lse, int nthreads)
+{
+    return oracle_bwd_groups_tail_b(q, k, v, dout, B, Hq, Hkv, N, d, scale, causal, window, NULL,
+                                    row0, groups, ngroups, dq, dk, dv, o, lse, nthreads);
 }
 
 int oracle_bwd_groups_tail(const uint16_t *q, const uint16_t *k, const uint16_t *v,
