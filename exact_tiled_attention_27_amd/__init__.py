@@ -1,8 +1,8 @@
 """Exact tiled attention for AMD MI355X (gfx950): Python binding of libfa.so.
 
 The functions fa_fwd, fa_fwd_window, fa_fwd_splitkv,
-fa_fwd_splitkv_workspace_bytes, fa_bwd, fa_bwd_window, fa_bwd_workspace_bytes
-and fa_status_string mirror the C ABI in include/fa.h one for one; this module only marshals arguments (device pointers, sizes, the
+fa_fwd_splitkv_workspace_bytes, fa_fwd_alibi, fa_bwd, fa_bwd_window,
+fa_bwd_alibi, fa_bwd_workspace_bytes and fa_status_string mirror the C ABI in include/fa.h one for one; this module only marshals arguments (device pointers, sizes, the
 current HIP stream).  Every step of the computation runs in the library's HIP
 kernels; there is no fallback path, and importing this package fails if
 libfa.so has not been built.
@@ -15,7 +15,7 @@ import math
 import os
 
 __all__ = ["fa_fwd", "fa_fwd_window", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_bytes",
-           "fa_bwd", "fa_bwd_window", "fa_bwd_workspace_bytes", "fa_status_string", "FAError",
+           "fa_fwd_alibi", "fa_bwd_alibi", "fa_bwd", "fa_bwd_window", "fa_bwd_workspace_bytes", "fa_status_string", "FAError",
            "attention_fwd", "attention_bwd", "LIB_PATH", "STATUS", "MAX_SPLITS",
            "BWD_ATOMIC", "BWD_SEPARATE", "BWD_ORDERED"]
 
@@ -60,6 +60,11 @@ _lib.fa_bwd.argtypes = [_vp, _vp, _vp, _fp, _fp, _vp, _fp, _fp, _fp, _i, _i, _i,
 _lib.fa_bwd.restype = _i
 _lib.fa_bwd_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i]
 _lib.fa_bwd_workspace_bytes.restype = _sz
+_lib.fa_fwd_alibi.argtypes = [_vp, _vp, _vp, _fp, _fp, _fp, _i, _i, _i, _i, _i, _f, _i, _vp]
+_lib.fa_fwd_alibi.restype = _i
+_lib.fa_bwd_alibi.argtypes = [_vp, _vp, _vp, _fp, _fp, _vp, _fp, _fp, _fp, _fp, _i, _i, _i, _i,
+                              _i, _f, _i, _i, _vp, _sz, _vp]
+_lib.fa_bwd_alibi.restype = _i
 _lib.fa_status_string.argtypes = [_i]
 _lib.fa_status_string.restype = ctypes.c_char_p
 
@@ -112,6 +117,22 @@ def fa_bwd_window(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, N, d, scale, wi
                               _addr(dq), _addr(dk), _addr(dv), B, Hq, Hkv, N, d, float(scale),
                               int(window), int(deterministic), _addr(workspace),
                               int(workspace_bytes), _stream(stream, q, dq))
+
+
+def fa_fwd_alibi(q, k, v, o, lse, slopes, B, Hq, Hkv, N, d, scale, causal, stream=None) -> int:
+    """C ABI fa_fwd_alibi (linear position bias; slopes fp32 [Hq] on the device).  Status out."""
+    return _lib.fa_fwd_alibi(_addr(q), _addr(k), _addr(v), _addr(o), _addr(lse), _addr(slopes),
+                             B, Hq, Hkv, N, d, float(scale), int(bool(causal)),
+                             _stream(stream, q, o))
+
+
+def fa_bwd_alibi(q, k, v, o, lse, dout, dq, dk, dv, slopes, B, Hq, Hkv, N, d, scale, causal,
+                 deterministic, workspace, workspace_bytes, stream=None) -> int:
+    """C ABI fa_bwd_alibi.  Status out."""
+    return _lib.fa_bwd_alibi(_addr(q), _addr(k), _addr(v), _addr(o), _addr(lse), _addr(dout),
+                             _addr(dq), _addr(dk), _addr(dv), _addr(slopes), B, Hq, Hkv, N, d,
+                             float(scale), int(bool(causal)), int(deterministic),
+                             _addr(workspace), int(workspace_bytes), _stream(stream, q, dq))
 
 
 def fa_fwd_splitkv(q, k, v, o, lse, B, Hq, Hkv, N, d, scale, causal, num_splits, workspace,

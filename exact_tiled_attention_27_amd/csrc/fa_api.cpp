@@ -66,7 +66,8 @@ int exp2_poly_share()
 // fa_fwd and fa_fwd_window: window 0 = none (then causal as given), else
 // causal with that window (>= 1, checked by the caller).
 int fwd_impl(const void *q, const void *k, const void *v, float *o, float *lse, int B, int Hq,
-             int Hkv, int N, int d, float scale, int causal, int window, void *stream)
+             int Hkv, int N, int d, float scale, int causal, int window, void *stream,
+             const float *slopes = nullptr)
 {
     if (!q || !k || !v || !o) return FA_ERR_NULL;
     int st = check_common(B, Hq, Hkv, N, d, scale);
@@ -75,8 +76,8 @@ int fwd_impl(const void *q, const void *k, const void *v, float *o, float *lse, 
         (lse && !aligned16(lse)))
         return FA_ERR_ALIGN;
     fa::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, N, d, scale, rescale_tau(), causal != 0,
-                  exp2_poly_share(), window < N ? window : 0, 1, nullptr, nullptr,
-                  reinterpret_cast<hipStream_t>(stream)};
+                  slopes ? 0 : exp2_poly_share(), window < N ? window : 0, 1, nullptr, nullptr,
+                  reinterpret_cast<hipStream_t>(stream), slopes};
     return hip_status(fa::launch_fwd(a));
 }
 
@@ -85,7 +86,7 @@ int fwd_impl(const void *q, const void *k, const void *v, float *o, float *lse, 
 int bwd_impl(const void *q, const void *k, const void *v, const float *o, const float *lse,
              const void *dout, float *dq, float *dk, float *dv, int B, int Hq, int Hkv, int N,
              int d, float scale, int causal, int window, int deterministic, void *workspace,
-             size_t workspace_bytes, void *stream)
+             size_t workspace_bytes, void *stream, const float *slopes = nullptr)
 {
     if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL;
     int st = check_common(B, Hq, Hkv, N, d, scale);
@@ -107,7 +108,7 @@ int bwd_impl(const void *q, const void *k, const void *v, const float *o, const 
                     : nullptr;
     fa::BwdArgs a{q, k, v, dout, o, lse, dq, dk, dv, delta, lse2, sync, B, Hq, Hkv, N, d, scale,
                   causal != 0, deterministic, window < N ? window : 0,
-                  reinterpret_cast<hipStream_t>(stream)};
+                  reinterpret_cast<hipStream_t>(stream), slopes};
     return hip_status(fa::launch_bwd(a));
 }
 
@@ -208,4 +209,23 @@ int fa_bwd_window(const void *q, const void *k, const void *v, const float *o, c
                     deterministic, workspace, workspace_bytes, stream);
 }
 
+int fa_fwd_alibi(const void *q, const void *k, const void *v, float *o, float *lse,
+                 const float *slopes, int B, int Hq, int Hkv, int N, int d, float scale,
+                 int causal, void *stream)
+{
+    if (!slopes) return FA_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(slopes) & 3u) != 0) return FA_ERR_ALIGN;
+    return fwd_impl(q, k, v, o, lse, B, Hq, Hkv, N, d, scale, causal, 0, stream, slopes);
+}
+
+int fa_bwd_alibi(const void *q, const void *k, const void *v, const float *o, const float *lse,
+                 const void *dout, float *dq, float *dk, float *dv, const float *slopes,
+                 int B, int Hq, int Hkv, int N, int d, float scale, int causal,
+                 int deterministic, void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (!slopes) return FA_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(slopes) & 3u) != 0) return FA_ERR_ALIGN;
+    return bwd_impl(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, N, d, scale, causal, 0,
+                    deterministic, workspace, workspace_bytes, stream, slopes);
+}
 }  // extern "C"

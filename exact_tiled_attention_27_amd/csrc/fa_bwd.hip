@@ -181,13 +181,16 @@ __device__ __forceinline__ void wait_turn(const int *turn, int want, int *sync, 
     asm volatile("" ::: "memory");
 }
 
-template <int D, bool CAUSAL, int DQ>
+// BIAS: the linear position bias, slopes[hq] * (key - query), enters P's
+// recomputation (added to the raw score as slope / scale * (key - query)).
+template <int D, bool CAUSAL, int DQ, bool BIAS = false>
 __global__ __launch_bounds__(512) void bwd_dkdv_split_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, const uint16_t *__restrict__ dout,
     const float *__restrict__ lse2, const float *__restrict__ delta, float *__restrict__ dq,
     float *__restrict__ dk, float *__restrict__ dv, int Hq, int Hkv, int N, int BHkv, int KT,
-    float scale, float scale_log2, int window, int *__restrict__ sync)
+    float scale, float scale_log2, int window, int *__restrict__ sync,
+    const float *__restrict__ slopes)
 {
     using S = DkdvSplitShape<D>;
     constexpr bool ATOMIC_DQ = DQ != kDqNone;
@@ -429,6 +432,9 @@ __global__ __launch_bounds__(512) void bwd_dkdv_split_kernel(
             // P = exp2(s * c - LSE2); masked pairs get a -inf exponent.
             const bool need_mask = kv0 + S::BN > N || qs + S::BM > N ||
                                    (CAUSAL && (qs < kv0 + S::BN - 1 || qs + S::BM - 1 - kv0 >= window));
+            // Slope / scale of this step's query head.
+            const float bias_a =
+                BIAS ? slopes[g * grp + st / steps_per_head] * (kLog2e / scale_log2) : 0.f;
             auto softmax = [&](auto masked) {
                 constexpr bool MASK = decltype(masked)::value;
 #pragma unroll
@@ -439,7 +445,9 @@ __global__ __launch_bounds__(512) void bwd_dkdv_split_kernel(
                         const f32x4 l2 = lds_read_f32x4(rows, qr * 4);
 #pragma unroll
                         for (int i = 0; i < 4; i++) {
-                            float e = __builtin_fmaf(x[qb][4 * gq + i], scale_log2, -l2[i]);
+                            float xs = x[qb][4 * gq + i];
+                            if (BIAS) xs += bias_a * (float)(key - (qs + qr + i));
+                            float e = __builtin_fmaf(xs, scale_log2, -l2[i]);
                             if (MASK) {
                                 const int qi = qs + qr + i;
                                 const bool dead = key >= N || qi >= N ||
@@ -578,12 +586,13 @@ struct DqShape {
 
 // K and V tiles live in four separate LDS arrays (slot t % 2 of each), so
 // that reads of one slot never wait for the copies into the other.
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool BIAS = false>
 __global__ __launch_bounds__(256, FA_DQ_MIN_WAVES) void bwd_dq_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, const uint16_t *__restrict__ dout,
     const float *__restrict__ lse2, const float *__restrict__ delta, float *__restrict__ dq,
-    int Hq, int Hkv, int N, int BH, int QT, float scale, float scale_log2, int window)
+    int Hq, int Hkv, int N, int BH, int QT, float scale, float scale_log2, int window,
+    const float *__restrict__ slopes)
 {
     using S = DqShape<D>;
     __shared__ __attribute__((aligned(16))) char k_lds0[S::TILE];
@@ -603,6 +612,7 @@ __global__ __launch_bounds__(256, FA_DQ_MIN_WAVES) void bwd_dq_kernel(
     const int q0 = qt * S::BM;
     const int qrow = q0 + wave * 32 + col;
     const size_t head_off = ((size_t)b * Hq + hq) * N;
+    const float bias_a = BIAS ? slopes[hq] * (kLog2e / scale_log2) : 0.f;  // slope / scale
 
     const uint16_t *qh = q + head_off * D;
     const uint16_t *doh = dout + head_off * D;
@@ -693,9 +703,11 @@ __global__ __launch_bounds__(256, FA_DQ_MIN_WAVES) void bwd_dq_kernel(
             }
 #pragma unroll
             for (int r = 0; r < 16; r++) {
-                float x = __builtin_fmaf(st[r], scale_log2, -l2);
+                const int kk = key0 + kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                float xs = st[r];
+                if (BIAS) xs += bias_a * (float)(kk - qrow);
+                float x = __builtin_fmaf(xs, scale_log2, -l2);
                 if (MASK) {
-                    const int kk = key0 + kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
                     const bool dead = kk >= N || (CAUSAL && (kk > qrow || qrow - kk >= window));
                     x = dead ? -INFINITY : x;
                 }
@@ -796,24 +808,28 @@ static hipError_t launch_bwd_t(const BwdArgs &a)
         auto kern = a.mode == kBwdSeparate  ? bwd_dkdv_split_kernel<D, CAUSAL, kDqNone>
                     : a.mode == kBwdOrdered ? bwd_dkdv_split_kernel<D, CAUSAL, kDqOrdered>
                                             : bwd_dkdv_split_kernel<D, CAUSAL, kDqAtomic>;
+        if (a.slopes)
+            kern = a.mode == kBwdSeparate  ? bwd_dkdv_split_kernel<D, CAUSAL, kDqNone, true>
+                 : a.mode == kBwdOrdered ? bwd_dkdv_split_kernel<D, CAUSAL, kDqOrdered, true>
+                                         : bwd_dkdv_split_kernel<D, CAUSAL, kDqAtomic, true>;
         hipLaunchKernelGGL(kern, dim3(BHkv * KT), dim3(S::THREADS), 0, a.stream,
                            (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v,
                            (const uint16_t *)a.dout, a.lse2, a.delta, a.dq, a.dk, a.dv, a.Hq,
                            a.Hkv, a.N, BHkv, KT, a.scale, scale_log2,
                            a.window > 0 ? a.window : kNoWindow,
-                           a.mode == kBwdOrdered ? a.sync : nullptr);
+                           a.mode == kBwdOrdered ? a.sync : nullptr, a.slopes);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     if (a.mode == kBwdSeparate) {
         using S = DqShape<D>;
         const int QT = (a.N + S::BM - 1) / S::BM;
-        auto kern = bwd_dq_kernel<D, CAUSAL>;
+        auto kern = a.slopes ? bwd_dq_kernel<D, CAUSAL, true> : bwd_dq_kernel<D, CAUSAL>;
         hipError_t e;
         hipLaunchKernelGGL(kern, dim3(BH * QT), dim3(S::THREADS), 0, a.stream,
                            (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v,
                            (const uint16_t *)a.dout, a.lse2, a.delta, a.dq, a.Hq, a.Hkv, a.N, BH,
-                           QT, a.scale, scale_log2, a.window > 0 ? a.window : kNoWindow);
+                           QT, a.scale, scale_log2, a.window > 0 ? a.window : kNoWindow, a.slopes);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     return hipSuccess;

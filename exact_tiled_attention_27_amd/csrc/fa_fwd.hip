@@ -78,12 +78,15 @@ struct FwdShape {
 // in its chunk (causal) gets O = 0 and LSE = -inf there.
 // window (causal only): query i sees keys i - window + 1 .. i; tiles before
 // the workgroup's first such key are skipped (kNoWindow when there is none).
-template <int D, bool CAUSAL, int POLY, bool SPLIT>
+// BIAS: the linear position bias, slopes[hq] * (key - query) added to every
+// scaled score (added here to the raw score as slope / scale * (key - query),
+// before the mask and the row maximum, so everything after is unchanged).
+template <int D, bool CAUSAL, int POLY, bool SPLIT, bool BIAS = false>
 __global__ __launch_bounds__(512, FA_FWD_MIN_WAVES) void fwd_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, float *__restrict__ o, float *__restrict__ lse, int Hq,
     int Hkv, int N, int BH, int QT, float scale_log2, float tau, int window, int n_splits,
-    float *__restrict__ opart, float *__restrict__ lpart)
+    float *__restrict__ opart, float *__restrict__ lpart, const float *__restrict__ slopes)
 {
     using S = FwdShape<D>;
     __shared__ __attribute__((aligned(16))) char k_lds0[S::TILE_BYTES];
@@ -110,6 +113,7 @@ __global__ __launch_bounds__(512, FA_FWD_MIN_WAVES) void fwd_kernel(
     const int g = hq / (Hq / Hkv);
     const int q0 = qt * S::BM;
     const int qrow = q0 + wave * 32 + col;  // the query column this lane owns
+    const float bias_a = BIAS ? slopes[hq] * (kLog2e / scale_log2) : 0.f;  // slope / scale
 
     const int n_tiles_all = (N + S::BN - 1) / S::BN;
     const int n_tiles_q = CAUSAL ? min(n_tiles_all, (min(q0 + S::BM, N) + S::BN - 1) / S::BN)
@@ -211,6 +215,16 @@ __global__ __launch_bounds__(512, FA_FWD_MIN_WAVES) void fwd_kernel(
         }
     };
     auto scores = [&](f32x16(&st)[S::NKB], auto slot) { scores_with(st, slot, [](int) {}); };
+    // Raw scores of tile t += slope / scale * (key - query): per lane one
+    // base for the tile, per register a fixed key offset.
+    auto add_bias = [&](f32x16(&st)[S::NKB], int t) {
+        const float base = bias_a * (float)(t * S::BN + 4 * h - qrow);
+#pragma unroll
+        for (int kb = 0; kb < S::NKB; kb++)
+#pragma unroll
+            for (int r = 0; r < 16; r++)
+                st[kb][r] += __builtin_fmaf(bias_a, (float)(kb * 32 + 8 * (r >> 2) + (r & 3)), base);
+    };
     auto apply_mask = [&](f32x16(&st)[S::NKB], int t) {
 #pragma unroll
         for (int kb = 0; kb < S::NKB; kb++)
@@ -307,6 +321,7 @@ __global__ __launch_bounds__(512, FA_FWD_MIN_WAVES) void fwd_kernel(
         }
         exp_pack(cur, pf);
         pv(pf, Here{});
+        if (BIAS && NEXT) add_bias(nxt, t + 1);
         if (NEXT == 2 && (t + 1 >= n_full || t + 1 < w_full)) apply_mask(nxt, t + 1);
         if (NEXT) row_max_rescale(nxt);
     };
@@ -325,6 +340,7 @@ __global__ __launch_bounds__(512, FA_FWD_MIN_WAVES) void fwd_kernel(
 #pragma unroll
     for (int s = 0; s < S::KSTEPS; s++) settle(qf[s]);
     scores(sa, Slot0{});
+    if (BIAS) add_bias(sa, t_begin);
     if (n_full <= t_begin || t_begin < w_full) apply_mask(sa, t_begin);
     row_max_rescale(sa);
 
@@ -425,11 +441,13 @@ static hipError_t launch_fwd_split(const FwdArgs &a)
     auto kern = a.poly == 1 ? fwd_kernel<D, CAUSAL, 1, SPLIT>
               : a.poly == 4 ? fwd_kernel<D, CAUSAL, 4, SPLIT>
                             : fwd_kernel<D, CAUSAL, 0, SPLIT>;
+    // The bias has one instance: exponentials on v_exp_f32, one pass.
+    if (!SPLIT && a.slopes) kern = fwd_kernel<D, CAUSAL, 0, SPLIT, !SPLIT>;
     const int splits = SPLIT ? a.splits : 1;
     hipLaunchKernelGGL(kern, dim3(BH * QT * splits), dim3(S::THREADS), 0, a.stream,
                        (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v, a.o,
                        a.lse, a.Hq, a.Hkv, a.N, BH, QT, a.scale * kLog2e, a.tau,
-                       a.window > 0 ? a.window : kNoWindow, splits, a.opart, a.lpart);
+                       a.window > 0 ? a.window : kNoWindow, splits, a.opart, a.lpart, a.slopes);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !SPLIT) return e;
     const size_t rows = (size_t)BH * a.N;

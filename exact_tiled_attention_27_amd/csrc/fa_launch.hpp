@@ -19,6 +19,7 @@ struct FwdArgs {
     float *opart;  // splits > 1: partial O, [splits][B * Hq][N][d] fp32
     float *lpart;  // splits > 1: partial LSE, [splits][B * Hq][N] fp32
     hipStream_t stream;
+    const float *slopes = nullptr;  // linear position bias: slope per query head, [Hq] fp32
 };
 
 // How the backward sums dQ: fp32 atomics from the dK/dV kernel; a separate
@@ -44,6 +45,7 @@ struct BwdArgs {
     int mode;      // kBwdAtomic, kBwdSeparate or kBwdOrdered
     int window;    // causal sliding window in keys (0: none)
     hipStream_t stream;
+    const float *slopes = nullptr;  // linear position bias: slope per query head, [Hq] fp32
 };
 
 hipError_t launch_fwd(const FwdArgs &a);

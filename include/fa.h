@@ -37,7 +37,7 @@
  *     work is enqueued.  A launch failure returns FA_ERR_HIP; faults during
  *     execution surface at the caller's next synchronisation.
  *   - The environment variable FA_EXP2_POLY, read on every forward call
- *     (fa_fwd, fa_fwd_window, fa_fwd_splitkv),
+ *     (fa_fwd, fa_fwd_window, fa_fwd_splitkv, fa_fwd_alibi),
  *     moves forward exponentials from the transcendental unit to a cubic
  *     polynomial on the FMA units (page "FlashAttention-4", Key Contributions
  *     item 2): "1" all of them, "4" one in four; unset or any other value,
@@ -193,6 +193,40 @@ int fa_bwd_window(const void *q, const void *k, const void *v, const float *o, c
                   const void *dout, float *dq, float *dk, float *dv,
                   int B, int Hq, int Hkv, int N, int d, float scale, int window,
                   int deterministic, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Forward with a linear position bias: every scaled score gets
+ * slopes[h] * (j - i) added for query head h, query i and key j,
+ *   S_ij = scale * q_i . k_j + slopes[h] * (j - i),
+ * and O = softmax(S) v, LSE_i = ln sum_j exp(S_ij).  This is the additive
+ * score modification of the FlexAttention kind that the page
+ * "FlashAttention-4 Guide: Kernel Pipelining on Blackwell", section
+ * "Production Deployment Guide", points to for custom masks and biases (the
+ * pages give no formula; the ALiBi form, a fixed slope per head times the
+ * signed key - query distance, is the reading stated here).
+ *   slopes  fp32 [Hq], device memory, 4-byte aligned (read).  Non-finite
+ *           slopes give non-finite outputs; values are not checked.
+ * causal as in fa_fwd; other arguments and outputs as in fa_fwd.  The
+ * exponentials always run on the transcendental unit (FA_EXP2_POLY is
+ * ignored); FA_RESCALE_TAU applies.  slopes == NULL is FA_ERR_NULL.
+ * Returns an fa_status.
+ */
+int fa_fwd_alibi(const void *q, const void *k, const void *v, float *o, float *lse,
+                 const float *slopes, int B, int Hq, int Hkv, int N, int d, float scale,
+                 int causal, void *stream);
+
+/*
+ * Backward of fa_fwd_alibi (o and lse from fa_fwd_alibi with the same
+ * slopes and causal flag); P is recomputed with the bias, the gradient
+ * formulas are unchanged (the bias depends on neither q, k nor v).
+ * Arguments, workspace (fa_bwd_workspace_bytes) and dQ modes as in fa_bwd;
+ * slopes as in fa_fwd_alibi.
+ * Returns an fa_status.
+ */
+int fa_bwd_alibi(const void *q, const void *k, const void *v, const float *o, const float *lse,
+                 const void *dout, float *dq, float *dk, float *dv, const float *slopes,
+                 int B, int Hq, int Hkv, int N, int d, float scale, int causal,
+                 int deterministic, void *workspace, size_t workspace_bytes, void *stream);
 
 /* Static, human-readable name of a status code (never NULL). */
 const char *fa_status_string(int status);

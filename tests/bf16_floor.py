@@ -24,8 +24,9 @@ def _bf16(x):
     return _f64(f32_to_bf16_bits(np.asarray(x, dtype=np.float32)))
 
 
-def backward_emulation(q, k, v, dout, scale, causal, window=0, round_operands=True):
-    """dQ, dK, dV (float64) with P and dS rounded to bf16 when round_operands."""
+def backward_emulation(q, k, v, dout, scale, causal, window=0, round_operands=True, slopes=None):
+    """dQ, dK, dV (float64) with P and dS rounded to bf16 when round_operands.
+    slopes: per-query-head linear position bias slopes[h] * (j - i), or None."""
     qf, kf, vf, df = _f64(q), _f64(k), _f64(v), _f64(dout)
     B, Hq, N, d = qf.shape
     Hkv = kf.shape[1]
@@ -44,7 +45,10 @@ def backward_emulation(q, k, v, dout, scale, causal, window=0, round_operands=Tr
     for b in range(B):
         for h in range(Hq):
             g = h // grp
-            s = np.where(keep, sc * qf[b, h] @ kf[b, g].T, -np.inf)
+            s = sc * qf[b, h] @ kf[b, g].T
+            if slopes is not None:
+                s = s + slopes[h] * (j - i)
+            s = np.where(keep, s, -np.inf)
             p = np.exp(s - s.max(1, keepdims=True))
             p /= p.sum(1, keepdims=True)
             o = p @ vf[b, g]
@@ -58,10 +62,10 @@ def backward_emulation(q, k, v, dout, scale, causal, window=0, round_operands=Tr
     return {"dq": dq, "dk": dk, "dv": dv}
 
 
-def backward_bars(q, k, v, dout, scale, causal, ref, window=0, max_abs=1e-2):
+def backward_bars(q, k, v, dout, scale, causal, ref, window=0, max_abs=1e-2, slopes=None):
     """Max-abs bar per gradient: max_abs, or 1.25 x the bf16-operand floor
     (deviation of the emulation from the exact `ref`) where that is larger."""
-    emu = backward_emulation(q, k, v, dout, scale, causal, window)
+    emu = backward_emulation(q, k, v, dout, scale, causal, window, slopes=slopes)
     bars, floors = {}, {}
     for name in ("dq", "dk", "dv"):
         floors[name] = float(np.abs(emu[name] - ref[name]).max())

@@ -26,9 +26,9 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert names == ["fa_bwd", "fa_bwd_window", "fa_bwd_workspace_bytes", "fa_fwd",
-                     "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_bytes", "fa_fwd_window",
-                     "fa_status_string"]
+    assert names == ["fa_bwd", "fa_bwd_alibi", "fa_bwd_window", "fa_bwd_workspace_bytes",
+                     "fa_fwd", "fa_fwd_alibi", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_bytes",
+                     "fa_fwd_window", "fa_status_string"]
     out = subprocess.run(["nm", "-D", "--defined-only", fa.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\sT\s(\w+)$", out, flags=re.M))
@@ -209,3 +209,25 @@ def test_bwd_ordered_workspace_bytes():
     need = fa.fa_bwd_workspace_bytes(1, 2, 2, 128, 64, fa.BWD_ORDERED)
     assert bwd(deterministic=fa.BWD_ORDERED, workspace_bytes=need - 1) == 5
     assert bwd(deterministic=fa.BWD_ORDERED, workspace_bytes=need, dq=MIS) == 4
+
+
+def test_alibi_validates():
+    """The bias entry points need their slopes (FA_ERR_NULL; 4-byte alignment)
+    and otherwise check like fa_fwd / fa_bwd."""
+    args = dict(q=A, k=A, v=A, o=A, lse=A, slopes=A, B=1, Hq=2, Hkv=2, N=128, d=64,
+                scale=0.125, causal=1, stream=0)
+    assert fa.fa_fwd_alibi(**dict(args, slopes=None)) == 1
+    assert fa.fa_fwd_alibi(**dict(args, slopes=A + 2)) == 4
+    assert fa.fa_fwd_alibi(**dict(args, q=None)) == 1
+    assert fa.fa_fwd_alibi(**dict(args, Hq=3)) == 2
+    assert fa.fa_fwd_alibi(**dict(args, d=96)) == 3
+    assert fa.fa_fwd_alibi(**dict(args, o=MIS)) == 4
+    bargs = dict(q=A, k=A, v=A, o=A, lse=A, dout=A, dq=A, dk=A, dv=A, slopes=A, B=1, Hq=2,
+                 Hkv=2, N=128, d=64, scale=0.125, causal=0, deterministic=1, workspace=A,
+                 workspace_bytes=1 << 20, stream=0)
+    assert fa.fa_bwd_alibi(**dict(bargs, slopes=None)) == 1
+    assert fa.fa_bwd_alibi(**dict(bargs, slopes=A + 1)) == 4
+    assert fa.fa_bwd_alibi(**dict(bargs, dk=None)) == 1
+    assert fa.fa_bwd_alibi(**dict(bargs, deterministic=3)) == 2
+    assert fa.fa_bwd_alibi(**dict(bargs, workspace_bytes=16)) == 5
+    assert fa.fa_bwd_alibi(**dict(bargs, dv=MIS)) == 4

@@ -5,6 +5,7 @@ the 1e-2 bar (the case the floor-aware bar exists for)."""
 import math
 
 import numpy as np
+import pytest
 
 import oracle
 from bf16_floor import backward_bars, backward_emulation
@@ -31,3 +32,17 @@ def test_floor_exceeds_bar_on_the_smoke_input():
     bars, floors = backward_bars(q, k, v, do, scale, True, ref)
     assert floors["dv"] > 1e-2 and bars["dv"] == 1.25 * floors["dv"]
     assert floors["dk"] < 1e-2 and bars["dk"] == 1e-2
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_emulation_with_bias_equals_oracle_without_rounding(causal):
+    """The floor's emulation with the linear position bias, rounding off,
+    reproduces the oracle's biased gradients (numpy vs the C oracle)."""
+    B, Hq, Hkv, N, d = 1, 4, 2, 40, 16
+    q, k, v, do = (random_bf16((B, Hq, N, d), 31), random_bf16((B, Hkv, N, d), 32),
+                   random_bf16((B, Hkv, N, d), 33), random_bf16((B, Hq, N, d), 34))
+    a = np.array([0.5, -0.4, 0.1, 0.9])
+    ref = oracle.bwd(q, k, v, do, 0.25, causal, slopes=a)
+    emu = backward_emulation(q, k, v, do, 0.25, causal, round_operands=False, slopes=a)
+    for name in ("dq", "dk", "dv"):
+        np.testing.assert_allclose(emu[name], ref[name], rtol=1e-9, atol=1e-11)
