@@ -86,7 +86,9 @@ def time_launches(fn, reps, stream, warm_s=0.3):
 
 def per_config(fa, reps, dev, stream):
     """Forward (and, for the backward workload and the long-context GQA shape,
-    both backward modes) of each synthetic workload, timed on its own."""
+    every backward mode) of each synthetic workload, timed on its own; the
+    backward workload also times the linear-position-bias forward and
+    deterministic backward."""
     import numpy as np
     import torch
     from synth import WORKLOADS, make_inputs
@@ -135,6 +137,32 @@ def per_config(fa, reps, dev, stream):
                 name = {fa.BWD_SEPARATE: "fa_bwd deterministic", fa.BWD_ATOMIC: "fa_bwd atomic",
                         fa.BWD_ORDERED: "fa_bwd ordered"}[det]
                 row["calls"].append(entry(name, w.bwd_flops(), time_launches(bwd, reps, stream)))
+            if w.name == "fwdbwd_causal_n8192":
+                # The linear position bias on the same inputs, geometric
+                # slopes 2^(-8 (h + 1) / Hq); same nominal FLOP counts.
+                slopes = torch.tensor([2.0 ** (-8.0 * (h + 1) / Hq) for h in range(Hq)],
+                                      dtype=torch.float32, device=dev)
+
+                def fwd_b():
+                    st = fa.fa_fwd_alibi(q, k, v, o, lse, slopes, B, Hq, Hkv, N, d, w.scale,
+                                         w.causal, stream.cuda_stream)
+                    if st:
+                        raise fa.FAError(st, "fa_fwd_alibi")
+
+                row["calls"].append(entry("fa_fwd_alibi", w.fwd_flops(),
+                                          time_launches(fwd_b, reps, stream)))
+                wsb = fa.fa_bwd_workspace_bytes(B, Hq, Hkv, N, d, fa.BWD_SEPARATE)
+                ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+
+                def bwd_b():
+                    st = fa.fa_bwd_alibi(q, k, v, o, lse, do, dq, dk, dv, slopes, B, Hq, Hkv, N,
+                                         d, w.scale, w.causal, fa.BWD_SEPARATE, ws, wsb,
+                                         stream.cuda_stream)
+                    if st:
+                        raise fa.FAError(st, "fa_bwd_alibi")
+
+                row["calls"].append(entry("fa_bwd_alibi deterministic", w.bwd_flops(),
+                                          time_launches(bwd_b, reps, stream)))
         torch.cuda.synchronize()
         return row
 
@@ -284,11 +312,11 @@ def main():
     # dP is not counted).
     cz = "true" if w.causal else "false"
     if parts["fwd_ms_avg"] >= parts["bwd_deterministic_ms_avg"]:
-        rl_kernels = [f"fa::fwd_kernel<{d}, {cz}, 0, false>"]
+        rl_kernels = [f"fa::fwd_kernel<{d}, {cz}, 0, false, false>"]
         rl_flops, rl_ms = f_fwd, parts["fwd_ms_avg"]
     else:
-        rl_kernels = [f"fa::bwd_pre_kernel<{d}>", f"fa::bwd_dkdv_split_kernel<{d}, {cz}, 0>",
-                      f"fa::bwd_dq_kernel<{d}, {cz}>"]
+        rl_kernels = [f"fa::bwd_pre_kernel<{d}>", f"fa::bwd_dkdv_split_kernel<{d}, {cz}, 0, false>",
+                      f"fa::bwd_dq_kernel<{d}, {cz}, false>"]
         rl_flops, rl_ms = f_bwd, parts["bwd_deterministic_ms_avg"]
     achieved = rl_flops / (rl_ms * 1e-3) / 1e12
     roofline = {"bound": "mfma", "kernel": " + ".join(rl_kernels), "achieved": achieved,

@@ -24,7 +24,7 @@ def test_more_than_one_gpu_is_refused(argv, env):
 def test_stored_traffic_matches_workload_and_build():
     sys.path.insert(0, ROOT)
     import bench
-    kernels = ["fa::fwd_kernel<128, false, 0, false>"]
+    kernels = ["fa::fwd_kernel<128, false, 0, false, false>"]
     assert bench.measured_traffic(kernels, "some_other_workload") is None
     assert bench.measured_traffic(["fa::no_such_kernel<1>"], "fwd_n4096") is None
     with open(bench.TRAFFIC_FILE) as f:
@@ -35,3 +35,20 @@ def test_stored_traffic_matches_workload_and_build():
         assert got == pytest.approx(k["read_bytes"] + k["write_bytes"]) and got > 0
     else:
         assert got is None
+
+
+def test_roofline_kernels_are_in_the_stored_traffic():
+    """The names bench.py looks up for the dominant call are the ones the
+    profiler recorded for the current build (template arguments included)."""
+    sys.path.insert(0, ROOT)
+    import bench
+    with open(bench.TRAFFIC_FILE) as f:
+        stored = json.load(f)
+    for name in ("fa::fwd_kernel<128, false, 0, false, false>", "fa::bwd_pre_kernel<128>",
+                 "fa::bwd_dkdv_split_kernel<128, false, 0, false>",
+                 "fa::bwd_dq_kernel<128, false, false>"):
+        assert name in stored["kernels"], name
+    src = open(os.path.join(ROOT, "bench.py")).read()
+    assert 'f"fa::bwd_dkdv_split_kernel<{d}, {cz}, 0, false>"' in src
+    assert 'f"fa::bwd_dq_kernel<{d}, {cz}, false>"' in src
+    assert 'f"fa::fwd_kernel<{d}, {cz}, 0, false, false>"' in src
