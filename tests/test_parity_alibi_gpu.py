@@ -1,19 +1,21 @@
 """GPU parity of the linear position bias entry points (fa_fwd_alibi,
 fa_bwd_alibi) against the fp64 oracle with the same slopes, through the C ABI.
 
-Same bars, guard zones and NaN poisoning as the plain parity tests; the
-backward's max-abs bar is the floor-aware one of the plain tests
-(max(1e-2, 1.25 x the bf16-operand floor), tests/bf16_floor.py), because a
-strong bias concentrates the softmax on few keys and rounding exactly P and dS
-to bf16 already moves the gradients by about 1e-2 there.
-Slopes: the forward sweep (causal and not) draws them per query head from
-U[-0.6, 0.9) (negative slopes favour distant keys); the backward sweep
-(causal) and the long causal case use the geometric ALiBi sequence
-2^(-8 (h + 1) / Hq).  Where the bias makes the softmax nearly one-hot over
-many rows (steeper slopes, or a positive slope without the causal mask, which
-pulls every early row onto the last keys), the gradients measured 1.3-1.7 x
-the bf16-operand floor (max-abs 1.0-1.4e-2; dV mean-abs up to 1.07e-3, with
-dV's max error equal to its floor); those cases are not held to a bar here.
+Same guard zones and NaN poisoning as the plain parity tests.  O and LSE
+keep the plain bars.  The ragged backward sweep isolates the backward: it
+feeds the oracle's own O and LSE (rounded to fp32) to fa_bwd_alibi, so the
+expected result is exactly the oracle's gradients, and holds them to the
+floor-aware max-abs bar of the plain tests, max(1e-2, 1.25 x the floor of
+rounding exactly P and dS to bf16; tests/bf16_floor.py, which takes the
+bias), and the plain mean-abs bar.  A strong bias makes the softmax nearly
+one-hot, so dS is a small difference P (dP - D) and the bf16 operands alone
+move dK and dQ by about 1e-2; the backward kernels then sit at that floor.
+End to end (the kernel's own O, whose bf16-weighted P V product enters
+D = rowsum(dO * O)), such rows measured 1.27-1.45 x the floor; the long causal
+case below runs end to end with the geometric slopes and the plain bars.
+Slopes: per query head from U[-0.6, 0.9) (negative slopes favour distant
+keys) for the ragged sweeps, causal and not; the geometric ALiBi sequence
+2^(-8 (h + 1) / Hq) for the long causal case.
 """
 import math
 
@@ -95,7 +97,7 @@ def test_alibi_fwd_small(fa, N, d, causal):
     compare_lse(lse, lse_ref)
 
 
-BWD_SWEEP = [(n, d, True) for n in (3, 64, 129, 300, 600) for d in (64, 128)]
+BWD_SWEEP = [(n, d, c) for n in (3, 64, 129, 300, 600) for d in (64, 128) for c in (False, True)]
 
 
 @pytest.mark.parametrize("mode", [0, 1, 2])
@@ -105,11 +107,11 @@ def test_alibi_bwd_small(fa, N, d, causal, mode):
     note(f"alibi bwd B={B} Hq={Hq} Hkv={Hkv} N={N} d={d} causal={causal} mode={mode}")
     q, k, v, do = (random_bf16((B, Hq, N, d), 5 * N), random_bf16((B, Hkv, N, d), 5 * N + 1),
                    random_bf16((B, Hkv, N, d), 5 * N + 2), random_bf16((B, Hq, N, d), 5 * N + 3))
-    st, a = dev_slopes(alibi_slopes(Hq))
+    st, a = dev_slopes(sweep_slopes(Hq, N + 7))
     scale = 1 / math.sqrt(d)
-    o, lse = gpu_fwd_alibi(fa, q, k, v, st, scale, causal)
     ref = oracle.bwd(q, k, v, do, scale, causal, slopes=a)
-    dq, dk, dv = gpu_bwd_alibi(fa, q, k, v, do, o, lse, st, scale, causal, mode)
+    o32, lse32 = ref["o"].astype(np.float32), ref["lse"].astype(np.float32)
+    dq, dk, dv = gpu_bwd_alibi(fa, q, k, v, do, o32, lse32, st, scale, causal, mode)
     mean_bar = MEAN_ABS_FEW_TERMS if N < 64 else MEAN_ABS
     bars, floors = backward_bars(q, k, v, do, scale, causal, ref, slopes=a)
     for name, got in (("dq", dq), ("dk", dk), ("dv", dv)):
