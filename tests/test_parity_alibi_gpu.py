@@ -97,7 +97,7 @@ def test_alibi_fwd_small(fa, N, d, causal):
     compare_lse(lse, lse_ref)
 
 
-BWD_SWEEP = [(n, d, c) for n in (3, 64, 129, 300, 600) for d in (64, 128) for c in (False, True)]
+BWD_SWEEP = [(n, d, c) for n in (1, 3, 64, 129, 300, 600) for d in (64, 128) for c in (False, True)]
 
 
 @pytest.mark.parametrize("mode", [0, 1, 2])
