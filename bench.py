@@ -9,15 +9,17 @@ forward, the same count for both backward modes.
 Prints ONE JSON line.  Inputs are resident in HBM before the timed region; the
 region is bracketed by device synchronisation.  HIP events recorded on the
 launch stream around each call give per-call durations for the roofline.  The
-atomic-dQ backward is timed after the step loop and reported under "parts".
+atomic-dQ and ordered-dQ backward modes are timed after the step loop and
+reported under "parts".
 The fp64 CPU oracle is timed on a bounded sample (16 heads' forward and
 backward) of the same workload as a reported baseline.
 
 "per_config" then times each of the five synthetic workloads on its own
-(forward; both backward modes for the backward workload and for the
-long-context GQA shape): launches back
-to back after 0.3 s of untimed ones, an event pair around each launch, median
-and minimum reported.  --no-per-config skips it (profiling runs use that, so the
+(forward; the three dQ modes of the backward for the backward workload and for
+the long-context GQA shape; the linear-position-bias forward and deterministic
+backward on the backward workload's inputs): launches back to back after
+0.3 s of untimed ones, an event pair around each launch, median and minimum
+reported.  --no-per-config skips it (profiling runs use that, so the
 kernel averages cover the step's launches only).
 """
 import argparse
