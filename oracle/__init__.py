@@ -42,36 +42,12 @@ def _load():
     i64p = ctypes.POINTER(ctypes.c_int64)
     c_int, c_float, c_i64 = ctypes.c_int, ctypes.c_float, ctypes.c_int64
     lib.oracle_fwd_rows.argtypes = [u16p, u16p, u16p, c_int, c_int, c_int, c_int, c_int,
-                                    c_float, c_int, i64p, c_i64, f64p, f64p, c_int]
+                                    c_float, c_int, c_int, f64p, i64p, c_i64, f64p, f64p, c_int]
     lib.oracle_fwd_rows.restype = c_int
-    lib.oracle_fwd.argtypes = [u16p, u16p, u16p, f64p, f64p, c_int, c_int, c_int, c_int,
-                               c_int, c_float, c_int, c_int]
-    lib.oracle_fwd.restype = c_int
-    lib.oracle_bwd_groups.argtypes = [u16p, u16p, u16p, u16p, c_int, c_int, c_int, c_int,
-                                      c_int, c_float, c_int, i64p, c_i64, f64p, f64p, f64p,
-                                      f64p, f64p, c_int]
-    lib.oracle_bwd_groups.restype = c_int
-    lib.oracle_bwd_groups_tail.argtypes = [u16p, u16p, u16p, u16p, c_int, c_int, c_int, c_int,
-                                           c_int, c_float, c_int, c_int, i64p, c_i64, f64p, f64p,
-                                           f64p, f64p, f64p, c_int]
-    lib.oracle_bwd_groups_tail.restype = c_int
-    lib.oracle_fwd_rows_w.argtypes = [u16p, u16p, u16p, c_int, c_int, c_int, c_int, c_int,
-                                      c_float, c_int, c_int, i64p, c_i64, f64p, f64p, c_int]
-    lib.oracle_fwd_rows_w.restype = c_int
-    lib.oracle_fwd_w.argtypes = [u16p, u16p, u16p, f64p, f64p, c_int, c_int, c_int, c_int,
-                                 c_int, c_float, c_int, c_int, c_int]
-    lib.oracle_fwd_w.restype = c_int
-    lib.oracle_bwd_groups_tail_w.argtypes = [u16p, u16p, u16p, u16p, c_int, c_int, c_int, c_int,
-                                             c_int, c_float, c_int, c_int, c_int, i64p, c_i64,
-                                             f64p, f64p, f64p, f64p, f64p, c_int]
-    lib.oracle_bwd_groups_tail_w.restype = c_int
-    lib.oracle_fwd_rows_b.argtypes = [u16p, u16p, u16p, c_int, c_int, c_int, c_int, c_int,
-                                      c_float, c_int, c_int, f64p, i64p, c_i64, f64p, f64p, c_int]
-    lib.oracle_fwd_rows_b.restype = c_int
-    lib.oracle_bwd_groups_tail_b.argtypes = [u16p, u16p, u16p, u16p, c_int, c_int, c_int, c_int,
-                                             c_int, c_float, c_int, c_int, f64p, c_int, i64p,
-                                             c_i64, f64p, f64p, f64p, f64p, f64p, c_int]
-    lib.oracle_bwd_groups_tail_b.restype = c_int
+    lib.oracle_bwd_block.argtypes = [u16p, u16p, u16p, u16p, c_int, c_int, c_int, c_int, c_int,
+                                     c_float, c_int, c_int, f64p, c_int, c_int, c_int, c_int,
+                                     i64p, c_i64, f64p, f64p, f64p, f64p, f64p, c_int]
+    lib.oracle_bwd_block.restype = c_int
     _lib = lib
     return lib
 
@@ -135,14 +111,62 @@ def fwd_rows(q, k, v, scale, causal, rows, threads=None, window=0, slopes=None):
     o = np.empty((rows.size, d), np.float64)
     lse = np.empty((rows.size,), np.float64)
     keep, sp = _slopes(slopes, Hq)
-    st = lib.oracle_fwd_rows_b(_ptr(q, ctypes.c_uint16), _ptr(k, ctypes.c_uint16),
-                               _ptr(v, ctypes.c_uint16), B, Hq, Hkv, N, d, float(scale),
-                               int(bool(causal)), int(window), sp, _ptr(rows, ctypes.c_int64),
-                               rows.size, _ptr(o, ctypes.c_double), _ptr(lse, ctypes.c_double),
-                               threads or default_threads())
+    st = lib.oracle_fwd_rows(_ptr(q, ctypes.c_uint16), _ptr(k, ctypes.c_uint16),
+                             _ptr(v, ctypes.c_uint16), B, Hq, Hkv, N, d, float(scale),
+                             int(bool(causal)), int(window), sp, _ptr(rows, ctypes.c_int64),
+                             rows.size, _ptr(o, ctypes.c_double), _ptr(lse, ctypes.c_double),
+                             threads or default_threads())
     if st:
         raise RuntimeError(f"oracle_fwd_rows failed with status {st}")
     return o, lse
+
+
+def fwd_heads(q, k, v, scale, causal, heads, threads=None, window=0, slopes=None):
+    """Forward for whole heads.  heads: flat indices b*Hq + h.
+    Returns (O [n, N, d] f64, LSE [n, N] f64)."""
+    N = q.shape[2]
+    heads = np.asarray(heads, dtype=np.int64)
+    rows = (heads[:, None] * N + np.arange(N, dtype=np.int64)[None, :]).reshape(-1)
+    o, lse = fwd_rows(q, k, v, scale, causal, rows, threads, window, slopes)
+    return o.reshape(heads.size, N, q.shape[3]), lse.reshape(heads.size, N)
+
+
+def bwd_block(q, k, v, dout, scale, causal, groups, rows, keys, threads=None, window=0,
+              slopes=None):
+    """Backward of the selected key/value groups (flat index b*Hkv + g),
+    restricted to dQ (and O, LSE) for query rows rows[0] .. rows[1]-1 of each
+    of the group's heads and dK, dV for keys keys[0] .. keys[1]-1.  Each
+    entry equals the same slice of the whole backward, bit for bit.
+
+    Returns dict with dq [G, Hq/Hkv, R, d], dk [G, K, d], dv [G, K, d],
+    o [G, Hq/Hkv, R, d], lse [G, Hq/Hkv, R], all float64."""
+    lib = _load()
+    q, k, v, dout = _u16(q, "q"), _u16(k, "k"), _u16(v, "v"), _u16(dout, "dout")
+    B, Hq, Hkv, N, d = _shape(q, k, v)
+    if dout.shape != q.shape:
+        raise ValueError("dout must have q's shape")
+    r0, r1 = int(rows[0]), int(rows[1])
+    k0, k1 = int(keys[0]), int(keys[1])
+    groups = np.ascontiguousarray(groups, dtype=np.int64)
+    G, grp, R, K = groups.size, Hq // Hkv, r1 - r0, k1 - k0
+    out = {
+        "dq": np.empty((G, grp, R, d), np.float64),
+        "dk": np.empty((G, K, d), np.float64),
+        "dv": np.empty((G, K, d), np.float64),
+        "o": np.empty((G, grp, R, d), np.float64),
+        "lse": np.empty((G, grp, R), np.float64),
+    }
+    keep, sp = _slopes(slopes, Hq)
+    st = lib.oracle_bwd_block(
+        _ptr(q, ctypes.c_uint16), _ptr(k, ctypes.c_uint16), _ptr(v, ctypes.c_uint16),
+        _ptr(dout, ctypes.c_uint16), B, Hq, Hkv, N, d, float(scale), int(bool(causal)),
+        int(window), sp, r0, r1, k0, k1, _ptr(groups, ctypes.c_int64), G,
+        _ptr(out["dq"], ctypes.c_double), _ptr(out["dk"], ctypes.c_double),
+        _ptr(out["dv"], ctypes.c_double), _ptr(out["o"], ctypes.c_double),
+        _ptr(out["lse"], ctypes.c_double), threads or default_threads())
+    if st:
+        raise RuntimeError(f"oracle_bwd_block failed with status {st}")
+    return out
 
 
 def bwd_groups(q, k, v, dout, scale, causal, groups, threads=None, window=0, slopes=None):
@@ -150,65 +174,33 @@ def bwd_groups(q, k, v, dout, scale, causal, groups, threads=None, window=0, slo
 
     Returns dict with dq [G, Hq/Hkv, N, d], dk [G, N, d], dv [G, N, d],
     o [G, Hq/Hkv, N, d], lse [G, Hq/Hkv, N], all float64."""
-    lib = _load()
-    q, k, v, dout = _u16(q, "q"), _u16(k, "k"), _u16(v, "v"), _u16(dout, "dout")
-    B, Hq, Hkv, N, d = _shape(q, k, v)
-    if dout.shape != q.shape:
-        raise ValueError("dout must have q's shape")
-    groups = np.ascontiguousarray(groups, dtype=np.int64)
-    G, grp = groups.size, Hq // Hkv
-    out = {
-        "dq": np.empty((G, grp, N, d), np.float64),
-        "dk": np.empty((G, N, d), np.float64),
-        "dv": np.empty((G, N, d), np.float64),
-        "o": np.empty((G, grp, N, d), np.float64),
-        "lse": np.empty((G, grp, N), np.float64),
-    }
-    keep, sp = _slopes(slopes, Hq)
-    st = lib.oracle_bwd_groups_tail_b(
-        _ptr(q, ctypes.c_uint16), _ptr(k, ctypes.c_uint16), _ptr(v, ctypes.c_uint16),
-        _ptr(dout, ctypes.c_uint16), B, Hq, Hkv, N, d, float(scale), int(bool(causal)),
-        int(window), sp, 0, _ptr(groups, ctypes.c_int64), G, _ptr(out["dq"], ctypes.c_double),
-        _ptr(out["dk"], ctypes.c_double), _ptr(out["dv"], ctypes.c_double),
-        _ptr(out["o"], ctypes.c_double), _ptr(out["lse"], ctypes.c_double),
-        threads or default_threads())
-    if st:
-        raise RuntimeError(f"oracle_bwd_groups failed with status {st}")
-    return out
+    N = q.shape[2]
+    return bwd_block(q, k, v, dout, scale, causal, groups, (0, N), (0, N), threads, window,
+                     slopes)
 
 
 def bwd_groups_tail(q, k, v, dout, scale, row0, groups, threads=None, window=0, slopes=None):
     """Causal backward restricted to rows and keys row0 .. N-1 of the selected
-    groups (exact there: a key only receives gradient from later rows).
+    groups (a key there only receives gradient from later rows, whose forward
+    statistics still run over all their keys).
 
     Returns dict with dq [G, Hq/Hkv, N-row0, d], dk [G, N-row0, d],
     dv [G, N-row0, d], o [G, Hq/Hkv, N-row0, d], lse [G, Hq/Hkv, N-row0]."""
-    lib = _load()
-    q, k, v, dout = _u16(q, "q"), _u16(k, "k"), _u16(v, "v"), _u16(dout, "dout")
-    B, Hq, Hkv, N, d = _shape(q, k, v)
-    if dout.shape != q.shape:
-        raise ValueError("dout must have q's shape")
-    groups = np.ascontiguousarray(groups, dtype=np.int64)
-    G, grp, NT = groups.size, Hq // Hkv, N - int(row0)
-    out = {
-        "dq": np.empty((G, grp, NT, d), np.float64),
-        "dk": np.empty((G, NT, d), np.float64),
-        "dv": np.empty((G, NT, d), np.float64),
-        "o": np.empty((G, grp, NT, d), np.float64),
-        "lse": np.empty((G, grp, NT), np.float64),
-    }
-    keep, sp = _slopes(slopes, Hq)
-    st = lib.oracle_bwd_groups_tail_b(
-        _ptr(q, ctypes.c_uint16), _ptr(k, ctypes.c_uint16), _ptr(v, ctypes.c_uint16),
-        _ptr(dout, ctypes.c_uint16), B, Hq, Hkv, N, d, float(scale), 1, int(window), sp,
-        int(row0),
-        _ptr(groups, ctypes.c_int64), G, _ptr(out["dq"], ctypes.c_double),
-        _ptr(out["dk"], ctypes.c_double), _ptr(out["dv"], ctypes.c_double),
-        _ptr(out["o"], ctypes.c_double), _ptr(out["lse"], ctypes.c_double),
-        threads or default_threads())
-    if st:
-        raise RuntimeError(f"oracle_bwd_groups_tail failed with status {st}")
-    return out
+    N = q.shape[2]
+    return bwd_block(q, k, v, dout, scale, True, groups, (row0, N), (row0, N), threads, window,
+                     slopes)
+
+
+def bwd_groups_head(q, k, v, dout, scale, causal, n0, groups, threads=None, window=0,
+                    slopes=None):
+    """Backward restricted to rows and keys 0 .. n0-1 of the selected groups:
+    the first keys, whose gradients sum over every later row (the forward
+    statistics of all those rows are computed).
+
+    Returns dict with dq [G, Hq/Hkv, n0, d], dk [G, n0, d], dv [G, n0, d],
+    o [G, Hq/Hkv, n0, d], lse [G, Hq/Hkv, n0]."""
+    return bwd_block(q, k, v, dout, scale, causal, groups, (0, n0), (0, n0), threads, window,
+                     slopes)
 
 
 def bwd(q, k, v, dout, scale, causal, threads=None, window=0, slopes=None):

@@ -382,6 +382,43 @@ def test_bwd_tail_block_matches_full():
         oracle.bwd_groups_tail(q, k, v, dout, 0.3, N, [0])
 
 
+@pytest.mark.parametrize("causal,window,bias", [(True, 0, False), (False, 0, False),
+                                                (True, 7, False), (True, 0, True),
+                                                (False, 0, True)])
+def test_bwd_head_block_matches_full(causal, window, bias):
+    """Head block: rows and keys 0 .. n0-1, whose dK/dV sum over every later
+    row (the block computes the forward statistics of all of them), give
+    exactly the first n0 rows/keys of the full backward; so do blocks whose
+    rows and keys are different ranges."""
+    B, Hq, Hkv, N, d = 2, 4, 2, 41, 8
+    q, k, v = random_bf16((B, Hq, N, d), 171), random_bf16((B, Hkv, N, d), 172), random_bf16((B, Hkv, N, d), 173)
+    dout = random_bf16((B, Hq, N, d), 174)
+    slopes = np.array([0.3, -0.2, 0.05, 0.6]) if bias else None
+    full = oracle.bwd(q, k, v, dout, 0.3, causal, window=window, slopes=slopes)
+    pairs = [(0, 1), (1, 0)]  # (b, g) of the flat groups 1 and 2
+    for n0 in (1, 5, 16, 41):
+        head = oracle.bwd_groups_head(q, k, v, dout, 0.3, causal, n0, [1, 2], window=window,
+                                      slopes=slopes)
+        for t, (b, g) in enumerate(pairs):
+            np.testing.assert_array_equal(head["dq"][t], full["dq"][b, 2 * g:2 * g + 2, :n0])
+            np.testing.assert_array_equal(head["dk"][t], full["dk"][b, g, :n0])
+            np.testing.assert_array_equal(head["dv"][t], full["dv"][b, g, :n0])
+            np.testing.assert_array_equal(head["o"][t], full["o"][b, 2 * g:2 * g + 2, :n0])
+            np.testing.assert_array_equal(head["lse"][t], full["lse"][b, 2 * g:2 * g + 2, :n0])
+    for rows, keys in (((3, 19), (10, 30)), ((30, 41), (0, 4)), ((0, 41), (40, 41))):
+        blk = oracle.bwd_block(q, k, v, dout, 0.3, causal, [1, 2], rows, keys, window=window,
+                               slopes=slopes)
+        for t, (b, g) in enumerate(pairs):
+            np.testing.assert_array_equal(blk["dq"][t],
+                                          full["dq"][b, 2 * g:2 * g + 2, rows[0]:rows[1]])
+            np.testing.assert_array_equal(blk["dk"][t], full["dk"][b, g, keys[0]:keys[1]])
+            np.testing.assert_array_equal(blk["dv"][t], full["dv"][b, g, keys[0]:keys[1]])
+    with pytest.raises(RuntimeError):
+        oracle.bwd_block(q, k, v, dout, 0.3, causal, [0], (5, 5), (0, 4))
+    with pytest.raises(RuntimeError):
+        oracle.bwd_block(q, k, v, dout, 0.3, causal, [0], (0, 4), (3, N + 1))
+
+
 def test_rejects_bad_shapes():
     q = random_bf16((1, 3, 4, 4), 1)
     k = random_bf16((1, 2, 4, 4), 2)
