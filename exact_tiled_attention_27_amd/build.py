@@ -14,6 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfa.so")
+DEBUG_LIB = os.path.join(PKG, "libfa_debug.so")  # the same sources with event counters
 SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_bwd.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 OBJDIR = os.path.join(ROOT, "_build")
@@ -61,5 +62,17 @@ def build(verbose: bool = False, extra=(), out: str = LIB, tag: str = "") -> str
     return out
 
 
+def build_all(verbose: bool = False) -> None:
+    """libfa.so and the debug-counter build libfa_debug.so, side by side."""
+    with ThreadPoolExecutor(max_workers=2) as ex:
+        jobs = [ex.submit(build, verbose),
+                ex.submit(build, verbose, ("-DFA_DEBUG_COUNTERS=1",), DEBUG_LIB, "_dbg")]
+        for j in jobs:
+            j.result()
+
+
 if __name__ == "__main__":
-    print(build(verbose=True, extra=sys.argv[1:]))
+    if len(sys.argv) > 1:
+        print(build(verbose=True, extra=sys.argv[1:]))
+    else:
+        build_all(verbose=True)

@@ -2,6 +2,7 @@
 // workspace layout and dispatch to the gfx950 kernels.  Nothing here touches
 // the GPU before every argument has been checked.
 #include "fa.h"
+#include "fa_debug.h"
 
 #include <cmath>
 #include <cstdlib>
@@ -208,6 +209,14 @@ int fa_bwd_window(const void *q, const void *k, const void *v, const float *o, c
     return bwd_impl(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, N, d, scale, 1, window,
                     deterministic, workspace, workspace_bytes, stream);
 }
+
+#if FA_DEBUG_COUNTERS
+int fa_debug_counters(unsigned long long *counters, int n)
+{
+    if (!counters || n < 1) return FA_ERR_NULL;
+    return hip_status(fa::debug_counters(counters, n));
+}
+#endif
 
 int fa_fwd_alibi(const void *q, const void *k, const void *v, float *o, float *lse,
                  const float *slopes, int B, int Hq, int Hkv, int N, int d, float scale,

@@ -586,13 +586,19 @@ struct DqShape {
 
 // K and V tiles live in four separate LDS arrays (slot t % 2 of each), so
 // that reads of one slot never wait for the copies into the other.
-template <int D, bool CAUSAL, bool BIAS = false>
+// DELTA: instead of dQ, the row terms D_i = sum_j P_ij dP_ij from this
+// pass's own recomputed P and dP (written to delta_out; delta and dq are
+// unused).  Equal to sum_c dO_ic O_ic for the exact O; computed this way it
+// is consistent with the P the other backward kernels recompute, so
+// sum_j dS_ij = 0 holds to fp32 rounding even where the forward's O carries
+// the rounding of its bf16 P.
+template <int D, bool CAUSAL, bool BIAS = false, bool DELTA = false>
 __global__ __launch_bounds__(256, FA_DQ_MIN_WAVES) void bwd_dq_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, const uint16_t *__restrict__ dout,
     const float *__restrict__ lse2, const float *__restrict__ delta, float *__restrict__ dq,
     int Hq, int Hkv, int N, int BH, int QT, float scale, float scale_log2, int window,
-    const float *__restrict__ slopes)
+    const float *__restrict__ slopes, float *__restrict__ delta_out)
 {
     using S = DqShape<D>;
     __shared__ __attribute__((aligned(16))) char k_lds0[S::TILE];
@@ -627,7 +633,8 @@ __global__ __launch_bounds__(256, FA_DQ_MIN_WAVES) void bwd_dq_kernel(
     }
     const size_t prow = ((size_t)b * Hq + hq) * pad_rows(N) + qrow;  // padded workspace row
     const float l2 = qrow < N ? lse2[prow] : INFINITY;
-    const float dl = qrow < N ? delta[prow] : 0.f;
+    const float dl = (qrow < N && !DELTA) ? delta[prow] : 0.f;
+    float dsum[4] = {0.f, 0.f, 0.f, 0.f};  // DELTA: this lane's part of D, four chains
 
     // K and V row reads (A operands of S^T and dP^T): row 32 kb + col, chunk
     // 2 s + h.  K^T by transposing reads (A operand of dQ^T): keys
@@ -711,10 +718,19 @@ __global__ __launch_bounds__(256, FA_DQ_MIN_WAVES) void bwd_dq_kernel(
                     const bool dead = kk >= N || (CAUSAL && (kk > qrow || qrow - kk >= window));
                     x = dead ? -INFINITY : x;
                 }
-                dpt[r] = exp2_hw(x) * (dpt[r] - dl);
+                if (DELTA)
+                    dsum[r & 3] = __builtin_fmaf(exp2_hw(x), dpt[r], dsum[r & 3]);
+                else
+                    dpt[r] = exp2_hw(x) * (dpt[r] - dl);
             }
-            dsf[2 * kb] = pack_half(dpt, 0);
-            dsf[2 * kb + 1] = pack_half(dpt, 1);
+            if (!DELTA) {
+                dsf[2 * kb] = pack_half(dpt, 0);
+                dsf[2 * kb + 1] = pack_half(dpt, 1);
+            }
+        }
+        if constexpr (DELTA) {
+            dma_barrier();  // tile t + 1 landed; slot P is free
+            return;
         }
         // dQ^T += K^T dS^T (contraction over the tile's keys), transposing
         // reads two products ahead.
@@ -770,6 +786,11 @@ __global__ __launch_bounds__(256, FA_DQ_MIN_WAVES) void bwd_dq_kernel(
     }
     if (t < n_tiles) step(std::true_type{}, Slot0{}, t);
 
+    if constexpr (DELTA) {
+        const float dsum_all = halves_sum((dsum[0] + dsum[1]) + (dsum[2] + dsum[3]));
+        if (qrow < N && h == 0) delta_out[prow] = dsum_all;
+        return;
+    }
     if (qrow < N) {
         float *dqr = dq + (head_off + qrow) * D;
 #pragma unroll
@@ -801,6 +822,20 @@ static hipError_t launch_bwd_t(const BwdArgs &a)
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
+    if (a.slopes) {
+        // Linear position bias: D_i from the recomputed P and dP (see
+        // bwd_dq_kernel's DELTA), replacing the preprocess's sum_c dO_ic O_ic.
+        using S = DqShape<D>;
+        const int QT = (a.N + S::BM - 1) / S::BM;
+        hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, true, true>), dim3(BH * QT), dim3(S::THREADS),
+                           0, a.stream, (const uint16_t *)a.q, (const uint16_t *)a.k,
+                           (const uint16_t *)a.v, (const uint16_t *)a.dout, a.lse2,
+                           (const float *)nullptr, (float *)nullptr, a.Hq, a.Hkv, a.N, BH, QT,
+                           a.scale, scale_log2, a.window > 0 ? a.window : kNoWindow, a.slopes,
+                           a.delta);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     {
         using S = DkdvSplitShape<D>;
         const int KT = (a.N + S::BN - 1) / S::BN;
@@ -829,7 +864,8 @@ static hipError_t launch_bwd_t(const BwdArgs &a)
         hipLaunchKernelGGL(kern, dim3(BH * QT), dim3(S::THREADS), 0, a.stream,
                            (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v,
                            (const uint16_t *)a.dout, a.lse2, a.delta, a.dq, a.Hq, a.Hkv, a.N, BH,
-                           QT, a.scale, scale_log2, a.window > 0 ? a.window : kNoWindow, a.slopes);
+                           QT, a.scale, scale_log2, a.window > 0 ? a.window : kNoWindow, a.slopes,
+                           (float *)nullptr);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     return hipSuccess;

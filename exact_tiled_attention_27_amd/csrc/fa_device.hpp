@@ -51,6 +51,15 @@ __device__ __forceinline__ bf16x8 pack_half(const f32x16 &c, int j)
                        c[8 * j + 5], c[8 * j + 6], c[8 * j + 7]);
 }
 
+// acc + lo + hi for the two bf16 values packed in `pair` (bits 0-15 and
+// 16-31): one v_dot2c_f32_bf16 against (1.0, 1.0), products exact.
+__device__ __forceinline__ float sum_bf16_pair(uint32_t pair, float acc)
+{
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), ones, acc, false);
+}
+
 // LDS (address space 3) 16-byte reads at a byte offset.
 __device__ __forceinline__ bf16x8 lds_read_bf16x8(const char *lds, uint32_t byte_off)
 {

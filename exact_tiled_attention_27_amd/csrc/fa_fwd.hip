@@ -36,6 +36,19 @@
 
 namespace fa {
 
+#if FA_DEBUG_COUNTERS
+// Debug build only: event counters of the forward kernels (indices in
+// fa_launch.hpp, kDbg*), read and cleared by debug_counters().
+__device__ unsigned long long dbg_counters[kDbgCount];
+
+// Adds popcount(pred over the wave's lanes) to counter c (one atomic per wave).
+__device__ __forceinline__ void dbg_count(int c, bool pred, int lane)
+{
+    const unsigned long long n = __popcll(__ballot(pred));
+    if (lane == 0 && n) atomicAdd(&dbg_counters[c], n);
+}
+#endif
+
 template <int D>
 struct FwdShape {
     static constexpr int BM = 256;           // query rows per workgroup (32 per wave)
@@ -180,7 +193,8 @@ __global__ __launch_bounds__(512, FA_FWD_MIN_WAVES) void fwd_kernel(
 #pragma unroll
         for (int r = 0; r < 16; r++) acc[db][r] = 0.f;
     float m_ref = -INFINITY;  // reference maximum (base-2 domain) the exponent subtracts
-    float l_part = 0.f;       // this lane's part of the row sum
+    float l_part = 0.f;       // this lane's part of the row sum (fp32 p: the LSE)
+    float w_part = 0.f;       // ... of the bf16 weights P V applies (O's divisor)
 
 
     // K and V tiles have one shape, so one set of per-lane copy offsets.
@@ -246,10 +260,22 @@ __global__ __launch_bounds__(512, FA_FWD_MIN_WAVES) void fwd_kernel(
             for (int r = 0; r < 16; r++) mx = fmaxf(mx, st[kb][r]);
         const float mt = halves_max(mx) * scale_log2;  // scale_log2 > 0: max commutes
         const bool grow = mt > m_ref + tau;
+#if FA_DEBUG_COUNTERS
+        {
+            // One decision per live query row (lanes of the first half) and
+            // tile, once the row has a reference; rows that move it; waves
+            // that take the rescale branch for such a row.
+            const bool decided = h == 0 && qrow < N && m_ref != -INFINITY;
+            dbg_count(kDbgRowDecisions, decided, lane);
+            dbg_count(kDbgRowRescales, decided && grow, lane);
+            dbg_count(kDbgWaveRescales, lane == 0 && __any(decided && grow), lane);
+        }
+#endif
         if (__any(grow)) {
             const float alpha = grow ? exp2_hw(m_ref - mt) : 1.f;
             m_ref = grow ? mt : m_ref;
             l_part *= alpha;
+            w_part *= alpha;
 #pragma unroll
             for (int db = 0; db < S::DBLK; db++)
 #pragma unroll
@@ -257,11 +283,17 @@ __global__ __launch_bounds__(512, FA_FWD_MIN_WAVES) void fwd_kernel(
         }
     };
     // P = exp2(s * scale * log2 e - m), its fp32 row sum (four short add
-    // chains) and the bf16 B operands.  The sum uses the fp32 values: the
-    // log-sum-exp output must not inherit bf16 rounding on short rows.
+    // chains), the bf16 B operands, and the row sum of those bf16 values
+    // (one dot product with (1, 1) per pair).  The fp32 sum gives the
+    // log-sum-exp, which must not inherit bf16 rounding on short rows; the
+    // bf16 sum divides O, so that O is an exact weighted mean of V rows with
+    // the weights P V applied: a dominant key's rounding (up to 2^-9 of its
+    // weight, whose exponent may reach tau above the reference) cancels
+    // instead of scaling O.
     auto exp_pack = [&](f32x16(&st)[S::NKB], bf16x8(&pf)[S::KVSTEPS]) {
         const float msub = (m_ref == -INFINITY) ? 0.f : m_ref;
         float ls[4] = {0.f, 0.f, 0.f, 0.f};
+        float ws[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < S::NKB; kb++) {
 #pragma unroll
@@ -274,8 +306,15 @@ __global__ __launch_bounds__(512, FA_FWD_MIN_WAVES) void fwd_kernel(
             }
             pf[2 * kb] = pack_half(st[kb], 0);
             pf[2 * kb + 1] = pack_half(st[kb], 1);
+#pragma unroll
+            for (int j = 0; j < 2; j++) {
+                const u32x4 pairs = __builtin_bit_cast(u32x4, pf[2 * kb + j]);
+#pragma unroll
+                for (int e = 0; e < 4; e++) ws[e] = sum_bf16_pair(pairs[e], ws[e]);
+            }
         }
         l_part += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+        w_part += (ws[0] + ws[1]) + (ws[2] + ws[3]);
     };
     // O^T += V_t^T P_t^T.
     auto pv = [&](const bf16x8(&pf)[S::KVSTEPS], auto slot) {
@@ -329,6 +368,17 @@ __global__ __launch_bounds__(512, FA_FWD_MIN_WAVES) void fwd_kernel(
     using Full = std::integral_constant<int, 1>;
     using Any = std::integral_constant<int, 2>;
 
+#if FA_DEBUG_COUNTERS
+    // Key tiles this workgroup walks, and how many of them take the masked
+    // path (diagonal, tail and window-edge tiles).
+    if (tid == 0) {
+        atomicAdd(&dbg_counters[kDbgTiles], (unsigned long long)(n_tiles - t_begin));
+        int masked = 0;
+        for (int t = t_begin; t < n_tiles; t++) masked += (t >= n_full || t < w_full);
+        atomicAdd(&dbg_counters[kDbgMaskedTiles], (unsigned long long)masked);
+        atomicAdd(&dbg_counters[kDbgWorkgroups], 1ull);
+    }
+#endif
     // Prologue: K_0, V_0, K_1 copied while the Q loads are in flight (the
     // barrier drains both; the loads are settled right after it, so none is
     // still counted when the loop's copies start); S_0.
@@ -368,13 +418,14 @@ __global__ __launch_bounds__(512, FA_FWD_MIN_WAVES) void fwd_kernel(
         step(Last{}, Slot0{}, sa, sa, t);
     }
 
-    // Epilogue: O = O / l, LSE = (m + log2 l) * ln 2.
+    // Epilogue: O = O / w (the bf16 weights' sum), LSE = (m + log2 l) * ln 2.
     const float l_tot = halves_sum(l_part);
+    const float w_tot = halves_sum(w_part);
     if (SPLIT) {
         if (qrow < N) {
             const size_t prow = ((size_t)split * BH + bh) * N + qrow;
             float *orow = opart + prow * D;
-            const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;  // no valid key: O = 0
+            const float inv = w_tot > 0.f ? 1.f / w_tot : 0.f;  // no valid key: O = 0
 #pragma unroll
             for (int db = 0; db < S::DBLK; db++)
 #pragma unroll
@@ -387,7 +438,7 @@ __global__ __launch_bounds__(512, FA_FWD_MIN_WAVES) void fwd_kernel(
         }
         return;
     }
-    const float inv = 1.f / l_tot;
+    const float inv = 1.f / w_tot;
     if (qrow < N) {
         float *orow = o + (((size_t)b * Hq + hq) * N + qrow) * D;
 #pragma unroll
@@ -463,6 +514,17 @@ static hipError_t launch_fwd_t(const FwdArgs &a)
     (void)hipGetLastError();  // clear an error left by an earlier, unrelated call
     return a.splits > 1 ? launch_fwd_split<D, CAUSAL, true>(a) : launch_fwd_split<D, CAUSAL, false>(a);
 }
+
+#if FA_DEBUG_COUNTERS
+hipError_t debug_counters(unsigned long long *host, int n)
+{
+    unsigned long long zero[kDbgCount] = {};
+    hipError_t e = hipMemcpyFromSymbol(host, HIP_SYMBOL(dbg_counters),
+                                       sizeof(unsigned long long) * (n < kDbgCount ? n : kDbgCount));
+    if (e != hipSuccess) return e;
+    return hipMemcpyToSymbol(HIP_SYMBOL(dbg_counters), zero, sizeof zero);
+}
+#endif
 
 hipError_t launch_fwd(const FwdArgs &a)
 {

@@ -49,6 +49,24 @@ struct BwdArgs {
 };
 
 hipError_t launch_fwd(const FwdArgs &a);
+
+#ifndef FA_DEBUG_COUNTERS
+#define FA_DEBUG_COUNTERS 0
+#endif
+// Debug build (FA_DEBUG_COUNTERS=1) event counters of the forward kernels.
+enum {
+    kDbgRowDecisions = 0,  // rescale decisions: (row, tile) pairs after the row's first valid tile
+    kDbgRowRescales,       // ... of which moved the row's reference maximum
+    kDbgWaveRescales,      // waves that took the rescale branch for such a row
+    kDbgTiles,             // key tiles walked, summed over workgroups
+    kDbgMaskedTiles,       // ... of which took the masked path
+    kDbgWorkgroups,        // workgroups launched
+    kDbgCount
+};
+#if FA_DEBUG_COUNTERS
+// Copies min(n, kDbgCount) counters to host memory, then clears them.
+hipError_t debug_counters(unsigned long long *host, int n);
+#endif
 hipError_t launch_bwd(const BwdArgs &a);
 
 // Rescale threshold: log2(256) = 8 (conditional rescaling).
