@@ -46,7 +46,8 @@ def _load():
     lib.oracle_fwd_rows.restype = c_int
     lib.oracle_bwd_block.argtypes = [u16p, u16p, u16p, u16p, c_int, c_int, c_int, c_int, c_int,
                                      c_float, c_int, c_int, f64p, c_int, c_int, c_int, c_int,
-                                     i64p, c_i64, f64p, f64p, f64p, f64p, f64p, c_int]
+                                     i64p, c_i64, f64p, f64p, f64p, f64p, f64p, f64p, f64p,
+                                     ctypes.POINTER(c_int), c_int]
     lib.oracle_bwd_block.restype = c_int
     _lib = lib
     return lib
@@ -132,14 +133,16 @@ def fwd_heads(q, k, v, scale, causal, heads, threads=None, window=0, slopes=None
 
 
 def bwd_block(q, k, v, dout, scale, causal, groups, rows, keys, threads=None, window=0,
-              slopes=None):
+              slopes=None, stats=False):
     """Backward of the selected key/value groups (flat index b*Hkv + g),
     restricted to dQ (and O, LSE) for query rows rows[0] .. rows[1]-1 of each
     of the group's heads and dK, dV for keys keys[0] .. keys[1]-1.  Each
     entry equals the same slice of the whole backward, bit for bit.
 
     Returns dict with dq [G, Hq/Hkv, R, d], dk [G, K, d], dv [G, K, d],
-    o [G, Hq/Hkv, R, d], lse [G, Hq/Hkv, R], all float64."""
+    o [G, Hq/Hkv, R, d], lse [G, Hq/Hkv, R], all float64.  With stats=True
+    also stat_rows (s0, s1), stat_lse and stat_D [G, Hq/Hkv, s1 - s0]: LSE_i
+    and D_i = sum_c dO_ic O_ic of every row the block needed."""
     lib = _load()
     q, k, v, dout = _u16(q, "q"), _u16(k, "k"), _u16(v, "v"), _u16(dout, "dout")
     B, Hq, Hkv, N, d = _shape(q, k, v)
@@ -157,15 +160,31 @@ def bwd_block(q, k, v, dout, scale, causal, groups, rows, keys, threads=None, wi
         "lse": np.empty((G, grp, R), np.float64),
     }
     keep, sp = _slopes(slopes, Hq)
+    srange = np.zeros(2, np.int32)
+    stat_lse = stat_D = None
+    if stats:
+        # the widest the stat rows can be; trimmed once the range is known
+        stat_lse = np.empty((G, grp, N), np.float64)
+        stat_D = np.empty((G, grp, N), np.float64)
     st = lib.oracle_bwd_block(
         _ptr(q, ctypes.c_uint16), _ptr(k, ctypes.c_uint16), _ptr(v, ctypes.c_uint16),
         _ptr(dout, ctypes.c_uint16), B, Hq, Hkv, N, d, float(scale), int(bool(causal)),
         int(window), sp, r0, r1, k0, k1, _ptr(groups, ctypes.c_int64), G,
         _ptr(out["dq"], ctypes.c_double), _ptr(out["dk"], ctypes.c_double),
         _ptr(out["dv"], ctypes.c_double), _ptr(out["o"], ctypes.c_double),
-        _ptr(out["lse"], ctypes.c_double), threads or default_threads())
+        _ptr(out["lse"], ctypes.c_double),
+        _ptr(stat_lse, ctypes.c_double) if stats else None,
+        _ptr(stat_D, ctypes.c_double) if stats else None,
+        _ptr(srange, ctypes.c_int), threads or default_threads())
     if st:
         raise RuntimeError(f"oracle_bwd_block failed with status {st}")
+    if stats:
+        s0, s1 = int(srange[0]), int(srange[1])
+        ns = s1 - s0
+        # the C side wrote [G, grp, ns] contiguously at the start of each buffer
+        out["stat_rows"] = (s0, s1)
+        out["stat_lse"] = stat_lse.reshape(-1)[:G * grp * ns].reshape(G, grp, ns).copy()
+        out["stat_D"] = stat_D.reshape(-1)[:G * grp * ns].reshape(G, grp, ns).copy()
     return out
 
 
@@ -192,7 +211,7 @@ def bwd_groups_tail(q, k, v, dout, scale, row0, groups, threads=None, window=0, 
 
 
 def bwd_groups_head(q, k, v, dout, scale, causal, n0, groups, threads=None, window=0,
-                    slopes=None):
+                    slopes=None, stats=False):
     """Backward restricted to rows and keys 0 .. n0-1 of the selected groups:
     the first keys, whose gradients sum over every later row (the forward
     statistics of all those rows are computed).
@@ -200,7 +219,7 @@ def bwd_groups_head(q, k, v, dout, scale, causal, n0, groups, threads=None, wind
     Returns dict with dq [G, Hq/Hkv, n0, d], dk [G, n0, d], dv [G, n0, d],
     o [G, Hq/Hkv, n0, d], lse [G, Hq/Hkv, n0]."""
     return bwd_block(q, k, v, dout, scale, causal, groups, (0, n0), (0, n0), threads, window,
-                     slopes)
+                     slopes, stats)
 
 
 def bwd(q, k, v, dout, scale, causal, threads=None, window=0, slopes=None):

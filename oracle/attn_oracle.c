@@ -55,7 +55,8 @@
  *
  * Layout: row-major [B, H, N, d] for Q/K/V/dO/O/dQ/dK/dV, [B, H, N] for LSE.
  *
- * Build: gcc -O2 -fopenmp -ffp-contract=off -fPIC -shared (no fast-math).
+ * Build: gcc -O3 -fopenmp -ffp-contract=off -fPIC -shared (no fast-math; without
+ * contraction or reassociation, -O3 vectorises only element-wise loops).
  */
 #include <math.h>
 #include <stdint.h>
@@ -249,6 +250,9 @@ int oracle_fwd_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v, int
  *   dq [ngroups, Hq/Hkv, r1 - r0, d], o likewise, lse [ngroups, Hq/Hkv, r1 - r0]
  *   dk, dv [ngroups, k1 - k0, d]
  * (o, lse may be NULL).  r0 = k0 = 0, r1 = k1 = N is the whole backward.
+ * stat_lse and stat_D (each may be NULL) receive LSE_i and D_i of every row
+ * whose statistics the block computes, rows s0 .. s1 - 1 (defined below),
+ * [ngroups, Hq/Hkv, s1 - s0]; stat_range (may be NULL) receives s0 and s1.
  *
  * The forward statistics (m, l, O, D) are computed here for every row the
  * block needs: rows r0 .. r1 - 1, and every row that sees a key of
@@ -265,7 +269,8 @@ int oracle_bwd_block(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                      const uint16_t *dout, int B, int Hq, int Hkv, int N, int d, float scale,
                      int causal, int window, const double *slopes, int r0, int r1, int k0, int k1,
                      const int64_t *groups, int64_t ngroups, double *dq, double *dk, double *dv,
-                     double *o, double *lse, int nthreads)
+                     double *o, double *lse, double *stat_lse, double *stat_D, int *stat_range,
+                     int nthreads)
 {
     if (!q || !k || !v || !dout || !groups || !dq || !dk || !dv || ngroups < 0)
         return ORACLE_BAD_ARGS;
@@ -288,6 +293,10 @@ int oracle_bwd_block(const uint16_t *q, const uint16_t *k, const uint16_t *v,
     const int s1 = r1 > kr1 ? r1 : kr1;
     const int NS = s1 - s0, NR = r1 - r0, NK = k1 - k0;
     const size_t stat_rows = (size_t)group * NS;
+    if (stat_range) {
+        stat_range[0] = s0;
+        stat_range[1] = s1;
+    }
 
     double *m_buf = (double *)malloc(sizeof(double) * stat_rows);
     double *l_buf = (double *)malloc(sizeof(double) * stat_rows);
@@ -349,6 +358,8 @@ int oracle_bwd_block(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                 m_buf[rr] = m;
                 l_buf[rr] = l;
                 D_buf[rr] = Di;
+                if (stat_lse) stat_lse[(size_t)t * stat_rows + rr] = m + log(l);
+                if (stat_D) stat_D[(size_t)t * stat_rows + rr] = Di;
                 if (i < r0 || i >= r1) continue;
                 const size_t out = (size_t)hl * NR + (i - r0);
                 if (o_t) memcpy(o_t + out * d, oi, sizeof(double) * d);

@@ -18,10 +18,28 @@ A = 0x10000   # 16-byte-aligned fake address (never dereferenced: validation fai
 MIS = A + 4   # misaligned fake address
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(fa_[a-z_]+)\s*\(", text)))
+
+
+def exported(lib_path):
+    out = subprocess.run(["nm", "-D", "--defined-only", lib_path], capture_output=True,
+                         text=True, check=True).stdout
+    return set(re.findall(r"\sT\s(\w+)$", out, flags=re.M))
+
+
+def test_debug_build_exports_both_headers():
+    """libfa_debug.so (the event-counter build) exports every fa.h function
+    plus fa_debug.h's; the product library libfa.so has no counter entry."""
+    debug_lib = os.path.join(os.path.dirname(fa.LIB_PATH), "libfa_debug.so")
+    dbg_names = declared_functions(os.path.join(ROOT, "include", "fa_debug.h"))
+    assert dbg_names == ["fa_debug_counters"]
+    syms = exported(debug_lib)
+    for n in declared_functions() + dbg_names:
+        assert n in syms, n
+    assert "fa_debug_counters" not in exported(fa.LIB_PATH)
 
 
 def test_exports_every_declared_symbol():

@@ -46,3 +46,23 @@ def test_emulation_with_bias_equals_oracle_without_rounding(causal):
     emu = backward_emulation(q, k, v, do, 0.25, causal, round_operands=False, slopes=a)
     for name in ("dq", "dk", "dv"):
         np.testing.assert_allclose(emu[name], ref[name], rtol=1e-9, atol=1e-11)
+
+
+def test_head_block_floor_without_rounding_is_the_oracle(monkeypatch):
+    """The head-block emulation with the bf16 rounding switched off equals the
+    oracle's head block (its P, dS and sums are the same mathematics in
+    numpy), causal and not, GQA 2:1; with rounding its floor is nonzero."""
+    import bf16_floor
+    B, Hq, Hkv, N, d, n0 = 1, 4, 2, 150, 16, 40
+    q, k, v = random_bf16((B, Hq, N, d), 31), random_bf16((B, Hkv, N, d), 32), random_bf16((B, Hkv, N, d), 33)
+    do = random_bf16((B, Hq, N, d), 34)
+    for causal in (True, False):
+        ref = oracle.bwd_groups_head(q, k, v, do, 0.25, causal, n0, [0, 1], stats=True)
+        _, floors = bf16_floor.head_block_floor(q, k, v, do, 0.25, causal, [0, 1], n0, ref,
+                                                chunk=64)
+        assert all(f > 1e-5 for f in floors.values()), floors
+        monkeypatch.setattr(bf16_floor, "_bf16", lambda x: np.asarray(x, np.float64))
+        emu, floors = bf16_floor.head_block_floor(q, k, v, do, 0.25, causal, [0, 1], n0, ref,
+                                                  chunk=64)
+        monkeypatch.undo()
+        assert all(f < 1e-12 for f in floors.values()), floors

@@ -66,11 +66,13 @@ class Guarded:
 MEAN_ABS_FEW_TERMS = 2e-3  # N < 64 only (see the module docstring)
 
 
-def compare(name, got, ref, mean_bar=MEAN_ABS):
+def compare(name, got, ref, mean_bar=MEAN_ABS, max_bar=MAX_ABS):
     err = np.abs(got.astype(np.float64) - ref)
     mx, mean = float(err.max()), float(err.mean())
-    note(f"  {name}: max_abs={mx:.3e} mean_abs={mean:.3e} (|ref| max {np.abs(ref).max():.3f})")
-    assert mx <= MAX_ABS and mean <= mean_bar, f"{name}: max_abs {mx:.3e}, mean_abs {mean:.3e}"
+    bar = "" if max_bar == MAX_ABS else (f", floor-aware bar {max_bar:.3e}; flat 1e-2 bar "
+                                         f"{'met' if mx <= MAX_ABS else 'MISSED'}")
+    note(f"  {name}: max_abs={mx:.3e} mean_abs={mean:.3e} (|ref| max {np.abs(ref).max():.3f}{bar})")
+    assert mx <= max_bar and mean <= mean_bar, f"{name}: max_abs {mx:.3e}, mean_abs {mean:.3e}"
 
 
 def compare_lse(got, ref):
@@ -242,22 +244,33 @@ def sampled_rows(w, n_rows, seed):
 
 
 @pytest.mark.parametrize("name", ["fwd_small_d64", "fwd_n4096", "fwd_causal_rowscale_n8192",
-                                  "fwd_causal_gqa_n32768", "fwdbwd_causal_n8192"])
+                                  "fwdbwd_causal_n8192"])
 def test_workload_forward(fa, name):
+    """Every element of O and LSE at the workload's full size against the
+    oracle (max-abs and mean-abs over the whole tensor)."""
     w = WORKLOADS[name]
-    note(f"workload forward {name}")
+    note(f"workload forward {name} (whole tensors)")
     x = make_inputs(w)
     o, lse = gpu_fwd(fa, x["q"], x["k"], x["v"], w.scale, w.causal)
     assert np.isfinite(lse).all()
-    if w.B * w.Hq * w.N <= 1024:
-        o_ref, lse_ref = oracle.fwd(x["q"], x["k"], x["v"], w.scale, w.causal)
-        compare("o", o, o_ref)
-        compare_lse(lse, lse_ref)
-        return
-    rows = sampled_rows(w, 512, w.seed)
-    o_ref, lse_ref = oracle.fwd_rows(x["q"], x["k"], x["v"], w.scale, w.causal, rows)
-    compare("o (sampled rows)", o.reshape(-1, w.d)[rows], o_ref)
-    compare_lse(lse.reshape(-1)[rows], lse_ref)
+    o_ref, lse_ref = oracle.fwd(x["q"], x["k"], x["v"], w.scale, w.causal)
+    compare("o", o, o_ref)
+    compare_lse(lse, lse_ref)
+
+
+def test_workload_forward_long_context_gqa(fa):
+    """B1 Hq32 Hkv8 N32768 causal: four whole query heads, two from the first
+    KV group and two from the last (every row of each; mean-abs over the
+    complete heads)."""
+    w = WORKLOADS["fwd_causal_gqa_n32768"]
+    note(f"workload forward {w.name} (4 whole heads)")
+    x = make_inputs(w)
+    o, lse = gpu_fwd(fa, x["q"], x["k"], x["v"], w.scale, w.causal)
+    assert np.isfinite(lse).all()
+    heads = [0, 3, w.Hq - 4, w.Hq - 1]  # KV groups 0 and Hkv - 1
+    o_ref, lse_ref = oracle.fwd_heads(x["q"], x["k"], x["v"], w.scale, w.causal, heads)
+    compare("o (4 heads)", o.reshape(-1, w.N, w.d)[heads], o_ref)
+    compare_lse(lse.reshape(-1, w.N)[heads], lse_ref)
 
 
 @pytest.mark.parametrize("share", ["1", "4"])
@@ -299,6 +312,46 @@ def test_rescale_threshold_zero_and_eight_agree(fa, monkeypatch):
     assert float(np.abs(outs["0"][1] - outs["8"][1]).max()) <= 2e-3 * 20
 
 
+def planted_jump_inputs(jump, seed_k=5, seed_v=6, N=320, d=64, H=2):
+    """Scores of every row (base-2 units) are 0 for keys 0 .. 159 and `jump`
+    from key 160 on: q_i = e_0, scale * log2(e) = 1, K[:, 0] = 0 before key
+    160 and `jump` after, the other coordinates of K small noise."""
+    rng = np.random.default_rng(seed_k)
+    qf = np.zeros((1, H, N, d), np.float32)
+    qf[..., 0] = 1.0
+    kf = rng.uniform(-0.25, 0.25, size=(1, H, N, d)).astype(np.float32)
+    kf[..., 0] = 0.0
+    kf[..., 160:, 0] = jump
+    return (f32_to_bf16_bits(qf), f32_to_bf16_bits(kf), random_bf16((1, H, N, d), seed_v),
+            float(np.float32(math.log(2.0))))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_rescale_taken_only_above_threshold(fa, monkeypatch, causal):
+    """The reference maximum moves only when a tile's maximum exceeds it by
+    more than 8 (base 2).  On the planted-jump input the first tile sets the
+    reference to 0; tau = 1000 then never moves it.  At jump 7.875, tau = 8
+    must not move it either, so the two outputs are bit-identical; at 8.125
+    and 40.5, tau = 8 must move it (a reference moved by a non-integer amount
+    changes the rounding of every later exponent and bf16 P), so the outputs
+    differ.  (A jump by a whole number, 40, moves it by an exact power of two:
+    the rescaled sums are bit-identical to the unmoved ones, which the test
+    checks too.)  Both match the oracle."""
+    for jump, same in ((7.875, True), (8.125, False), (40.5, False), (40.0, True)):
+        q, k, v, scale = planted_jump_inputs(jump)
+        o_ref, lse_ref = oracle.fwd(q, k, v, scale, causal)
+        outs = {}
+        for tau in ("8", "1000"):
+            monkeypatch.setenv("FA_RESCALE_TAU", tau)
+            note(f"rescale skip: jump {jump} tau={tau} causal={causal}")
+            outs[tau] = gpu_fwd(fa, q, k, v, scale, causal)
+            compare("o", outs[tau][0], o_ref)
+            compare_lse(outs[tau][1], lse_ref)
+        eq = np.array_equal(outs["8"][0].view(np.uint32), outs["1000"][0].view(np.uint32))
+        note(f"  tau 8 vs 1000 bit-identical: {eq}")
+        assert eq == same, f"jump {jump}: tau 8 and tau 1000 outputs {'differ' if same else 'agree'}"
+
+
 @pytest.mark.parametrize("share", ["1", "4"])
 def test_workload_forward_exp2_polynomial(fa, monkeypatch, share):
     """Row-scaled causal workload (rescales taken) with polynomial exponentials."""
@@ -314,27 +367,24 @@ def test_workload_forward_exp2_polynomial(fa, monkeypatch, share):
 
 
 def test_workload_backward_both_modes(fa):
-    """Full-size causal backward: one key/value group per batch compared element
-    by element with the oracle in every dQ mode; the two reproducible modes must
-    repeat bit for bit; exact identities sum_j dK_j = 0 and sum_j dV_j =
-    sum_i dO_i checked on every group."""
+    """Full-size causal backward: every element of dQ, dK and dV against the
+    oracle in every dQ mode (all key/value groups); the two reproducible modes
+    must repeat bit for bit; exact identities sum_j dK_j = 0 and
+    sum_j dV_j = sum_i dO_i checked on every group."""
     w = WORKLOADS["fwdbwd_causal_n8192"]
-    note("workload backward fwdbwd_causal_n8192")
+    note("workload backward fwdbwd_causal_n8192 (whole tensors)")
     x = make_inputs(w)
     o, lse = gpu_fwd(fa, x["q"], x["k"], x["v"], w.scale, w.causal)
-    groups = [0, w.B * w.Hkv - 1]
-    ref = oracle.bwd_groups(x["q"], x["k"], x["v"], x["dout"], w.scale, w.causal, groups)
+    ref = oracle.bwd(x["q"], x["k"], x["v"], x["dout"], w.scale, w.causal)
     grp = w.Hq // w.Hkv
     results = {}
     for det in MODES:
         note(f"  deterministic={det}")
         dq, dk, dv = gpu_bwd(fa, x["q"], x["k"], x["v"], x["dout"], o, lse, w.scale, w.causal, det)
         results[det] = (dq, dk, dv)
-        for t, gflat in enumerate(groups):
-            b, g = divmod(gflat, w.Hkv)
-            compare(f"dq[{b},{g}]", dq[b, g * grp:(g + 1) * grp], ref["dq"][t])
-            compare(f"dk[{b},{g}]", dk[b, g], ref["dk"][t])
-            compare(f"dv[{b},{g}]", dv[b, g], ref["dv"][t])
+        compare("dq", dq, ref["dq"])
+        compare("dk", dk, ref["dk"])
+        compare("dv", dv, ref["dv"])
         dsum = dk.astype(np.float64).sum(2)
         scale_k = np.abs(dk).astype(np.float64).sum(2)
         note(f"  max |sum_j dK_j| / sum_j |dK_j| = {float((np.abs(dsum) / scale_k).max()):.2e}")
@@ -384,18 +434,32 @@ def test_ordered_mode_repeats_across_xcds(fa, causal):
 
 def test_long_context_gqa_backward(fa):
     """Backward at the long-context GQA shape (B1 Hq32 Hkv8 N32768 d128,
-    causal), every dQ mode.  Element by element against the oracle on the
-    causal tail block (rows and keys N-256 .. N-1 of the first and last KV
-    group: exact there, since a key only receives gradient from later rows);
+    causal), every dQ mode.  Element by element against the oracle on two
+    blocks of the first and last KV group:
+      - the head block, rows and keys 0 .. 255: these keys' dK and dV sum
+        over all 4 x 32768 (head, row) pairs of the group, the longest sums
+        of the whole backward (the oracle computes every row's statistics);
+      - the causal tail block, rows and keys N-256 .. N-1 (each tail row's
+        dQ sums over all of its keys);
     the exact identities on every group; the reproducible modes repeat bit for
-    bit."""
+    bit.  The head block's max-abs bar is floor-aware (as for the smoke input):
+    rounding exactly P and dS to bf16, and nothing else, moves these long sums
+    by about 1e-2 (tests/bf16_floor.py, head_block_floor)."""
+    from bf16_floor import head_block_floor
     w = replace(WORKLOADS["fwd_causal_gqa_n32768"], backward=True)
     note("long-context GQA backward")
     x = make_inputs(w)
     o, lse = gpu_fwd(fa, x["q"], x["k"], x["v"], w.scale, w.causal)
     row0 = w.N - 256
     groups = [0, w.B * w.Hkv - 1]
+    note("  oracle: tail and head blocks")
     ref = oracle.bwd_groups_tail(x["q"], x["k"], x["v"], x["dout"], w.scale, row0, groups)
+    head = oracle.bwd_groups_head(x["q"], x["k"], x["v"], x["dout"], w.scale, True, 256, groups,
+                                  stats=True)
+    _, floors = head_block_floor(x["q"], x["k"], x["v"], x["dout"], w.scale, True, groups, 256,
+                                 head)
+    bars = {n: max(MAX_ABS, 1.25 * f) for n, f in floors.items()}
+    note(f"  head block bf16-operand floors {floors}")
     grp = w.Hq // w.Hkv
     dof = (x["dout"].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     want_dv = dof.reshape(w.B, w.Hkv, grp, w.N, w.d).sum((2, 3))
@@ -409,6 +473,10 @@ def test_long_context_gqa_backward(fa):
             compare(f"dq[{b},{g}] tail", dq[b, g * grp:(g + 1) * grp, row0:], ref["dq"][t])
             compare(f"dk[{b},{g}] tail", dk[b, g, row0:], ref["dk"][t])
             compare(f"dv[{b},{g}] tail", dv[b, g, row0:], ref["dv"][t])
+            compare(f"dq[{b},{g}] head", dq[b, g * grp:(g + 1) * grp, :256], head["dq"][t],
+                    max_bar=bars["dq"])
+            compare(f"dk[{b},{g}] head", dk[b, g, :256], head["dk"][t], max_bar=bars["dk"])
+            compare(f"dv[{b},{g}] head", dv[b, g, :256], head["dv"][t], max_bar=bars["dv"])
         dsum = dk.astype(np.float64).sum(2)
         scale_k = np.abs(dk).astype(np.float64).sum(2)
         assert (np.abs(dsum) <= 1e-3 * scale_k + 1e-3).all()
@@ -649,7 +717,8 @@ def test_bf16_operand_floor_case(fa, deterministic):
     note(f"  floors {floors}")
     for name, got in (("dq", dq), ("dk", dk), ("dv", dv)):
         err = np.abs(got.astype(np.float64) - ref[name])
-        note(f"  {name}: max_abs={err.max():.3e} (bar {bars[name]:.3e}) mean_abs={err.mean():.3e}")
+        note(f"  {name}: max_abs={err.max():.3e} (bar {bars[name]:.3e}; flat 1e-2 bar "
+             f"{'met' if err.max() <= 1e-2 else 'MISSED'}) mean_abs={err.mean():.3e}")
         assert err.max() <= bars[name] and err.mean() <= MEAN_ABS, name
 
 
