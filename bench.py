@@ -1,18 +1,21 @@
 """Throughput of exact tiled attention (forward + backward) on one MI355X.
 
-One step = the whole path over one batch: fa_fwd (O, LSE) then fa_bwd (dQ, dK,
-dV; deterministic dQ pass) on the B=4, Hq=Hkv=16, N=4096, d=128 non-causal
-bf16 workload (iid N(0,1) inputs, dO drawn after V).  FLOPs are counted
-nominally: forward 4*B*Hq*N^2*d (halved when causal), backward 2.5x the
-forward, the same count for both backward modes.
+One step = the whole path over one batch of the causal forward + backward
+workload (B=2, Hq=Hkv=16, N=8192, d=128, bf16 iid N(0,1) Q, K, V, dO):
+fa_fwd (O, LSE), then fa_bwd in both dQ modes the workload names: the
+deterministic separate dQ pass and the atomic dQ.  FLOPs are counted
+nominally: forward 4*B*Hq*N^2*d, halved when causal; each backward 2.5x the
+forward, the same count for every dQ mode.  The step's value is
+(forward + 2 backward) nominal FLOPs over the step time.
 
 Prints ONE JSON line.  Inputs are resident in HBM before the timed region; the
 region is bracketed by device synchronisation.  HIP events recorded on the
 launch stream around each call give per-call durations for the roofline.  The
-atomic-dQ and ordered-dQ backward modes are timed after the step loop and
-reported under "parts".
-The fp64 CPU oracle is timed on a bounded sample (16 heads' forward and
-backward) of the same workload as a reported baseline.
+ordered-dQ backward mode is timed after the step loop and reported under
+"parts".
+The fp64 CPU oracle is timed on bounded samples of every workload (whole
+heads of the forward; whole key/value groups of the backward) as a reported
+baseline.
 
 "per_config" then times each of the five synthetic workloads on its own
 (forward; the three dQ modes of the backward for the backward workload and for
@@ -37,24 +40,35 @@ PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
 
-def library_sha256():
-    """Hash of the libfa.so this process loads, to tell whether the stored
-    counters were taken with the same compiled kernels."""
+def source_sha256():
+    """Hash of the kernel sources and build flags (not of the binary, whose
+    bytes depend on the checkout path): the stored counters stay valid
+    exactly as long as the code they measured does."""
     import hashlib
-    with open(os.path.join(ROOT, "exact_tiled_attention_27_amd", "libfa.so"), "rb") as fh:
-        return hashlib.sha256(fh.read()).hexdigest()
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "_fa_build", os.path.join(ROOT, "exact_tiled_attention_27_amd", "build.py"))
+    b = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(b)
+    h = hashlib.sha256(" ".join(b.FLAGS[:-2]).encode())
+    csrc = os.path.join(ROOT, "exact_tiled_attention_27_amd", "csrc")
+    paths = [os.path.join(csrc, n) for n in sorted(os.listdir(csrc))]
+    for path in paths + [os.path.join(ROOT, "include", "fa.h")]:
+        with open(path, "rb") as fh:
+            h.update(os.path.basename(path).encode() + b"\0" + fh.read())
+    return h.hexdigest()
 
 
 def measured_traffic(kernels, workload):
     """HBM bytes per launch (read + write) of `kernels` from the rocprofv3
     FETCH_SIZE / WRITE_SIZE passes stored in profiles/, or None when they were
-    taken on another workload or with another build of the library."""
+    taken on another workload or with other kernel sources."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("workload") != workload or t.get("library_sha256") != library_sha256():
+    if t.get("workload") != workload or t.get("source_sha256") != source_sha256():
         return None
     try:
         return sum(t["kernels"][k]["read_bytes"] + t["kernels"][k]["write_bytes"] for k in kernels)
@@ -178,16 +192,61 @@ def per_config(fa, reps, dev, stream):
     return rows
 
 
+def cpu_baseline(x_head, threads):
+    """The fp64 oracle, as it stands, on bounded samples of every workload:
+    whole heads of each forward and whole key/value groups of the backward
+    workload, with the inputs those workloads draw.  The headline figure is
+    the backward workload's sample (forward + backward); the others are
+    listed per workload.  About 20 s on 16 host cores."""
+    import numpy as np
+    import oracle
+    from synth import WORKLOADS, make_inputs
+    per = []
+    head = None
+    samples = {"fwd_small_d64": 2, "fwd_n4096": 16, "fwd_causal_rowscale_n8192": 8,
+               "fwd_causal_gqa_n32768": 4, "fwdbwd_causal_n8192": 16}
+    for name, n_heads in samples.items():
+        w = WORKLOADS[name]
+        x = x_head if name == "fwdbwd_causal_n8192" else make_inputs(w)
+        heads = list(range(n_heads))
+        t0 = time.perf_counter()
+        oracle.fwd_heads(x["q"], x["k"], x["v"], w.scale, w.causal, heads, threads=threads)
+        secs = time.perf_counter() - t0
+        flops = w.fwd_flops() * n_heads / (w.B * w.Hq)
+        row = {"workload": name, "call": "forward", "heads": n_heads, "of_heads": w.B * w.Hq,
+               "seconds": secs, "tflops": flops / secs / 1e12}
+        per.append(row)
+        if w.backward:
+            groups = list(range(n_heads))   # Hq == Hkv: one head per group
+            t0 = time.perf_counter()
+            oracle.bwd_groups(x["q"], x["k"], x["v"], x["dout"], w.scale, w.causal, groups,
+                              threads=threads)
+            bsecs = time.perf_counter() - t0
+            # bwd_groups also recomputes the forward of its groups
+            bflops = (w.fwd_flops() + w.bwd_flops()) * len(groups) / (w.B * w.Hkv)
+            per.append({"workload": name, "call": "forward+backward", "groups": len(groups),
+                        "of_groups": w.B * w.Hkv, "seconds": bsecs,
+                        "tflops": bflops / bsecs / 1e12})
+            head = (bflops / bsecs / 1e12, len(groups), w.B * w.Hkv, bsecs)
+        del x
+    value, ng, of, secs = head
+    return {"value": value, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"fp64 forward+backward of {ng} of {of} key/value groups of "
+                      f"fwdbwd_causal_n8192 (same inputs), {secs:.1f} s; per_workload lists "
+                      f"whole-head forward samples of every workload",
+            "per_workload": per}
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=40)
-    p.add_argument("--workload", default="fwd_n4096")
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default="fwdbwd_causal_n8192")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--atomic-reps", type=int, default=10,
-                   help="timed launches of the atomic-dQ and ordered-dQ backward reported under "
-                        "parts (0: skip)")
+    p.add_argument("--ordered-reps", type=int, default=10,
+                   help="timed launches of the ordered-dQ backward reported under parts "
+                        "(0: skip)")
     p.add_argument("--no-per-config", action="store_true",
                    help="skip timing each synthetic workload on its own")
     p.add_argument("--per-config-reps", type=int, default=10)
@@ -201,14 +260,15 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this benchmark runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "this benchmark runs on one GPU only: every workload of "
+                                   "the attention hot path fits one MI355X, so --gpus must be 1"}))
         sys.exit(2)
 
     import numpy as np
     import torch
 
     import exact_tiled_attention_27_amd as fa
-    from synth import WORKLOADS, make_inputs, random_bf16
+    from synth import WORKLOADS, make_inputs
     from dataclasses import replace
 
     w = WORKLOADS[args.workload]
@@ -246,6 +306,8 @@ def main():
         if st:
             raise fa.FAError(st, "fa_bwd")
 
+    calls = [("fwd", fwd), ("bwd_deterministic", lambda: bwd(fa.BWD_SEPARATE)),
+             ("bwd_atomic", lambda: bwd(fa.BWD_ATOMIC))]
     print(f"bench: workload {w.name} ({w.note}); warmup {args.warmup}, steps {args.steps}",
           file=sys.stderr, flush=True)
     if args.copy_calibration:
@@ -255,76 +317,75 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     for _ in range(args.warmup):
-        fwd()
-        bwd(1)
+        for _, fn in calls:
+            fn()
     torch.cuda.synchronize()
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
+          for _ in range(args.steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record(stream)
     for i in range(args.steps):
         ev[i][0].record(stream)
-        fwd()
-        ev[i][1].record(stream)
-        bwd(1)
-        ev[i][2].record(stream)
+        for j, (_, fn) in enumerate(calls):
+            fn()
+            ev[i][j + 1].record(stream)
     t_end.record(stream)
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
-    fwd_ms = [e[0].elapsed_time(e[1]) for e in ev]
-    bwd_ms = [e[1].elapsed_time(e[2]) for e in ev]
     ms_step = total_ms / args.steps
     f_fwd, f_bwd = w.fwd_flops(), w.bwd_flops()
-    value = (f_fwd + f_bwd) / (ms_step * 1e-3) / 1e12
+    flops = {"fwd": f_fwd, "bwd_deterministic": f_bwd, "bwd_atomic": f_bwd}
+    value = (f_fwd + 2 * f_bwd) / (ms_step * 1e-3) / 1e12
 
-    parts = {
-        "fwd_ms_avg": float(np.mean(fwd_ms)),
-        "fwd_ms_min": float(np.min(fwd_ms)),
-        "fwd_tflops": f_fwd / (np.mean(fwd_ms) * 1e-3) / 1e12,
-        "bwd_deterministic_ms_avg": float(np.mean(bwd_ms)),
-        "bwd_deterministic_ms_min": float(np.min(bwd_ms)),
-        "bwd_deterministic_tflops": f_bwd / (np.mean(bwd_ms) * 1e-3) / 1e12,
-    }
-    parts["fwd_frac_peak"] = parts["fwd_tflops"] / PEAK_BF16_TFLOPS
-    parts["bwd_deterministic_frac_peak"] = parts["bwd_deterministic_tflops"] / PEAK_BF16_TFLOPS
+    parts = {}
+    for j, (name, _) in enumerate(calls):
+        ms = [e[j].elapsed_time(e[j + 1]) for e in ev]
+        parts[f"{name}_ms_avg"] = float(np.mean(ms))
+        parts[f"{name}_ms_min"] = float(np.min(ms))
+        parts[f"{name}_tflops"] = flops[name] / (np.mean(ms) * 1e-3) / 1e12
+        parts[f"{name}_frac_peak"] = parts[f"{name}_tflops"] / PEAK_BF16_TFLOPS
 
-    # The other two dQ modes of the same backward, back to back after one
-    # untimed call each.
-    for mode, key in ((fa.BWD_ATOMIC, "atomic"), (fa.BWD_ORDERED, "ordered")):
-        if args.atomic_reps <= 0:
-            break
+    # The third dQ mode of the same backward, back to back after one untimed
+    # call.
+    if args.ordered_reps > 0:
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        bwd(mode)
+        bwd(fa.BWD_ORDERED)
         torch.cuda.synchronize()
         e0.record(stream)
-        for _ in range(args.atomic_reps):
-            bwd(mode)
+        for _ in range(args.ordered_reps):
+            bwd(fa.BWD_ORDERED)
         e1.record(stream)
         torch.cuda.synchronize()
-        at_ms = e0.elapsed_time(e1) / args.atomic_reps
-        parts[f"bwd_{key}_ms_avg"] = at_ms
-        parts[f"bwd_{key}_tflops"] = f_bwd / (at_ms * 1e-3) / 1e12
+        at_ms = e0.elapsed_time(e1) / args.ordered_reps
+        parts["bwd_ordered_ms_avg"] = at_ms
+        parts["bwd_ordered_tflops"] = f_bwd / (at_ms * 1e-3) / 1e12
 
-    # Roofline of the dominant launch.  fa_fwd is one kernel; fa_bwd
-    # (deterministic) is a short preprocess kernel, the dK/dV kernel and the dQ
-    # kernel, timed together by the events around the call.  Algorithmic work
-    # is the nominal count of each call (the dQ pass's recomputation of S and
-    # dP is not counted).
+    # Roofline of the dominant launch: the call of the step that takes the
+    # longest.  fa_fwd is one kernel; fa_bwd is a short preprocess kernel and
+    # the dK/dV kernel (atomic mode: with the dQ atomics), plus the dQ kernel
+    # in deterministic mode, timed together by the events around the call.
+    # Algorithmic work is the nominal count of the call (the dQ pass's
+    # recomputation of S and dP is not counted).
     cz = "true" if w.causal else "false"
-    if parts["fwd_ms_avg"] >= parts["bwd_deterministic_ms_avg"]:
-        rl_kernels = [f"fa::fwd_kernel<{d}, {cz}, 0, false, false>"]
-        rl_flops, rl_ms = f_fwd, parts["fwd_ms_avg"]
-    else:
-        rl_kernels = [f"fa::bwd_pre_kernel<{d}>", f"fa::bwd_dkdv_split_kernel<{d}, {cz}, 0, false>",
-                      f"fa::bwd_dq_kernel<{d}, {cz}, false>"]
-        rl_flops, rl_ms = f_bwd, parts["bwd_deterministic_ms_avg"]
-    achieved = rl_flops / (rl_ms * 1e-3) / 1e12
-    roofline = {"bound": "mfma", "kernel": " + ".join(rl_kernels), "achieved": achieved,
-                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                "traffic": measured_traffic(rl_kernels, w.name), "traffic_unit": "bytes",
-                "flops_per_launch": rl_flops, "avg_launch_ms": rl_ms}
+    kernels = {
+        "fwd": [f"fa::fwd_kernel<{d}, {cz}, 0, false, false>"],
+        "bwd_deterministic": [f"fa::bwd_pre_kernel<{d}>",
+                              f"fa::bwd_dkdv_split_kernel<{d}, {cz}, 0, false>",
+                              f"fa::bwd_dq_kernel<{d}, {cz}, false, false>"],
+        "bwd_atomic": [f"fa::bwd_pre_kernel<{d}>",
+                       f"fa::bwd_dkdv_split_kernel<{d}, {cz}, 1, false>"],
+    }
+    dom = max((name for name, _ in calls), key=lambda n: parts[f"{n}_ms_avg"])
+    rl_ms = parts[f"{dom}_ms_avg"]
+    achieved = flops[dom] / (rl_ms * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "call": dom, "kernel": " + ".join(kernels[dom]),
+                "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / PEAK_BF16_TFLOPS,
+                "traffic": measured_traffic(kernels[dom], w.name), "traffic_unit": "bytes",
+                "flops_per_launch": flops[dom], "avg_launch_ms": rl_ms}
 
     configs = None
     if not args.no_per_config:
@@ -333,20 +394,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
-        threads = oracle.default_threads()
-        # Sample: the forward and backward of the first 16 (batch, kv-head)
-        # groups, about 10 s on 16 host cores.
-        groups = list(range(min(16, B * Hkv)))
-        t0 = time.perf_counter()
-        oracle.bwd_groups(x["q"], x["k"], x["v"], x["dout"], w.scale, w.causal, groups,
-                          threads=threads)
-        secs = time.perf_counter() - t0
-        heads = len(groups) * (Hq // Hkv)
-        sample_flops = (f_fwd + f_bwd) * heads / (B * Hq)
-        cpu = {"value": sample_flops / secs / 1e12, "unit": "TFLOP/s", "cores": threads,
-               "kind": "oracle",
-               "sample": f"fp64 forward+backward of {heads} of {B * Hq} heads "
-                         f"(N={N}, d={d}, same inputs); {secs:.1f} s"}
+        cpu = cpu_baseline(x, oracle.default_threads())
 
     out = {
         "metric": "attention fwd/bwd TFLOP/s (bf16, d=128) and % of MI355X bf16 MFMA peak",
@@ -355,8 +403,9 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "frac_peak": value / PEAK_BF16_TFLOPS,
         "config": {"workload": w.name, "B": B, "Hq": Hq, "Hkv": Hkv, "N": N, "d": d,
-                   "causal": w.causal, "step": "fa_fwd + fa_bwd (deterministic dQ)",
-                   "flops_per_step": f_fwd + f_bwd},
+                   "causal": w.causal,
+                   "step": "fa_fwd + fa_bwd (deterministic dQ) + fa_bwd (atomic dQ)",
+                   "flops_per_step": f_fwd + 2 * f_bwd},
         "parts": parts,
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -12,9 +12,9 @@
       conflicts, transcendental share) from --pmc passes
 
 Only the attention kernels (names in namespace fa::) and the calibration copy
-are reported.  The JSON written by `traffic` carries a hash of the built
-library (libfa.so); bench.py reports the stored traffic only while that hash
-matches the library it loads.
+are reported.  The JSON written by `traffic` carries a hash of the kernel
+sources and build flags; bench.py reports the stored traffic only while that
+hash matches the sources it runs.
 """
 import argparse
 import collections
@@ -85,13 +85,12 @@ def cmd_stats(a):
     write(a.out, out)
 
 
-def library_sha256():
-    """Hash of the built libfa.so the counters were taken with.  The build is
-    deterministic, and comments do not reach the binary, so the stored
-    traffic stays valid exactly as long as the compiled kernels do."""
-    import hashlib
-    with open(os.path.join(ROOT, "exact_tiled_attention_27_amd", "libfa.so"), "rb") as fh:
-        return hashlib.sha256(fh.read()).hexdigest()
+def source_sha256():
+    """Hash of the kernel sources and build flags the counters were taken
+    with (bench.py's key for the stored traffic)."""
+    sys.path.insert(0, ROOT)
+    import bench
+    return bench.source_sha256()
 
 
 def cmd_traffic(a):
@@ -109,7 +108,7 @@ def cmd_traffic(a):
             continue
         res[k] = {"read_bytes": mean(fk) * 1024 * ff, "write_bytes": mean(wk) * 1024 * wf,
                   "launches": min(len(fk), len(wk))}
-    js = {"workload": a.workload, "library_sha256": library_sha256(),
+    js = {"workload": a.workload, "source_sha256": source_sha256(),
           "calibration": {"kernel": COPY_KERNEL, "bytes_read_and_written": COPY_BYTES,
                           "fetch_size_kib": f_copy, "write_size_kib": w_copy,
                           "fetch_factor": ff, "write_factor": wf},

@@ -21,34 +21,59 @@ def test_more_than_one_gpu_is_refused(argv, env):
     assert "one GPU" in msg["error"]
 
 
-def test_stored_traffic_matches_workload_and_build():
+def test_stored_traffic_matches_workload_and_sources():
     sys.path.insert(0, ROOT)
     import bench
-    kernels = ["fa::fwd_kernel<128, false, 0, false, false>"]
-    assert bench.measured_traffic(kernels, "some_other_workload") is None
-    assert bench.measured_traffic(["fa::no_such_kernel<1>"], "fwd_n4096") is None
     with open(bench.TRAFFIC_FILE) as f:
         stored = json.load(f)
-    got = bench.measured_traffic(kernels, "fwd_n4096")
-    if stored["library_sha256"] == bench.library_sha256():
+    workload = stored["workload"]
+    kernels = sorted(stored["kernels"])[:1]
+    assert bench.measured_traffic(kernels, "some_other_workload") is None
+    assert bench.measured_traffic(["fa::no_such_kernel<1>"], workload) is None
+    got = bench.measured_traffic(kernels, workload)
+    if stored.get("source_sha256") == bench.source_sha256():
         k = stored["kernels"][kernels[0]]
         assert got == pytest.approx(k["read_bytes"] + k["write_bytes"]) and got > 0
     else:
         assert got is None
 
 
+def test_source_hash_ignores_the_checkout_path(tmp_path):
+    """The traffic key hashes the kernel sources and flags, not the binary
+    (whose bytes depend on where the library was built)."""
+    import shutil
+    sys.path.insert(0, ROOT)
+    import bench
+    for sub in ("exact_tiled_attention_27_amd/csrc", "include"):
+        shutil.copytree(os.path.join(ROOT, sub), tmp_path / sub)
+    shutil.copy(os.path.join(ROOT, "exact_tiled_attention_27_amd", "build.py"),
+                tmp_path / "exact_tiled_attention_27_amd" / "build.py")
+    shutil.copy(os.path.join(ROOT, "bench.py"), tmp_path / "bench.py")
+    code = "import bench; print(bench.source_sha256())"
+    r = subprocess.run([sys.executable, "-c", code], cwd=tmp_path, capture_output=True,
+                       text=True, timeout=120, env={**os.environ, "PYTHONPATH": str(tmp_path)})
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.strip() == bench.source_sha256()
+
+
 def test_roofline_kernels_are_in_the_stored_traffic():
-    """The names bench.py looks up for the dominant call are the ones the
-    profiler recorded for the current build (template arguments included)."""
+    """The names bench.py looks up for each call of its step are the ones the
+    profiler recorded (template arguments included), when the stored counters
+    are for the bench's default workload."""
     sys.path.insert(0, ROOT)
     import bench
     with open(bench.TRAFFIC_FILE) as f:
         stored = json.load(f)
-    for name in ("fa::fwd_kernel<128, false, 0, false, false>", "fa::bwd_pre_kernel<128>",
-                 "fa::bwd_dkdv_split_kernel<128, false, 0, false>",
-                 "fa::bwd_dq_kernel<128, false, false>"):
-        assert name in stored["kernels"], name
     src = open(os.path.join(ROOT, "bench.py")).read()
-    assert 'f"fa::bwd_dkdv_split_kernel<{d}, {cz}, 0, false>"' in src
-    assert 'f"fa::bwd_dq_kernel<{d}, {cz}, false>"' in src
-    assert 'f"fa::fwd_kernel<{d}, {cz}, 0, false, false>"' in src
+    for pat in ('f"fa::bwd_dkdv_split_kernel<{d}, {cz}, 0, false>"',
+                'f"fa::bwd_dkdv_split_kernel<{d}, {cz}, 1, false>"',
+                'f"fa::bwd_dq_kernel<{d}, {cz}, false, false>"',
+                'f"fa::fwd_kernel<{d}, {cz}, 0, false, false>"', 'f"fa::bwd_pre_kernel<{d}>"'):
+        assert pat in src, pat
+    if stored["workload"] != "fwdbwd_causal_n8192":
+        pytest.skip("stored counters are for another workload")
+    for name in ("fa::fwd_kernel<128, true, 0, false, false>", "fa::bwd_pre_kernel<128>",
+                 "fa::bwd_dkdv_split_kernel<128, true, 0, false>",
+                 "fa::bwd_dkdv_split_kernel<128, true, 1, false>",
+                 "fa::bwd_dq_kernel<128, true, false, false>"):
+        assert name in stored["kernels"], name
