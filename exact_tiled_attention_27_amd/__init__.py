@@ -2,8 +2,9 @@
 
 The functions fa_fwd, fa_fwd_window, fa_fwd_splitkv,
 fa_fwd_splitkv_workspace_bytes, fa_fwd_alibi, fa_bwd, fa_bwd_window,
-fa_bwd_alibi, fa_bwd_workspace_bytes and fa_status_string mirror the C ABI in include/fa.h one for one; this module only marshals arguments (device pointers, sizes, the
-current HIP stream).  Every step of the computation runs in the library's HIP
+fa_bwd_alibi, fa_bwd_noalloc, fa_bwd_workspace_bytes and fa_status_string
+mirror the C ABI in include/fa.h one for one; this module only marshals
+arguments (device pointers, sizes, the current HIP stream).  Every step of the computation runs in the library's HIP
 kernels; there is no fallback path, and importing this package fails if
 libfa.so has not been built.
 
@@ -15,13 +16,15 @@ import math
 import os
 
 __all__ = ["fa_fwd", "fa_fwd_window", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_bytes",
-           "fa_fwd_alibi", "fa_bwd_alibi", "fa_bwd", "fa_bwd_window", "fa_bwd_workspace_bytes", "fa_status_string", "FAError",
+           "fa_fwd_alibi", "fa_bwd_alibi", "fa_bwd", "fa_bwd_window", "fa_bwd_noalloc",
+           "fa_bwd_workspace_bytes", "fa_status_string", "FAError",
            "attention_fwd", "attention_bwd", "LIB_PATH", "STATUS", "MAX_SPLITS",
-           "BWD_ATOMIC", "BWD_SEPARATE", "BWD_ORDERED"]
+           "NOALLOC_MAX_WORKSPACE", "BWD_ATOMIC", "BWD_SEPARATE", "BWD_ORDERED"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
 MAX_SPLITS = 64  # FA_MAX_SPLITS
+NOALLOC_MAX_WORKSPACE = 32 << 20  # FA_NOALLOC_MAX_WORKSPACE (bytes)
 
 # dQ modes of fa_bwd's `deterministic` argument (FA_BWD_ATOMIC, FA_BWD_SEPARATE,
 # FA_BWD_ORDERED); False and True select the first two.
@@ -58,6 +61,9 @@ _lib.fa_fwd_splitkv_workspace_bytes.restype = _sz
 _lib.fa_bwd.argtypes = [_vp, _vp, _vp, _fp, _fp, _vp, _fp, _fp, _fp, _i, _i, _i, _i, _i, _f,
                         _i, _i, _vp, _sz, _vp]
 _lib.fa_bwd.restype = _i
+_lib.fa_bwd_noalloc.argtypes = [_vp, _vp, _vp, _fp, _fp, _vp, _fp, _fp, _fp, _i, _i, _i, _i, _i,
+                                _f, _i, _i, _vp]
+_lib.fa_bwd_noalloc.restype = _i
 _lib.fa_bwd_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i]
 _lib.fa_bwd_workspace_bytes.restype = _sz
 _lib.fa_fwd_alibi.argtypes = [_vp, _vp, _vp, _fp, _fp, _fp, _i, _i, _i, _i, _i, _f, _i, _vp]
@@ -158,6 +164,15 @@ def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, N, d, scale, causal, d
                        _addr(dq), _addr(dk), _addr(dv), B, Hq, Hkv, N, d, float(scale),
                        int(bool(causal)), int(deterministic), _addr(workspace),
                        int(workspace_bytes), _stream(stream, q, dq))
+
+
+def fa_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, N, d, scale, causal,
+                   deterministic, stream=None) -> int:
+    """C ABI fa_bwd_noalloc (workspace in the library's static device array).
+    Status out."""
+    return _lib.fa_bwd_noalloc(_addr(q), _addr(k), _addr(v), _addr(o), _addr(lse), _addr(dout),
+                               _addr(dq), _addr(dk), _addr(dv), B, Hq, Hkv, N, d, float(scale),
+                               int(bool(causal)), int(deterministic), _stream(stream, q, dq))
 
 
 def _dims(q, k):

@@ -200,6 +200,29 @@ int fa_bwd(const void *q, const void *k, const void *v, const float *o, const fl
                     deterministic, workspace, workspace_bytes, stream);
 }
 
+int fa_bwd_noalloc(const void *q, const void *k, const void *v, const float *o,
+                   const float *lse, const void *dout, float *dq, float *dk, float *dv, int B,
+                   int Hq, int Hkv, int N, int d, float scale, int causal, int deterministic,
+                   void *stream)
+{
+    static_assert(fa::kNoAllocScratchBytes == FA_NOALLOC_MAX_WORKSPACE, "fa.h limit");
+    // Every argument check of fa_bwd first, so that nothing touches the
+    // device before they pass.
+    if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL;
+    int st = check_common(B, Hq, Hkv, N, d, scale);
+    if (st != FA_OK) return st;
+    if (deterministic < FA_BWD_ATOMIC || deterministic > FA_BWD_ORDERED) return FA_ERR_SHAPE;
+    const void *ptrs[] = {q, k, v, o, lse, dout, dq, dk, dv};
+    for (const void *p : ptrs)
+        if (!aligned16(p)) return FA_ERR_ALIGN;
+    const size_t need = fa_bwd_workspace_bytes(B, Hq, Hkv, N, d, deterministic);
+    if (need > fa::kNoAllocScratchBytes) return FA_ERR_WORKSPACE;
+    void *ws = nullptr;
+    if (fa::noalloc_scratch(&ws) != hipSuccess) return FA_ERR_HIP;
+    return bwd_impl(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, N, d, scale, causal, 0,
+                    deterministic, ws, fa::kNoAllocScratchBytes, stream);
+}
+
 int fa_bwd_window(const void *q, const void *k, const void *v, const float *o, const float *lse,
                   const void *dout, float *dq, float *dk, float *dv, int B, int Hq, int Hkv,
                   int N, int d, float scale, int window, int deterministic, void *workspace,

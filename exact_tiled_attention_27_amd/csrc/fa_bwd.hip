@@ -33,6 +33,7 @@
 // compiler never drains them before unrelated LDS reads) into per-slot LDS
 // arrays; each kernel settles its own global loads before the first copy and
 // waits for the copies at its step barriers.
+#include <mutex>
 #include <type_traits>
 
 #include "fa_device.hpp"
@@ -868,6 +869,32 @@ static hipError_t launch_bwd_t(const BwdArgs &a)
                            (float *)nullptr);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
+    return hipSuccess;
+}
+
+// Backward workspace of fa_bwd_noalloc, for callers that cannot allocate
+// device memory: one copy of this array per device, held until the process
+// ends.  Host code never uses its name as an address: the device address
+// comes from hipGetSymbolAddress, looked up once per device.
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+hipError_t noalloc_scratch(void **ptr)
+{
+    static std::mutex mu;
+    static void *addr[kMaxDevices] = {};
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
     return hipSuccess;
 }
 

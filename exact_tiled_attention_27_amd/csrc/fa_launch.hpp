@@ -69,6 +69,13 @@ hipError_t debug_counters(unsigned long long *host, int n);
 #endif
 hipError_t launch_bwd(const BwdArgs &a);
 
+// fa_bwd_noalloc's workspace: a static device array of this many bytes per
+// device (FA_NOALLOC_MAX_WORKSPACE in fa.h); devices 0 .. kMaxDevices - 1.
+constexpr size_t kNoAllocScratchBytes = (size_t)32 << 20;
+constexpr int kMaxDevices = 64;
+// Device address of the current device's array (looked up on its first use).
+hipError_t noalloc_scratch(void **ptr);
+
 // Rescale threshold: log2(256) = 8 (conditional rescaling).
 constexpr float kRescaleTau = 8.0f;
 

@@ -31,7 +31,9 @@
  *     LSE_i = ln sum_j exp(scale * q_i . k_j).
  *   - The caller owns every buffer; the library allocates no device memory,
  *     keeps no state between calls and may be called concurrently on
- *     different streams with disjoint outputs.
+ *     different streams with disjoint outputs.  The one exception is
+ *     fa_bwd_noalloc, whose workspace is a static device array of the
+ *     library shared by all its calls on a device (see there).
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
  *     without any host synchronisation.  Argument errors return before any
  *     work is enqueued.  A launch failure returns FA_ERR_HIP; faults during
@@ -182,6 +184,32 @@ int fa_bwd(const void *q, const void *k, const void *v, const float *o, const fl
            const void *dout, float *dq, float *dk, float *dv,
            int B, int Hq, int Hkv, int N, int d, float scale, int causal, int deterministic,
            void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * fa_bwd without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The same kernels and results as fa_bwd
+ * with the same dQ mode (the reproducible modes give the same bits); the
+ * workspace fa_bwd would take lives instead in a static device array of the
+ * library, FA_NOALLOC_MAX_WORKSPACE bytes on every device it runs on, held
+ * until the process ends.  The call allocates nothing; its first call on a
+ * device looks the array's address up (hipGetSymbolAddress).
+ *   Limit: fa_bwd_workspace_bytes(B, Hq, Hkv, N, d, deterministic) must not
+ *     exceed FA_NOALLOC_MAX_WORKSPACE (about 4 million rows B * Hq * N,
+ *     e.g. B = 1, Hq = 32, N = 131072); otherwise FA_ERR_WORKSPACE, before
+ *     anything is enqueued.
+ *   Every call on one device shares that device's array: calls that overlap
+ *   in time on one device (different streams, or different host threads
+ *   without ordering) race and give wrong results.  Calls ordered on one
+ *   stream are safe; each call rewrites all of the array it uses.
+ * Other arguments as in fa_bwd.  A failed address lookup is FA_ERR_HIP.
+ * Returns an fa_status.
+ */
+#define FA_NOALLOC_MAX_WORKSPACE ((size_t)32 << 20)
+int fa_bwd_noalloc(const void *q, const void *k, const void *v, const float *o,
+                   const float *lse, const void *dout, float *dq, float *dk, float *dv,
+                   int B, int Hq, int Hkv, int N, int d, float scale, int causal,
+                   int deterministic, void *stream);
 
 /*
  * Backward of fa_fwd_window (same band; o and lse from fa_fwd_window with the

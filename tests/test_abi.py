@@ -44,9 +44,9 @@ def test_debug_build_exports_both_headers():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert names == ["fa_bwd", "fa_bwd_alibi", "fa_bwd_window", "fa_bwd_workspace_bytes",
-                     "fa_fwd", "fa_fwd_alibi", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_bytes",
-                     "fa_fwd_window", "fa_status_string"]
+    assert names == ["fa_bwd", "fa_bwd_alibi", "fa_bwd_noalloc", "fa_bwd_window",
+                     "fa_bwd_workspace_bytes", "fa_fwd", "fa_fwd_alibi", "fa_fwd_splitkv",
+                     "fa_fwd_splitkv_workspace_bytes", "fa_fwd_window", "fa_status_string"]
     out = subprocess.run(["nm", "-D", "--defined-only", fa.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\sT\s(\w+)$", out, flags=re.M))
@@ -249,3 +249,20 @@ def test_alibi_validates():
     assert fa.fa_bwd_alibi(**dict(bargs, deterministic=3)) == 2
     assert fa.fa_bwd_alibi(**dict(bargs, workspace_bytes=16)) == 5
     assert fa.fa_bwd_alibi(**dict(bargs, dv=MIS)) == 4
+
+
+def test_noalloc_checks_arguments_before_the_device():
+    """fa_bwd_noalloc refuses bad arguments, and a workspace beyond
+    FA_NOALLOC_MAX_WORKSPACE, before any HIP call (fake aligned addresses)."""
+    base = dict(q=A, k=A, v=A, o=A, lse=A, dout=A, dq=A, dk=A, dv=A, B=1, Hq=64, Hkv=64,
+                N=131072, d=128, scale=0.1, causal=1, deterministic=1)
+    need = fa.fa_bwd_workspace_bytes(1, 64, 64, 131072, 128, 1)
+    assert need > fa.NOALLOC_MAX_WORKSPACE
+    assert fa.fa_bwd_noalloc(**base) == 5
+    assert fa.fa_bwd_noalloc(**{**base, "dq": None}) == 1
+    assert fa.fa_bwd_noalloc(**{**base, "dk": MIS}) == 4
+    assert fa.fa_bwd_noalloc(**{**base, "deterministic": 3}) == 2
+    assert fa.fa_bwd_noalloc(**{**base, "d": 96}) == 3
+    src = open(os.path.join(ROOT, "include", "fa.h")).read()
+    assert "#define FA_NOALLOC_MAX_WORKSPACE ((size_t)32 << 20)" in src
+    assert fa.NOALLOC_MAX_WORKSPACE == 32 << 20
