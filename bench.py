@@ -42,10 +42,12 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
 def source_sha256():
     """Hash of the kernel sources and build flags (not of the binary, whose
-    bytes depend on the checkout path): the stored counters stay valid
-    exactly as long as the code they measured does."""
+    bytes depend on the checkout path), with comments and runs of white space
+    removed: the stored counters stay valid exactly as long as the code they
+    measured does."""
     import hashlib
     import importlib.util
+    import re
     spec = importlib.util.spec_from_file_location(
         "_fa_build", os.path.join(ROOT, "exact_tiled_attention_27_amd", "build.py"))
     b = importlib.util.module_from_spec(spec)
@@ -54,8 +56,10 @@ def source_sha256():
     csrc = os.path.join(ROOT, "exact_tiled_attention_27_amd", "csrc")
     paths = [os.path.join(csrc, n) for n in sorted(os.listdir(csrc))]
     for path in paths + [os.path.join(ROOT, "include", "fa.h")]:
-        with open(path, "rb") as fh:
-            h.update(os.path.basename(path).encode() + b"\0" + fh.read())
+        with open(path) as fh:
+            code = re.sub(r"//[^\n]*|/\*.*?\*/", " ", fh.read(), flags=re.S)
+        code = " ".join(code.split())
+        h.update(os.path.basename(path).encode() + b"\0" + code.encode())
     return h.hexdigest()
 
 

@@ -52,6 +52,15 @@ float rescale_tau()
     return t;
 }
 
+// FA_WORKGROUP_ORDER=linear launches workgroups in plain head-major order
+// instead of the XCD-grouped (and, causal, longest-first) order: a switch for
+// measuring what that order gains.  Read on every call.
+int linear_map()
+{
+    const char *e = std::getenv("FA_WORKGROUP_ORDER");
+    return (e && std::strcmp(e, "linear") == 0) ? 1 : 0;
+}
+
 // FA_EXP2_POLY selects how many of the forward's exponentials run as the
 // cubic polynomial on the FMA units: "1" all, "4" one in four, anything else
 // (or unset) none.  Read on every call.
@@ -78,7 +87,7 @@ int fwd_impl(const void *q, const void *k, const void *v, float *o, float *lse, 
         return FA_ERR_ALIGN;
     fa::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, N, d, scale, rescale_tau(), causal != 0,
                   slopes ? 0 : exp2_poly_share(), window < N ? window : 0, 1, nullptr, nullptr,
-                  reinterpret_cast<hipStream_t>(stream), slopes};
+                  reinterpret_cast<hipStream_t>(stream), slopes, linear_map()};
     return hip_status(fa::launch_fwd(a));
 }
 
@@ -109,7 +118,7 @@ int bwd_impl(const void *q, const void *k, const void *v, const float *o, const 
                     : nullptr;
     fa::BwdArgs a{q, k, v, dout, o, lse, dq, dk, dv, delta, lse2, sync, B, Hq, Hkv, N, d, scale,
                   causal != 0, deterministic, window < N ? window : 0,
-                  reinterpret_cast<hipStream_t>(stream), slopes};
+                  reinterpret_cast<hipStream_t>(stream), slopes, linear_map()};
     return hip_status(fa::launch_bwd(a));
 }
 
@@ -178,7 +187,7 @@ int fa_fwd_splitkv(const void *q, const void *k, const void *v, float *o, float 
     }
     fa::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, N, d, scale, rescale_tau(), causal != 0,
                   exp2_poly_share(), 0, num_splits, opart, lpart,
-                  reinterpret_cast<hipStream_t>(stream)};
+                  reinterpret_cast<hipStream_t>(stream), nullptr, linear_map()};
     return hip_status(fa::launch_fwd(a));
 }
 

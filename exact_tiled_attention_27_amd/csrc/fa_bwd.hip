@@ -191,7 +191,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_split_kernel(
     const float *__restrict__ lse2, const float *__restrict__ delta, float *__restrict__ dq,
     float *__restrict__ dk, float *__restrict__ dv, int Hq, int Hkv, int N, int BHkv, int KT,
     float scale, float scale_log2, int window, int *__restrict__ sync,
-    const float *__restrict__ slopes)
+    const float *__restrict__ slopes, int linear_map)
 {
     using S = DkdvSplitShape<D>;
     constexpr bool ATOMIC_DQ = DQ != kDqNone;
@@ -242,7 +242,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_split_kernel(
         kt = hw / BHkv;
         bg = hw % BHkv;
     } else {
-        xcd_tile_map(blockIdx.x, BHkv, KT, false, bg, kt);
+        xcd_tile_map(blockIdx.x, BHkv, KT, false, linear_map, bg, kt);
     }
     const int b = bg / Hkv, g = bg % Hkv;
     const int grp = Hq / Hkv;
@@ -599,7 +599,7 @@ __global__ __launch_bounds__(256, FA_DQ_MIN_WAVES) void bwd_dq_kernel(
     const uint16_t *__restrict__ v, const uint16_t *__restrict__ dout,
     const float *__restrict__ lse2, const float *__restrict__ delta, float *__restrict__ dq,
     int Hq, int Hkv, int N, int BH, int QT, float scale, float scale_log2, int window,
-    const float *__restrict__ slopes, float *__restrict__ delta_out)
+    const float *__restrict__ slopes, float *__restrict__ delta_out, int linear_map)
 {
     using S = DqShape<D>;
     __shared__ __attribute__((aligned(16))) char k_lds0[S::TILE];
@@ -613,7 +613,7 @@ __global__ __launch_bounds__(256, FA_DQ_MIN_WAVES) void bwd_dq_kernel(
     const int g16 = lane >> 4;
 
     int bh, qt;
-    xcd_tile_map(blockIdx.x, BH, QT, CAUSAL, bh, qt);
+    xcd_tile_map(blockIdx.x, BH, QT, CAUSAL, linear_map, bh, qt);
     const int b = bh / Hq, hq = bh % Hq;
     const int g = hq / (Hq / Hkv);
     const int q0 = qt * S::BM;
@@ -833,7 +833,7 @@ static hipError_t launch_bwd_t(const BwdArgs &a)
                            (const uint16_t *)a.v, (const uint16_t *)a.dout, a.lse2,
                            (const float *)nullptr, (float *)nullptr, a.Hq, a.Hkv, a.N, BH, QT,
                            a.scale, scale_log2, a.window > 0 ? a.window : kNoWindow, a.slopes,
-                           a.delta);
+                           a.delta, a.linear_map);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -853,7 +853,7 @@ static hipError_t launch_bwd_t(const BwdArgs &a)
                            (const uint16_t *)a.dout, a.lse2, a.delta, a.dq, a.dk, a.dv, a.Hq,
                            a.Hkv, a.N, BHkv, KT, a.scale, scale_log2,
                            a.window > 0 ? a.window : kNoWindow,
-                           a.mode == kBwdOrdered ? a.sync : nullptr, a.slopes);
+                           a.mode == kBwdOrdered ? a.sync : nullptr, a.slopes, a.linear_map);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -866,7 +866,7 @@ static hipError_t launch_bwd_t(const BwdArgs &a)
                            (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v,
                            (const uint16_t *)a.dout, a.lse2, a.delta, a.dq, a.Hq, a.Hkv, a.N, BH,
                            QT, a.scale, scale_log2, a.window > 0 ? a.window : kNoWindow, a.slopes,
-                           (float *)nullptr);
+                           (float *)nullptr, a.linear_map);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     return hipSuccess;

@@ -146,12 +146,17 @@ __device__ __forceinline__ float halves_sum(float x)
 // Round-robin dispatch puts workgroup i on XCD i % 8.  Map the hardware id to
 // (head, tile) so each XCD works through whole heads: the workgroups that
 // share one head's K/V run on the same XCD and share its L2.  With a causal
-// mask the tiles of an XCD are issued longest first.
+// mask the tiles of an XCD are issued longest first.  linear: the plain
+// order instead (head-major, tile t of a head at id head * T + t), kept as a
+// measurement switch for what the map above gains.
 constexpr int kNumXcd = 8;
 __device__ __forceinline__ void xcd_tile_map(int hw, int BH, int T, bool longest_first,
-                                             int &bh, int &t)
+                                             bool linear, int &bh, int &t)
 {
-    if (BH % kNumXcd == 0) {
+    if (linear) {
+        bh = hw / T;
+        t = hw % T;
+    } else if (BH % kNumXcd == 0) {
         const int per = BH / kNumXcd;
         const int xcd = hw % kNumXcd, slot = hw / kNumXcd;
         if (longest_first) {

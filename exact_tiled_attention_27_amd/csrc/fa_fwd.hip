@@ -99,7 +99,8 @@ __global__ __launch_bounds__(512, FA_FWD_MIN_WAVES) void fwd_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, float *__restrict__ o, float *__restrict__ lse, int Hq,
     int Hkv, int N, int BH, int QT, float scale_log2, float tau, int window, int n_splits,
-    float *__restrict__ opart, float *__restrict__ lpart, const float *__restrict__ slopes)
+    float *__restrict__ opart, float *__restrict__ lpart, const float *__restrict__ slopes,
+    int linear_map)
 {
     using S = FwdShape<D>;
     __shared__ __attribute__((aligned(16))) char k_lds0[S::TILE_BYTES];
@@ -116,11 +117,11 @@ __global__ __launch_bounds__(512, FA_FWD_MIN_WAVES) void fwd_kernel(
     int bh, qt, split = 0;
     if (SPLIT) {
         int vt;  // (query tile, chunk) pairs, longest first when causal
-        xcd_tile_map(blockIdx.x, BH, QT * n_splits, CAUSAL, bh, vt);
+        xcd_tile_map(blockIdx.x, BH, QT * n_splits, CAUSAL, linear_map, bh, vt);
         qt = vt / n_splits;
         split = vt % n_splits;
     } else {
-        xcd_tile_map(blockIdx.x, BH, QT, CAUSAL, bh, qt);
+        xcd_tile_map(blockIdx.x, BH, QT, CAUSAL, linear_map, bh, qt);
     }
     const int b = bh / Hq, hq = bh % Hq;
     const int g = hq / (Hq / Hkv);
@@ -498,7 +499,8 @@ static hipError_t launch_fwd_split(const FwdArgs &a)
     hipLaunchKernelGGL(kern, dim3(BH * QT * splits), dim3(S::THREADS), 0, a.stream,
                        (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v, a.o,
                        a.lse, a.Hq, a.Hkv, a.N, BH, QT, a.scale * kLog2e, a.tau,
-                       a.window > 0 ? a.window : kNoWindow, splits, a.opart, a.lpart, a.slopes);
+                       a.window > 0 ? a.window : kNoWindow, splits, a.opart, a.lpart, a.slopes,
+                       a.linear_map);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !SPLIT) return e;
     const size_t rows = (size_t)BH * a.N;

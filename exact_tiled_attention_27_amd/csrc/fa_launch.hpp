@@ -20,6 +20,7 @@ struct FwdArgs {
     float *lpart;  // splits > 1: partial LSE, [splits][B * Hq][N] fp32
     hipStream_t stream;
     const float *slopes = nullptr;  // linear position bias: slope per query head, [Hq] fp32
+    int linear_map = 0;             // 1: workgroups in plain order (measurement switch)
 };
 
 // How the backward sums dQ: fp32 atomics from the dK/dV kernel; a separate
@@ -46,6 +47,7 @@ struct BwdArgs {
     int window;    // causal sliding window in keys (0: none)
     hipStream_t stream;
     const float *slopes = nullptr;  // linear position bias: slope per query head, [Hq] fp32
+    int linear_map = 0;             // 1: workgroups in plain order (measurement switch)
 };
 
 hipError_t launch_fwd(const FwdArgs &a);

@@ -48,6 +48,13 @@
  *     replaces the rescale threshold 8 by another finite value >= 0 (0:
  *     rescale whenever the running maximum grows); the result is the same
  *     up to rounding.
+ *   - The environment variable FA_WORKGROUP_ORDER, read on every call, set
+ *     to "linear" launches workgroups in plain head-major order instead of
+ *     grouping each head's workgroups on one XCD (and, with the causal mask,
+ *     issuing the longest query tiles first), for measuring what the
+ *     default order gains.  Every workgroup computes the same values either
+ *     way, so the outputs are the same bits (apart from dQ in FA_BWD_ATOMIC
+ *     mode, whose order of additions is unspecified in any case).
  *   - Supported: d in {64, 128}; B, Hq, Hkv, N >= 1; Hq % Hkv == 0;
  *     scale > 0 and finite; every pointer 16-byte aligned; N need not be a
  *     multiple of any tile size; one head's bf16 rows, N * d * 2 bytes, must

@@ -10,6 +10,11 @@
   python rocprof_summary.py counters DIR... --cmd C... --title T --out FILE.md
       SQ counter ratios per kernel (MFMA busy, VALU co-execution, LDS bank
       conflicts, transcendental share) from --pmc passes
+  python rocprof_summary.py compare DIR... --label L... --cmd C... --title T --out FILE.md
+      average kernel durations of several --kernel-trace --stats runs side by side
+  python rocprof_summary.py pmc DIR... --label L... --cmd C... --title T --out FILE.md
+      raw per-kernel --pmc averages (with the L2 hit rate and the share of
+      atomics sent on to memory when those counters are present)
 
 Only the attention kernels (names in namespace fa::) and the calibration copy
 are reported.  The JSON written by `traffic` carries a hash of the kernel
@@ -82,6 +87,69 @@ def cmd_stats(a):
         out.append(f"| `{name}` | {calls} | {avg:.1f} | {mn:.1f} | {mx:.1f} | {100 * tot / total:.1f}% |")
     if a.note:
         out += ["", a.note]
+    write(a.out, out)
+
+
+def cmd_compare(a):
+    """Average kernel durations of several --kernel-trace --stats runs side by
+    side (one column per labelled run)."""
+    runs = []
+    for d in a.dirs:
+        avg = {}
+        with open(one_csv(d, "_kernel_stats.csv")) as f:
+            for r in csv.DictReader(f):
+                if "fa::" in r["Name"]:
+                    avg[short_name(r["Name"])] = float(r["AverageNs"]) / 1e3
+        runs.append(avg)
+    names = sorted(set().union(*runs), key=lambda k: -runs[0].get(k, 0))
+    out = [f"# {a.title}", "", "Commands (from the repository root, on one MI355X):", "", "```",
+           "export TMPDIR=/tmp"] + a.cmd + ["```", "",
+           "| kernel | " + " | ".join(f"{l} average (us)" for l in a.label) +
+           (f" | {a.label[1]} / {a.label[0]}" if len(runs) == 2 else "") + " |",
+           "|---|" + "---|" * (len(runs) + (1 if len(runs) == 2 else 0))]
+    for k in names:
+        vals = [r.get(k) for r in runs]
+        cells = " | ".join("-" if v is None else f"{v:.1f}" for v in vals)
+        ratio = (f" | {vals[1] / vals[0]:.2f}x" if len(runs) == 2 and None not in vals else
+                 (" | -" if len(runs) == 2 else ""))
+        out.append(f"| `{k}` | {cells}{ratio} |")
+    if a.note:
+        out += ["", a.note]
+    write(a.out, out)
+
+
+def cmd_pmc(a):
+    """Per-kernel averages of raw --pmc counters (one or more labelled runs),
+    with the L2 hit rate when TCC_HIT_sum / TCC_MISS_sum are present and the
+    share of L2 atomic requests sent on to memory when TCC_ATOMIC_sum /
+    TCC_EA0_ATOMIC_sum are."""
+    out = [f"# {a.title}", "", "Commands (from the repository root, on one MI355X):", "", "```",
+           "export TMPDIR=/tmp"] + a.cmd + ["```", ""]
+    for d, label in zip(a.dirs, a.label):
+        vals, _ = counter_rows(d)
+        per = collections.defaultdict(dict)
+        for (k, c), v in vals.items():
+            if k != COPY_KERNEL:
+                per[k][c] = mean(v)
+        counters = sorted({c for kv in per.values() for c in kv})
+        extra = []
+        if {"TCC_HIT_sum", "TCC_MISS_sum"} <= set(counters):
+            extra.append(("L2 hit rate", lambda c: c["TCC_HIT_sum"] / (c["TCC_HIT_sum"] + c["TCC_MISS_sum"]),
+                          "{:.1%}"))
+        if {"TCC_ATOMIC_sum", "TCC_EA0_ATOMIC_sum"} <= set(counters):
+            extra.append(("atomics sent on to memory",
+                          lambda c: c["TCC_EA0_ATOMIC_sum"] / c["TCC_ATOMIC_sum"] if c["TCC_ATOMIC_sum"] else 0.0,
+                          "{:.1%}"))
+        out += [f"## {label}", "", "| kernel | " + " | ".join(counters + [e[0] for e in extra]) + " |",
+                "|---|" + "---|" * (len(counters) + len(extra))]
+        for k in sorted(per):
+            c = per[k]
+            cells = [f"{c.get(n, float('nan')):.4g}" for n in counters]
+            cells += [fmt.format(fn(c)) for _, fn, fmt in extra]
+            out.append(f"| `{k}` | " + " | ".join(cells) + " |")
+        out.append("")
+    if a.note:
+        out += [a.note]
     write(a.out, out)
 
 
@@ -208,8 +276,23 @@ def main():
     c.add_argument("--title", required=True)
     c.add_argument("--note", default="")
     c.add_argument("--out", required=True)
+    m = sp.add_parser("compare")
+    m.add_argument("dirs", nargs="+")
+    m.add_argument("--label", action="append", required=True)
+    m.add_argument("--cmd", action="append", required=True)
+    m.add_argument("--title", required=True)
+    m.add_argument("--note", default="")
+    m.add_argument("--out", required=True)
+    q = sp.add_parser("pmc")
+    q.add_argument("dirs", nargs="+")
+    q.add_argument("--label", action="append", required=True)
+    q.add_argument("--cmd", action="append", required=True)
+    q.add_argument("--title", required=True)
+    q.add_argument("--note", default="")
+    q.add_argument("--out", required=True)
     a = p.parse_args()
-    {"stats": cmd_stats, "traffic": cmd_traffic, "counters": cmd_counters}[a.mode](a)
+    {"stats": cmd_stats, "traffic": cmd_traffic, "counters": cmd_counters, "compare": cmd_compare,
+     "pmc": cmd_pmc}[a.mode](a)
 
 
 if __name__ == "__main__":

@@ -492,6 +492,28 @@ def test_long_context_gqa_backward(fa):
         del again
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_linear_workgroup_order_same_bits(fa, monkeypatch, causal):
+    """FA_WORKGROUP_ORDER=linear (plain head-major workgroup order, the
+    measurement switch for the XCD-grouped, longest-first map) changes where
+    each workgroup runs, not what it computes: forward and deterministic
+    backward outputs are bit-identical to the default order's.  B2 Hq8 Hkv4
+    (8 KV heads, so the grouped map is in effect), N 1000."""
+    B, Hq, Hkv, N, d = 2, 8, 4, 1000, 128
+    q, k, v = random_bf16((B, Hq, N, d), 91), random_bf16((B, Hkv, N, d), 92), random_bf16((B, Hkv, N, d), 93)
+    dout = random_bf16((B, Hq, N, d), 94)
+    scale = 1 / math.sqrt(d)
+    outs = {}
+    for order in ("default", "linear"):
+        if order == "linear":
+            monkeypatch.setenv("FA_WORKGROUP_ORDER", "linear")
+        note(f"workgroup order {order} causal={causal}")
+        o, lse = gpu_fwd(fa, q, k, v, scale, causal)
+        outs[order] = (o, lse) + gpu_bwd(fa, q, k, v, dout, o, lse, scale, causal, 1)
+    for a, b in zip(outs["default"], outs["linear"]):
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
 # ---------------------------------------------------------- split-KV forward
 
 def gpu_fwd_split(fa, q, k, v, scale, causal, splits):
