@@ -42,9 +42,10 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
 def source_sha256():
     """Hash of the kernel sources and build flags (not of the binary, whose
-    bytes depend on the checkout path), with comments and runs of white space
-    removed: the stored counters stay valid exactly as long as the code they
-    measured does."""
+    bytes depend on the checkout path), with comments, runs of white space and
+    the debug build's `#if FA_DEBUG_COUNTERS` blocks removed: the stored
+    counters stay valid exactly as long as the code of libfa.so they measured
+    does."""
     import hashlib
     import importlib.util
     import re
@@ -58,6 +59,7 @@ def source_sha256():
     for path in paths + [os.path.join(ROOT, "include", "fa.h")]:
         with open(path) as fh:
             code = re.sub(r"//[^\n]*|/\*.*?\*/", " ", fh.read(), flags=re.S)
+            code = re.sub(r"#if FA_DEBUG_COUNTERS\b.*?#endif", " ", code, flags=re.S)
         code = " ".join(code.split())
         h.update(os.path.basename(path).encode() + b"\0" + code.encode())
     return h.hexdigest()

@@ -248,6 +248,15 @@ int fa_debug_counters(unsigned long long *counters, int n)
     if (!counters || n < 1) return FA_ERR_NULL;
     return hip_status(fa::debug_counters(counters, n));
 }
+
+int fa_debug_atomic_tiles(float *buf, int n_slots, int tiles, int blocks, void *stream)
+{
+    if (!buf) return FA_ERR_NULL;
+    if (n_slots < 1 || tiles < 1 || blocks < 1) return FA_ERR_SHAPE;
+    if (!aligned16(buf)) return FA_ERR_ALIGN;
+    return hip_status(fa::debug_atomic_tiles(buf, n_slots, tiles, blocks,
+                                             reinterpret_cast<hipStream_t>(stream)));
+}
 #endif
 
 int fa_fwd_alibi(const void *q, const void *k, const void *v, float *o, float *lse,

@@ -872,6 +872,39 @@ static hipError_t launch_bwd_t(const BwdArgs &a)
     return hipSuccess;
 }
 
+#if FA_DEBUG_COUNTERS
+// Debug build only: the dQ atomics of bwd_dkdv_split_kernel's atomic modes
+// without anything else, to measure the device's rate for them.  Workgroup
+// w (256 threads) adds `tiles` tiles of 64 x D fp32 values into tile slot
+// (7 w + 13 i) % n_slots of buf, each wave two 32 x 32 blocks per tile with
+// the B waves' lane pattern (lanes 0-31 and 32-63 on 128 contiguous bytes
+// of rows 4 apart).
+template <int D>
+__global__ __launch_bounds__(256) void dbg_atomic_tiles_kernel(float *buf, int n_slots, int tiles)
+{
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int h = lane >> 5, col = lane & 31;
+    constexpr int DBLK = D / 32;
+    for (int i = 0; i < tiles; i++) {
+        const int slot = (int)(((long long)blockIdx.x * 7 + (long long)i * 13) % n_slots);
+        float *tile = buf + (size_t)slot * 64 * D;
+        for (int tt = wave; tt < 2 * DBLK; tt += 4) {
+            const int qb = tt / DBLK, db = tt % DBLK;
+            float *p = tile + (size_t)(32 * qb + 4 * h) * D + 32 * db + col;
+#pragma unroll
+            for (int r = 0; r < 16; r++) unsafeAtomicAdd(p + (8 * (r >> 2) + (r & 3)) * D, 1.0f);
+        }
+    }
+}
+
+hipError_t debug_atomic_tiles(float *buf, int n_slots, int tiles, int blocks, hipStream_t stream)
+{
+    hipLaunchKernelGGL(dbg_atomic_tiles_kernel<128>, dim3(blocks), dim3(256), 0, stream, buf,
+                       n_slots, tiles);
+    return hipGetLastError();
+}
+#endif
+
 // Backward workspace of fa_bwd_noalloc, for callers that cannot allocate
 // device memory: one copy of this array per device, held until the process
 // ends.  Host code never uses its name as an address: the device address

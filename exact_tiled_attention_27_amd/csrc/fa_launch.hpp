@@ -68,6 +68,9 @@ enum {
 #if FA_DEBUG_COUNTERS
 // Copies min(n, kDbgCount) counters to host memory, then clears them.
 hipError_t debug_counters(unsigned long long *host, int n);
+// The dQ atomic pattern alone (d = 128): blocks workgroups x tiles tiles of
+// 64 x 128 fp32 atomic adds of 1.0 into n_slots tiles of buf.
+hipError_t debug_atomic_tiles(float *buf, int n_slots, int tiles, int blocks, hipStream_t stream);
 #endif
 hipError_t launch_bwd(const BwdArgs &a);
 

@@ -3,6 +3,7 @@
 The same forward entry points as the package (fa_fwd, fa_fwd_window), served
 by libfa_debug.so, whose forward kernels count rescale decisions, rescales
 taken and key tiles walked; fa_debug_counters() reads and clears the counts.
+fa_debug_atomic_tiles() runs the backward's dQ atomic pattern alone.
 For measurement only: the counters' atomics perturb timings.  Importing this
 module fails if libfa_debug.so has not been built.
 """
@@ -28,6 +29,8 @@ _lib.fa_fwd_window.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, 
 _lib.fa_fwd_window.restype = _i
 _lib.fa_debug_counters.argtypes = [ctypes.POINTER(ctypes.c_ulonglong), _i]
 _lib.fa_debug_counters.restype = _i
+_lib.fa_debug_atomic_tiles.argtypes = [_vp, _i, _i, _i, _vp]
+_lib.fa_debug_atomic_tiles.restype = _i
 
 
 def fa_fwd(q, k, v, o, lse, B, Hq, Hkv, N, d, scale, causal, stream=None) -> int:
@@ -40,6 +43,12 @@ def fa_fwd_window(q, k, v, o, lse, B, Hq, Hkv, N, d, scale, window, stream=None)
     """fa_fwd_window of the debug build.  Status out."""
     return _lib.fa_fwd_window(_addr(q), _addr(k), _addr(v), _addr(o), _addr(lse), B, Hq, Hkv, N,
                               d, float(scale), int(window), _stream(stream, q, o))
+
+
+def fa_debug_atomic_tiles(buf, n_slots, tiles, blocks, stream=None) -> int:
+    """fa_debug_atomic_tiles: the dQ atomic pattern alone.  Status out."""
+    return _lib.fa_debug_atomic_tiles(_addr(buf), int(n_slots), int(tiles), int(blocks),
+                                      _stream(stream, buf))
 
 
 def fa_debug_counters() -> dict:

@@ -39,6 +39,19 @@ extern "C" {
  */
 int fa_debug_counters(unsigned long long *counters, int n);
 
+/*
+ * The dQ atomics of the backward's atomic modes, alone: the device's rate
+ * for them is what bounds those modes (every such fp32 add is executed at
+ * the memory side, not in an XCD's L2).  `blocks` workgroups of 256 threads
+ * each add `tiles` tiles of 64 x 128 fp32 values 1.0 into tile slot
+ * (7 w + 13 i) % n_slots of buf (w the workgroup, i the tile; each slot
+ * 64 * 128 floats), with the lane pattern of the dK/dV kernel's dQ adds.
+ * buf: fp32 device memory of at least n_slots * 64 * 128 floats, 16-byte
+ * aligned.  Enqueued on `stream`; FA_ERR_NULL / FA_ERR_SHAPE / FA_ERR_ALIGN
+ * for bad arguments, FA_ERR_HIP for a launch error.
+ */
+int fa_debug_atomic_tiles(float *buf, int n_slots, int tiles, int blocks, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -35,11 +35,12 @@ def test_debug_build_exports_both_headers():
     plus fa_debug.h's; the product library libfa.so has no counter entry."""
     debug_lib = os.path.join(os.path.dirname(fa.LIB_PATH), "libfa_debug.so")
     dbg_names = declared_functions(os.path.join(ROOT, "include", "fa_debug.h"))
-    assert dbg_names == ["fa_debug_counters"]
+    assert dbg_names == ["fa_debug_atomic_tiles", "fa_debug_counters"]
     syms = exported(debug_lib)
     for n in declared_functions() + dbg_names:
         assert n in syms, n
-    assert "fa_debug_counters" not in exported(fa.LIB_PATH)
+    for n in dbg_names:
+        assert n not in exported(fa.LIB_PATH), n
 
 
 def test_exports_every_declared_symbol():

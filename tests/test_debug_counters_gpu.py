@@ -98,3 +98,30 @@ def test_rescale_rate_on_workloads(fa, dbg, name):
     assert c["workgroups"] == w.B * w.Hq * math.ceil(w.N / 256)
     if w.row_scale:
         assert 0 < c["row_rescales"] < 0.05 * c["row_decisions"]
+
+
+def test_dq_atomic_pattern_rate(fa, dbg):
+    """The backward's dQ atomic pattern alone (fa_debug_atomic_tiles): every
+    add lands exactly once (the buffer sums to the count of adds), and the
+    device's rate for it is printed: the atomic dK/dV kernel's adds per
+    second are compared against it in the design notes."""
+    n_slots, tiles = 4096, 64
+    buf = torch.zeros(n_slots * 64 * 128, dtype=torch.float32, device="cuda")
+    for blocks in (1024, 4096):
+        buf.zero_()
+        st = dbg.fa_debug_atomic_tiles(buf, n_slots, tiles, blocks)
+        assert st == 0
+        torch.cuda.synchronize()
+        total = float(buf.double().sum())
+        assert total == blocks * tiles * 64 * 128
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            assert dbg.fa_debug_atomic_tiles(buf, n_slots, tiles, blocks) == 0
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 5
+        lanes = blocks * tiles * 64 * 128
+        note(f"dQ atomic pattern: {blocks} workgroups x {tiles} tiles: {ms:.3f} ms, "
+             f"{lanes / ms / 1e6:.1f} G fp32 adds/s, {lanes / 16 / ms / 1e6:.2f} G 64-byte "
+             f"requests/s")
