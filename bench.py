@@ -11,14 +11,14 @@ forward, the same count for every dQ mode.  The step's value is
 Prints ONE JSON line.  Inputs are resident in HBM before the timed region; the
 region is bracketed by device synchronisation.  HIP events recorded on the
 launch stream around each call give per-call durations for the roofline.  The
-ordered-dQ backward mode is timed after the step loop and reported under
-"parts".
+ordered-dQ and paired-atomic backward modes are timed after the step loop and
+reported under "parts".
 The fp64 CPU oracle is timed on bounded samples of every workload (whole
 heads of the forward; whole key/value groups of the backward) as a reported
 baseline.
 
 "per_config" then times each of the five synthetic workloads on its own
-(forward; the three dQ modes of the backward for the backward workload and for
+(forward; the four dQ modes of the backward for the backward workload and for
 the long-context GQA shape; the linear-position-bias forward and deterministic
 backward on the backward workload's inputs): launches back to back after
 0.3 s of untimed ones, an event pair around each launch, median and minimum
@@ -146,7 +146,7 @@ def per_config(fa, reps, dev, stream):
             dq = torch.empty((B, Hq, N, d), dtype=torch.float32, device=dev)
             dk = torch.empty((B, Hkv, N, d), dtype=torch.float32, device=dev)
             dv = torch.empty_like(dk)
-            for det in (fa.BWD_SEPARATE, fa.BWD_ATOMIC, fa.BWD_ORDERED):
+            for det in (fa.BWD_SEPARATE, fa.BWD_ATOMIC, fa.BWD_ORDERED, fa.BWD_ATOMIC_PAIRED):
                 wsb = fa.fa_bwd_workspace_bytes(B, Hq, Hkv, N, d, det)
                 ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
 
@@ -157,7 +157,8 @@ def per_config(fa, reps, dev, stream):
                         raise fa.FAError(st, "fa_bwd")
 
                 name = {fa.BWD_SEPARATE: "fa_bwd deterministic", fa.BWD_ATOMIC: "fa_bwd atomic",
-                        fa.BWD_ORDERED: "fa_bwd ordered"}[det]
+                        fa.BWD_ORDERED: "fa_bwd ordered",
+                        fa.BWD_ATOMIC_PAIRED: "fa_bwd atomic paired"}[det]
                 row["calls"].append(entry(name, w.bwd_flops(), time_launches(bwd, reps, stream)))
             if w.name == "fwdbwd_causal_n8192":
                 # The linear position bias on the same inputs, geometric
@@ -251,8 +252,8 @@ def parse():
     p.add_argument("--workload", default="fwdbwd_causal_n8192")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--ordered-reps", type=int, default=10,
-                   help="timed launches of the ordered-dQ backward reported under parts "
-                        "(0: skip)")
+                   help="timed launches of each of the ordered and the paired-atomic "
+                        "backward, reported under parts (0: skip)")
     p.add_argument("--no-per-config", action="store_true",
                    help="skip timing each synthetic workload on its own")
     p.add_argument("--per-config-reps", type=int, default=10)
@@ -297,7 +298,8 @@ def main():
     dk = torch.empty((B, Hkv, N, d), dtype=torch.float32, device=dev)
     dv = torch.empty_like(dk)
     ws_bytes = max(fa.fa_bwd_workspace_bytes(B, Hq, Hkv, N, d, m)
-                   for m in (fa.BWD_ATOMIC, fa.BWD_SEPARATE, fa.BWD_ORDERED))
+                   for m in (fa.BWD_ATOMIC, fa.BWD_SEPARATE, fa.BWD_ORDERED,
+                             fa.BWD_ATOMIC_PAIRED))
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
@@ -354,20 +356,22 @@ def main():
         parts[f"{name}_tflops"] = flops[name] / (np.mean(ms) * 1e-3) / 1e12
         parts[f"{name}_frac_peak"] = parts[f"{name}_tflops"] / PEAK_BF16_TFLOPS
 
-    # The third dQ mode of the same backward, back to back after one untimed
-    # call.
-    if args.ordered_reps > 0:
+    # The other two dQ modes of the same backward, each back to back after
+    # one untimed call.
+    for mode, key in ((fa.BWD_ORDERED, "bwd_ordered"), (fa.BWD_ATOMIC_PAIRED, "bwd_atomic_paired")):
+        if args.ordered_reps <= 0:
+            break
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        bwd(fa.BWD_ORDERED)
+        bwd(mode)
         torch.cuda.synchronize()
         e0.record(stream)
         for _ in range(args.ordered_reps):
-            bwd(fa.BWD_ORDERED)
+            bwd(mode)
         e1.record(stream)
         torch.cuda.synchronize()
         at_ms = e0.elapsed_time(e1) / args.ordered_reps
-        parts["bwd_ordered_ms_avg"] = at_ms
-        parts["bwd_ordered_tflops"] = f_bwd / (at_ms * 1e-3) / 1e12
+        parts[f"{key}_ms_avg"] = at_ms
+        parts[f"{key}_tflops"] = f_bwd / (at_ms * 1e-3) / 1e12
 
     # Roofline of the dominant launch: the call of the step that takes the
     # longest.  fa_fwd is one kernel; fa_bwd is a short preprocess kernel and

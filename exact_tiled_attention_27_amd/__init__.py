@@ -19,7 +19,8 @@ __all__ = ["fa_fwd", "fa_fwd_window", "fa_fwd_splitkv", "fa_fwd_splitkv_workspac
            "fa_fwd_alibi", "fa_bwd_alibi", "fa_bwd", "fa_bwd_window", "fa_bwd_noalloc",
            "fa_bwd_workspace_bytes", "fa_status_string", "FAError",
            "attention_fwd", "attention_bwd", "LIB_PATH", "STATUS", "MAX_SPLITS",
-           "NOALLOC_MAX_WORKSPACE", "BWD_ATOMIC", "BWD_SEPARATE", "BWD_ORDERED"]
+           "NOALLOC_MAX_WORKSPACE", "BWD_ATOMIC", "BWD_SEPARATE", "BWD_ORDERED",
+           "BWD_ATOMIC_PAIRED"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
@@ -27,8 +28,8 @@ MAX_SPLITS = 64  # FA_MAX_SPLITS
 NOALLOC_MAX_WORKSPACE = 32 << 20  # FA_NOALLOC_MAX_WORKSPACE (bytes)
 
 # dQ modes of fa_bwd's `deterministic` argument (FA_BWD_ATOMIC, FA_BWD_SEPARATE,
-# FA_BWD_ORDERED); False and True select the first two.
-BWD_ATOMIC, BWD_SEPARATE, BWD_ORDERED = 0, 1, 2
+# FA_BWD_ORDERED, FA_BWD_ATOMIC_PAIRED); False and True select the first two.
+BWD_ATOMIC, BWD_SEPARATE, BWD_ORDERED, BWD_ATOMIC_PAIRED = 0, 1, 2, 3
 
 STATUS = {0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_UNSUPPORTED",
           4: "FA_ERR_ALIGN", 5: "FA_ERR_WORKSPACE", 6: "FA_ERR_HIP"}
@@ -217,7 +218,8 @@ def attention_fwd(q, k, v, scale=None, causal=False, o=None, lse=None, stream=No
 def attention_bwd(q, k, v, o, lse, dout, scale=None, causal=False, deterministic=False,
                   dq=None, dk=None, dv=None, workspace=None, stream=None):
     """Backward attention on device tensors.  Returns (dq, dk, dv) fp32.
-    deterministic: BWD_ATOMIC (False), BWD_SEPARATE (True) or BWD_ORDERED."""
+    deterministic: BWD_ATOMIC (False), BWD_SEPARATE (True), BWD_ORDERED or
+    BWD_ATOMIC_PAIRED."""
     import torch
     _check_inputs(q, k, v, dout)
     B, Hq, Hkv, N, d = _dims(q, k)

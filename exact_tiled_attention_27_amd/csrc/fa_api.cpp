@@ -61,6 +61,20 @@ int linear_map()
     return (e && std::strcmp(e, "linear") == 0) ? 1 : 0;
 }
 
+bool valid_bwd_mode(int mode) { return mode >= FA_BWD_ATOMIC && mode <= FA_BWD_ATOMIC_PAIRED; }
+
+// Backward workspace bytes for dQ mode `mode`: the D and LSE2 rows, then the
+// ordered mode's counters, or the paired atomic mode's pair block and ring.
+size_t bwd_bytes(int B, int Hq, int Hkv, int N, int d, int mode)
+{
+    const size_t rows_part = 2 * round256(workspace_rows(B, Hq, N) * sizeof(float));
+    if (mode == FA_BWD_ORDERED) return rows_part + round256(fa::bwd_sync_words(B * Hq, N) * sizeof(int));
+    if (mode == FA_BWD_ATOMIC_PAIRED)
+        return rows_part + round256(fa::bwd_pair_words(B, Hq, Hkv, N, fa::kPairSlots) * sizeof(int)) +
+               round256(fa::bwd_pair_ring_bytes(B, Hkv, N, d, fa::kPairSlots));
+    return rows_part;
+}
+
 // FA_EXP2_POLY selects how many of the forward's exponentials run as the
 // cubic polynomial on the FMA units: "1" all, "4" one in four, anything else
 // (or unset) none.  Read on every call.
@@ -92,7 +106,8 @@ int fwd_impl(const void *q, const void *k, const void *v, float *o, float *lse, 
 }
 
 // fa_bwd and fa_bwd_window: window as in fwd_impl; deterministic is the dQ
-// mode (FA_BWD_ATOMIC, FA_BWD_SEPARATE or FA_BWD_ORDERED).
+// mode (FA_BWD_ATOMIC, FA_BWD_SEPARATE, FA_BWD_ORDERED or
+// FA_BWD_ATOMIC_PAIRED).
 int bwd_impl(const void *q, const void *k, const void *v, const float *o, const float *lse,
              const void *dout, float *dq, float *dk, float *dv, int B, int Hq, int Hkv, int N,
              int d, float scale, int causal, int window, int deterministic, void *workspace,
@@ -101,24 +116,34 @@ int bwd_impl(const void *q, const void *k, const void *v, const float *o, const 
     if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL;
     int st = check_common(B, Hq, Hkv, N, d, scale);
     if (st != FA_OK) return st;
-    if (deterministic < FA_BWD_ATOMIC || deterministic > FA_BWD_ORDERED) return FA_ERR_SHAPE;
+    if (!valid_bwd_mode(deterministic)) return FA_ERR_SHAPE;
     const void *ptrs[] = {q, k, v, o, lse, dout, dq, dk, dv};
     for (const void *p : ptrs)
         if (!aligned16(p)) return FA_ERR_ALIGN;
-    const size_t need = fa_bwd_workspace_bytes(B, Hq, Hkv, N, d, deterministic);
+    const size_t need = bwd_bytes(B, Hq, Hkv, N, d, deterministic);
     if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
     if (!aligned16(workspace)) return FA_ERR_ALIGN;
+    const int pair_slots = deterministic == FA_BWD_ATOMIC_PAIRED ? fa::kPairSlots : 0;
     const size_t rows = workspace_rows(B, Hq, N);
-    float *delta = reinterpret_cast<float *>(workspace);
-    float *lse2 = reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) +
-                                            round256(rows * sizeof(float)));
-    int *sync = deterministic == FA_BWD_ORDERED
-                    ? reinterpret_cast<int *>(reinterpret_cast<char *>(workspace) +
-                                              2 * round256(rows * sizeof(float)))
+    char *ws = reinterpret_cast<char *>(workspace);
+    float *delta = reinterpret_cast<float *>(ws);
+    float *lse2 = reinterpret_cast<float *>(ws + round256(rows * sizeof(float)));
+    char *after_rows = ws + 2 * round256(rows * sizeof(float));
+    int *sync = deterministic == FA_BWD_ORDERED || pair_slots > 0
+                    ? reinterpret_cast<int *>(after_rows)
                     : nullptr;
+    float *xring = pair_slots > 0
+                       ? reinterpret_cast<float *>(
+                             after_rows +
+                             round256(fa::bwd_pair_words(B, Hq, Hkv, N, pair_slots) * sizeof(int)))
+                       : nullptr;
+    static_assert(fa::kBwdAtomic == FA_BWD_ATOMIC && fa::kBwdSeparate == FA_BWD_SEPARATE &&
+                      fa::kBwdOrdered == FA_BWD_ORDERED &&
+                      fa::kBwdAtomicPaired == FA_BWD_ATOMIC_PAIRED,
+                  "dQ mode values");
     fa::BwdArgs a{q, k, v, dout, o, lse, dq, dk, dv, delta, lse2, sync, B, Hq, Hkv, N, d, scale,
                   causal != 0, deterministic, window < N ? window : 0,
-                  reinterpret_cast<hipStream_t>(stream), slopes, linear_map()};
+                  reinterpret_cast<hipStream_t>(stream), slopes, linear_map(), xring, pair_slots};
     return hip_status(fa::launch_bwd(a));
 }
 
@@ -194,10 +219,8 @@ int fa_fwd_splitkv(const void *q, const void *k, const void *v, float *o, float 
 size_t fa_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d, int deterministic)
 {
     if (check_common(B, Hq, Hkv, N, d, 1.0f) != FA_OK) return 0;
-    if (deterministic < FA_BWD_ATOMIC || deterministic > FA_BWD_ORDERED) return 0;
-    const size_t rows_part = 2 * round256(workspace_rows(B, Hq, N) * sizeof(float));
-    if (deterministic != FA_BWD_ORDERED) return rows_part;
-    return rows_part + round256(fa::bwd_sync_words(B * Hq, N) * sizeof(int));
+    if (!valid_bwd_mode(deterministic)) return 0;
+    return bwd_bytes(B, Hq, Hkv, N, d, deterministic);
 }
 
 int fa_bwd(const void *q, const void *k, const void *v, const float *o, const float *lse,
@@ -220,12 +243,12 @@ int fa_bwd_noalloc(const void *q, const void *k, const void *v, const float *o,
     if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL;
     int st = check_common(B, Hq, Hkv, N, d, scale);
     if (st != FA_OK) return st;
-    if (deterministic < FA_BWD_ATOMIC || deterministic > FA_BWD_ORDERED) return FA_ERR_SHAPE;
+    if (!valid_bwd_mode(deterministic)) return FA_ERR_SHAPE;
     const void *ptrs[] = {q, k, v, o, lse, dout, dq, dk, dv};
     for (const void *p : ptrs)
         if (!aligned16(p)) return FA_ERR_ALIGN;
-    const size_t need = fa_bwd_workspace_bytes(B, Hq, Hkv, N, d, deterministic);
-    if (need > fa::kNoAllocScratchBytes) return FA_ERR_WORKSPACE;
+    if (bwd_bytes(B, Hq, Hkv, N, d, deterministic) > fa::kNoAllocScratchBytes)
+        return FA_ERR_WORKSPACE;
     void *ws = nullptr;
     if (fa::noalloc_scratch(&ws) != hipSuccess) return FA_ERR_HIP;
     return bwd_impl(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, N, d, scale, causal, 0,

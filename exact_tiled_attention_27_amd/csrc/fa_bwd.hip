@@ -64,10 +64,11 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t *__restrict
                                                       int zero_dq, int *__restrict__ sync,
                                                       size_t n_sync)
 {
-    // Ordered mode: clear the ticket, timeout and turn counters (the grid
-    // has at least 8 threads per padded row, more than n_sync).
+    // Ordered mode's ticket, timeout and turn counters, or the atomic mode's
+    // pair block: cleared with a grid-stride loop.
     const size_t gid = (size_t)blockIdx.x * 256 + threadIdx.x;
-    if (sync && gid < n_sync) sync[gid] = 0;
+    if (sync)
+        for (size_t i = gid; i < n_sync; i += (size_t)gridDim.x * 256) sync[i] = 0;
     constexpr int TPR = D / 8;  // threads per row, 8 elements each
     const int NP = pad_rows(N);
     const size_t prow = (size_t)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;  // padded row
@@ -116,8 +117,8 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t *__restrict
 // live in separate LDS arrays per slot (step st uses slot st % 2), so reads of
 // one slot never wait for the copies into the other.
 // DQ selects what the kernel does for dQ: kDqNone (the deterministic mode's
-// separate pass computes it), kDqAtomic or kDqOrdered.  Both atomic modes add
-// dQ += dS K: wave B stores dS^T to LDS after the products of step st, and the
+// separate pass computes it), kDqAtomic, kDqOrdered or kDqPaired.  The atomic
+// modes add dQ += dS K: wave B stores dS^T to LDS after the products of step st, and the
 // four B waves add that step's dQ tiles with fp32 atomics at the start of step
 // st + 1 (before the mid-step barrier, after which dS^T is overwritten).
 // kDqOrdered makes the adds into each 64-row dQ tile happen in ascending
@@ -148,7 +149,7 @@ struct DkdvSplitShape {
     static constexpr int X_SLICE = 64 * 32 * 4;            // P exchange per slice: 64 lanes x 32 fp32
 };
 
-constexpr int kDqNone = 0, kDqAtomic = 1, kDqOrdered = 2;
+constexpr int kDqNone = 0, kDqAtomic = 1, kDqOrdered = 2, kDqPaired = 3;
 
 // Longest wait for a turn: 2 s at the 100 MHz wall clock.
 constexpr long long kTurnTimeout = 200000000LL;
@@ -182,6 +183,70 @@ __device__ __forceinline__ void wait_turn(const int *turn, int want, int *sync, 
     asm volatile("" ::: "memory");
 }
 
+// Paired atomic mode: waits (the whole wave) until the ring-slot counter
+// reaches `want` and returns the last value read (less than `want` after
+// kTurnTimeout ticks, counted in sync[kSyncTimeouts], or once any wait of
+// the launch has timed out).
+__device__ __forceinline__ int wait_count(const int *count, int want, int *sync, int lane)
+{
+    const long long t0 = wall_clock64();
+    int c = 0;
+    while (true) {
+        __builtin_amdgcn_s_sleep(1);
+        c = __builtin_amdgcn_readfirstlane(
+            __hip_atomic_load(count, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        if (c >= want) break;
+        if (__builtin_amdgcn_readfirstlane(__hip_atomic_load(
+                sync + kSyncTimeouts, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) != 0)
+            break;
+        if (wall_clock64() - t0 > kTurnTimeout) {
+            if (lane == 0)
+                __hip_atomic_fetch_add(sync + kSyncTimeouts, 1, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+            break;
+        }
+    }
+    // The ring stores that follow wait for the counter's value (branch).
+    asm volatile("" ::: "memory");
+    return c;
+}
+
+// Cache-policy bits of a buffer load or store: sc1, device scope (the
+// access is coherent for every XCD of the device).
+constexpr int kSc1 = 16;
+
+// Paired atomic mode: waits (the whole wave) until the exchange word has
+// bit 2 or 3 set (value 4 or 8) and returns it; 0 after kTurnTimeout ticks (counted in
+// sync[kSyncTimeouts]), and at once once any wait of the launch has timed
+// out, so that the kernel always finishes quickly.
+__device__ __forceinline__ int wait_flag(const int *word, int *sync, int lane)
+{
+    const long long t0 = wall_clock64();
+    int w = 0;
+    while (true) {
+        __builtin_amdgcn_s_sleep(1);
+        w = __builtin_amdgcn_readfirstlane(
+            __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        if (w & 12) break;
+        if (__builtin_amdgcn_readfirstlane(__hip_atomic_load(
+                sync + kSyncTimeouts, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) != 0) {
+            w = 0;
+            break;
+        }
+        if (wall_clock64() - t0 > kTurnTimeout) {
+            if (lane == 0)
+                __hip_atomic_fetch_add(sync + kSyncTimeouts, 1, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+            w = 0;
+            break;
+        }
+    }
+    // The ring loads that follow wait for the word's value (branch): keep
+    // the compiler from moving them above the wait.
+    asm volatile("" ::: "memory");
+    return w;
+}
+
 // BIAS: the linear position bias, slopes[hq] * (key - query), enters P's
 // recomputation (added to the raw score as slope / scale * (key - query)).
 template <int D, bool CAUSAL, int DQ, bool BIAS = false>
@@ -191,7 +256,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_split_kernel(
     const float *__restrict__ lse2, const float *__restrict__ delta, float *__restrict__ dq,
     float *__restrict__ dk, float *__restrict__ dv, int Hq, int Hkv, int N, int BHkv, int KT,
     float scale, float scale_log2, int window, int *__restrict__ sync,
-    const float *__restrict__ slopes, int linear_map)
+    const float *__restrict__ slopes, int linear_map, float *__restrict__ xring, int pair_slots)
 {
     using S = DkdvSplitShape<D>;
     constexpr bool ATOMIC_DQ = DQ != kDqNone;
@@ -281,6 +346,44 @@ __global__ __launch_bounds__(512) void bwd_dkdv_split_kernel(
     const int n_qt = CAUSAL ? min(n_qt_all, (kv0 + S::BN + window - 2) / S::BM + 1) : n_qt_all;
     const int steps_per_head = n_qt - first_qt;
     const int n_steps = grp * steps_per_head;
+    // Atomic mode with a pair block (pair_slots > 0): key blocks 2p and
+    // 2p + 1 walk the query tiles both of them see, [c_lo, c_hi) of every
+    // query head, first and in the same order (exchange e = step e), then
+    // each its own remaining tiles.  Otherwise c_lo = c_hi = first_qt and
+    // the walk is head-major in tile order.
+    int c_lo = first_qt, c_hi = first_qt;
+    const bool paired = DQ == kDqPaired && pair_slots > 0 && (kt ^ 1) < KT;
+    if (paired) {
+        const int pk = kt ^ 1;
+        const int p_first = CAUSAL ? pk * S::BN / S::BM : 0;
+        const int p_nqt =
+            CAUSAL ? min(n_qt_all, (pk * S::BN + S::BN + window - 2) / S::BM + 1) : n_qt_all;
+        c_lo = max(first_qt, p_first);
+        c_hi = min(n_qt, p_nqt);
+        if (c_hi <= c_lo) c_lo = c_hi = first_qt;
+    }
+    const int n_common = grp * (c_hi - c_lo);
+    const int n_extra = steps_per_head - (c_hi - c_lo);  // per head
+    // Local query head and 64-row tile of step st.
+    auto tile_of = [&](int st, int &hl, int &qt) {
+        if constexpr (DQ != kDqPaired) {
+            hl = st / steps_per_head;
+            qt = first_qt + st % steps_per_head;
+            return;
+        }
+        if (st < n_common) {
+            hl = st / (c_hi - c_lo);
+            qt = c_lo + st % (c_hi - c_lo);
+        } else {
+            const int e = st - n_common;
+            hl = e / n_extra;
+            const int j = e % n_extra;
+            qt = j < c_lo - first_qt ? first_qt + j : c_hi + (j - (c_lo - first_qt));
+        }
+        // Uniform per wave: keep them in scalar registers (tile copy bases).
+        hl = __builtin_amdgcn_readfirstlane(hl);
+        qt = __builtin_amdgcn_readfirstlane(qt);
+    };
 
     typename S::QTile qtile;
     qtile.init(wave, lane);
@@ -289,8 +392,10 @@ __global__ __launch_bounds__(512) void bwd_dkdv_split_kernel(
     // lanes 0-15 fetch LSE2, lanes 16-31 fetch D, 16 bytes each.
     auto issue = [&](int st, auto slot) {
         constexpr int P = decltype(slot)::value;
-        const int hq = g * grp + st / steps_per_head;
-        const int qs = (first_qt + st % steps_per_head) * S::BM;
+        int hl, qt;
+        tile_of(st, hl, qt);
+        const int hq = g * grp + hl;
+        const int qs = qt * S::BM;
         const size_t ho = ((size_t)b * Hq + hq) * N;
         qtile.issue(make_rsrc(q + ho * D, (uint32_t)N * D * 2), qs, N,
                     P == 0 ? q_lds0 : P == 1 ? q_lds1 : q_lds2, wave);
@@ -314,12 +419,14 @@ __global__ __launch_bounds__(512) void bwd_dkdv_split_kernel(
     // rank of key block kt among the key blocks that add into that tile
     // (those whose query range, first_qt .. n_qt - 1 above, holds it).
     auto turn_of = [&](int st) {
-        const int hq = g * grp + st / steps_per_head;
-        const int qt = first_qt + st % steps_per_head;
+        int hl, qt;
+        tile_of(st, hl, qt);
+        const int hq = g * grp + hl;
         return sync + kSyncHead + (((size_t)b * Hq + hq) * (NP / S::BM) + qt) * 4 + slice;
     };
     auto rank_of = [&](int st) {
-        const int qt = first_qt + st % steps_per_head;
+        int hl, qt;
+        tile_of(st, hl, qt);
         const int num = S::BM * qt - (S::BN - 2) - window;
         return kt - (CAUSAL && num > 0 ? (num + S::BN - 1) / S::BN : 0);
     };
@@ -334,38 +441,159 @@ __global__ __launch_bounds__(512) void bwd_dkdv_split_kernel(
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         if (lane == 0) __hip_atomic_fetch_add(turn_of(st), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     };
-    auto dq_update = [&](int st) {
-        const int hq = g * grp + st / steps_per_head;
-        const int qs = (first_qt + st % steps_per_head) * S::BM;
+    // dQ tile tt (32 x 32) of the step whose dS^T is in dst_lds, unscaled.
+    auto dq_tile = [&](int tt) {
+        const int qb = tt / S::DBLK, db = tt % S::DBLK;
+        const uint32_t a0 = tr_off(8 * h, 32 * qb + 16 * (g16 & 1), lane, S::BM);
+        const uint32_t a1 = tr_off(8 * h + 4, 32 * qb + 16 * (g16 & 1), lane, S::BM);
+        const uint32_t b0 = tr_off(8 * h, 32 * db + 16 * (g16 & 1), lane, D);
+        const uint32_t b1 = tr_off(8 * h + 4, 32 * db + 16 * (g16 & 1), lane, D);
+        f32x16 c = {};
+#pragma unroll
+        for (int ks = 0; ks < S::BN / 16; ks++) {
+            const char *al = dst_lds + 16 * ks * S::BM * 2;
+            const char *bl = k_lds + 16 * ks * D * 2;
+            c = mfma32(join_bf16x8(lds_read_tr16(al, a0), lds_read_tr16(al, a1)),
+                       join_bf16x8(lds_read_tr16(bl, b0), lds_read_tr16(bl, b1)), c);
+        }
+        return c;
+    };
+    // dQ[qs + tile tt rows] += scale * c with fp32 atomics.
+    auto dq_add = [&](float *dqh, int qs, int tt, const f32x16 &c) {
+        const int qb = tt / S::DBLK, db = tt % S::DBLK;
+        float *dqt = dqh + (size_t)(qs + 32 * qb + 4 * h) * D + 32 * db + col;
+        if (qs + S::BM <= N) {
+#pragma unroll
+            for (int r = 0; r < 16; r++)
+                unsafeAtomicAdd(dqt + (8 * (r >> 2) + (r & 3)) * D, c[r] * scale);
+        } else {
+#pragma unroll
+            for (int r = 0; r < 16; r++)
+                if (qs + 32 * qb + 4 * h + 8 * (r >> 2) + (r & 3) < N)
+                    unsafeAtomicAdd(dqt + (8 * (r >> 2) + (r & 3)) * D, c[r] * scale);
+        }
+    };
+    constexpr int TILES = 2 * S::DBLK;  // 32 x 32 dQ tiles per step
+    constexpr int NT = TILES / 4;       // ... per B wave: tiles slice, slice + 4, ...
+    // Paired atomic mode, exchange e = st (a step both key blocks of the
+    // pair walk) of this B wave; the partner block's wave with the same slice
+    // holds the other partial of the same dQ tiles.
+    //  - Each of the two adds 1 to the exchange word on arrival (bits 0-1
+    //    count the arrivals).
+    //  - The first to arrive stores its partial into ring slot
+    //    e % pair_slots, once the slot's previous use is complete (its
+    //    counter equals e / pair_slots), adds 4 to the word when the stores
+    //    have completed, and issues no atomics.  The second waits for that 4,
+    //    adds the stored partial to its own, issues the atomics for both and
+    //    then raises the slot counter.
+    //  - A first arrival that finds the slot still in use waits for it only
+    //    if the partner has already arrived at the slot's previous use
+    //    (exchange e - pair_slots), which then completes without anything
+    //    further from this wave; otherwise it raises the counter itself,
+    //    adds 8 instead, and both add their own partials.
+    // Every wait is bounded and waits for a wave that has started and needs
+    // nothing from the waiting one, so no dispatch order can deadlock.  The
+    // ring is written and read with device-scope (sc1) stores and loads,
+    // visible across XCDs without an L2 write-back or invalidate.
+    const size_t pair_id = (size_t)bg * ((KT + 1) / 2) + (kt >> 1);
+    const size_t xwords = (size_t)BHkv * ((KT + 1) / 2) * grp * (NP / S::BM) * 4;
+    // Returns 0 (partial handed over: no atomics), 1 (add c) or 2 (add c,
+    // which now holds both partials, then raise *freec).
+    auto word_of = [&](int st) {
+        return sync + kSyncHead + (pair_id * (size_t)(grp * (NP / S::BM)) + st) * 4 + slice;
+    };
+    auto freec_of = [&](int st) {
+        return sync + kSyncHead + xwords + (pair_id * pair_slots + st % pair_slots) * 4 + slice;
+    };
+    // The arrival at exchange st (and a first read of its slot counter) is
+    // made at the end of step st, once dS is known, so that both values are
+    // back by the time the exchange runs at the start of step st + 1.
+    int arr_t = 0, arr_fv = 0;  // lane 0: returned word, slot counter
+    auto arrive = [&](int st) {
+        if (lane == 0) {
+            arr_t = __hip_atomic_fetch_add(word_of(st), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            arr_fv = __hip_atomic_load(freec_of(st), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    };
+    auto exchange = [&](int st, f32x16 (&c)[NT], int *&freec) __attribute__((always_inline)) {
+        int *word = word_of(st);
+        const int slot = st % pair_slots;
+        freec = freec_of(st);
+        const auto rs = __builtin_amdgcn_make_buffer_rsrc(
+            xring + ((pair_id * pair_slots + slot) * 4 + slice) * (16 * D), 0, 16 * D * 4, 0x00020000);
+        const int t = __builtin_amdgcn_readfirstlane(arr_t);
+        int fv = __builtin_amdgcn_readfirstlane(arr_fv);
+        if (!(t & 1)) {
+            if (fv != st / pair_slots) {
+                int prev = 0;
+                if (lane == 0)
+                    prev = __hip_atomic_load(word - 4 * pair_slots, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+                prev = __builtin_amdgcn_readfirstlane(prev);
+                if ((prev & 3) == 2) fv = wait_count(freec, st / pair_slots, sync, lane);
+            }
+            if (fv == st / pair_slots) {
+#pragma unroll
+                for (int i = 0; i < NT; i++)
+#pragma unroll
+                    for (int j = 0; j < 4; j++) {
+                        const f32x4 v4 = {c[i][4 * j], c[i][4 * j + 1], c[i][4 * j + 2], c[i][4 * j + 3]};
+                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v4), rs,
+                                                               ((i * 4 + j) * 64 + lane) * 16, 0, kSc1);
+                    }
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                if (lane == 0) __hip_atomic_fetch_add(word, 4, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                return 0;
+            }
+            if (lane == 0) {
+                __hip_atomic_fetch_add(freec, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_fetch_add(word, 8, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            return 1;
+        }
+        const int w = (t & 12) ? t : wait_flag(word, sync, lane);
+        if (w & 4) {
+#pragma unroll
+            for (int i = 0; i < NT; i++)
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    const f32x4 v4 = __builtin_bit_cast(
+                        f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, ((i * 4 + j) * 64 + lane) * 16, 0, kSc1));
+#pragma unroll
+                    for (int r = 0; r < 4; r++) c[i][4 * j + r] += v4[r];
+                }
+            return 2;
+        }
+        return 1;
+    };
+    auto dq_update = [&](int st) __attribute__((always_inline)) {
+        int hl, qt;
+        tile_of(st, hl, qt);
+        const int hq = g * grp + hl;
+        const int qs = qt * S::BM;
         float *dqh = dq + ((size_t)b * Hq + hq) * N * D;
-        constexpr int TILES = 2 * S::DBLK;
+        if (DQ == kDqPaired && paired && st < n_common) {
+            f32x16 c[NT];
+#pragma unroll
+            for (int i = 0; i < NT; i++) c[i] = dq_tile(slice + 4 * i);
+            int *freec;
+            const int how = exchange(st, c, freec);
+            if (how != 0) {
+#pragma unroll
+                for (int i = 0; i < NT; i++) dq_add(dqh, qs, slice + 4 * i, c[i]);
+            }
+            // The ring loads have returned (the sums used them): free the
+            // slot, after those uses in program order.
+            asm volatile("" ::: "memory");
+            if (how == 2 && lane == 0)
+                __hip_atomic_fetch_add(freec, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            return;
+        }
 #pragma unroll
         for (int tt = slice; tt < TILES; tt += 4) {
-            const int qb = tt / S::DBLK, db = tt % S::DBLK;
-            const uint32_t a0 = tr_off(8 * h, 32 * qb + 16 * (g16 & 1), lane, S::BM);
-            const uint32_t a1 = tr_off(8 * h + 4, 32 * qb + 16 * (g16 & 1), lane, S::BM);
-            const uint32_t b0 = tr_off(8 * h, 32 * db + 16 * (g16 & 1), lane, D);
-            const uint32_t b1 = tr_off(8 * h + 4, 32 * db + 16 * (g16 & 1), lane, D);
-            f32x16 c = {};
-#pragma unroll
-            for (int ks = 0; ks < S::BN / 16; ks++) {
-                const char *al = dst_lds + 16 * ks * S::BM * 2;
-                const char *bl = k_lds + 16 * ks * D * 2;
-                c = mfma32(join_bf16x8(lds_read_tr16(al, a0), lds_read_tr16(al, a1)),
-                           join_bf16x8(lds_read_tr16(bl, b0), lds_read_tr16(bl, b1)), c);
-            }
-            float *dqt = dqh + (size_t)(qs + 32 * qb + 4 * h) * D + 32 * db + col;
+            const f32x16 c = dq_tile(tt);
             if (ORDERED && tt == slice) wait_turn(turn_of(st), rank_of(st), sync, lane);
-            if (qs + S::BM <= N) {
-#pragma unroll
-                for (int r = 0; r < 16; r++)
-                    unsafeAtomicAdd(dqt + (8 * (r >> 2) + (r & 3)) * D, c[r] * scale);
-            } else {
-#pragma unroll
-                for (int r = 0; r < 16; r++)
-                    if (qs + 32 * qb + 4 * h + 8 * (r >> 2) + (r & 3) < N)
-                        unsafeAtomicAdd(dqt + (8 * (r >> 2) + (r & 3)) * D, c[r] * scale);
-            }
+            dq_add(dqh, qs, tt, c);
         }
     };
 
@@ -387,7 +615,9 @@ __global__ __launch_bounds__(512) void bwd_dkdv_split_kernel(
 
     auto step = [&](auto slot, int st) {
         constexpr int P = decltype(slot)::value;
-        const int qs = (first_qt + st % steps_per_head) * S::BM;
+        int hl_st, qt_st;
+        tile_of(st, hl_st, qt_st);
+        const int qs = qt_st * S::BM;
         constexpr int PN = (P + 1) % NSLOT;          // slot of step st + 1
         constexpr int PP = (P + NSLOT - 1) % NSLOT;  // slot of step st - 1
         const char *ql = P == 0 ? q_lds0 : P == 1 ? q_lds1 : q_lds2;
@@ -397,13 +627,17 @@ __global__ __launch_bounds__(512) void bwd_dkdv_split_kernel(
         // wait; publish them before this step's copies are in flight (the
         // release waits for every outstanding memory operation of the wave).
         if (ORDERED && !wave_a && st > 1) release(st - 2);
+        // Paired atomic mode: the B waves add (or hand over) the previous
+        // step's dQ before this step's copies are in flight, so that a first
+        // arrival's wait for its ring stores waits for nothing else.
+        if (paired && !wave_a && st > 0) dq_update(st - 1);
         if (st + 1 < n_steps) issue(st + 1, std::integral_constant<int, PN>{});
         // Deferred mode, B waves: dK^T += Q^T dS of step st - 1 (its Q tile
         // is still in slot PP, its dS in bprev) while the A waves compute S.
         if (DEFER && !wave_a && st > 0) tr_products(PP == 0 ? q_lds0 : PP == 1 ? q_lds1 : q_lds2, bprev);
         // Atomic modes: the B waves add the previous step's dS K into dQ first
         // (no score registers live yet), while the A waves start on S.
-        if (ATOMIC_DQ && !wave_a && st > 0) dq_update(st - 1);
+        if (ATOMIC_DQ && !paired && !wave_a && st > 0) dq_update(st - 1);
 
         // A: S = Q K^T.  B: dP = dO V^T.  (rows = queries, one key per lane)
         const char *rl = wave_a ? ql : dol;
@@ -435,7 +669,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_split_kernel(
                                    (CAUSAL && (qs < kv0 + S::BN - 1 || qs + S::BM - 1 - kv0 >= window));
             // Slope / scale of this step's query head.
             const float bias_a =
-                BIAS ? slopes[g * grp + st / steps_per_head] * (kLog2e / scale_log2) : 0.f;
+                BIAS ? slopes[g * grp + hl_st] * (kLog2e / scale_log2) : 0.f;
             auto softmax = [&](auto masked) {
                 constexpr bool MASK = decltype(masked)::value;
 #pragma unroll
@@ -502,6 +736,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_split_kernel(
                     *reinterpret_cast<i16x4 *>(dst_lds + tile_off(kin, 2 * ks, S::BM) + 8 * h) = lo;
                     *reinterpret_cast<i16x4 *>(dst_lds + tile_off(kin, 2 * ks + 1, S::BM) + 8 * h) = hi;
                 }
+                if (DQ == kDqPaired && paired && st < n_common) arrive(st);
             }
         }
         if (DEFER && !wave_a) {
@@ -812,14 +1047,18 @@ static hipError_t launch_bwd_t(const BwdArgs &a)
     (void)hipGetLastError();  // clear an error left by an earlier, unrelated call
     const int BH = a.B * a.Hq;
     const float scale_log2 = a.scale * kLog2e;
+    // Atomic mode with a pair block and ring in the workspace.
+    const bool pairs = a.mode == kBwdAtomicPaired;
     {
         constexpr int RPB = 256 / (D / 8);
         const size_t rows = (size_t)BH * pad_rows(a.N);
         const unsigned grid = (unsigned)((rows + RPB - 1) / RPB);
+        const size_t n_sync = a.mode == kBwdOrdered ? bwd_sync_words(BH, a.N)
+                              : pairs ? bwd_pair_words(a.B, a.Hq, a.Hkv, a.N, a.pair_slots)
+                                      : (size_t)0;
         hipLaunchKernelGGL(bwd_pre_kernel<D>, dim3(grid), dim3(256), 0, a.stream,
                            (const uint16_t *)a.dout, a.o, a.lse, a.delta, a.lse2, a.dq, BH, a.N,
-                           a.mode == kBwdSeparate ? 0 : 1, a.sync,
-                           a.mode == kBwdOrdered ? bwd_sync_words(BH, a.N) : (size_t)0);
+                           a.mode == kBwdSeparate ? 0 : 1, n_sync ? a.sync : nullptr, n_sync);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -843,17 +1082,20 @@ static hipError_t launch_bwd_t(const BwdArgs &a)
         const int BHkv = a.B * a.Hkv;
         auto kern = a.mode == kBwdSeparate  ? bwd_dkdv_split_kernel<D, CAUSAL, kDqNone>
                     : a.mode == kBwdOrdered ? bwd_dkdv_split_kernel<D, CAUSAL, kDqOrdered>
+                    : pairs                 ? bwd_dkdv_split_kernel<D, CAUSAL, kDqPaired>
                                             : bwd_dkdv_split_kernel<D, CAUSAL, kDqAtomic>;
         if (a.slopes)
             kern = a.mode == kBwdSeparate  ? bwd_dkdv_split_kernel<D, CAUSAL, kDqNone, true>
                  : a.mode == kBwdOrdered ? bwd_dkdv_split_kernel<D, CAUSAL, kDqOrdered, true>
+                 : pairs                 ? bwd_dkdv_split_kernel<D, CAUSAL, kDqPaired, true>
                                          : bwd_dkdv_split_kernel<D, CAUSAL, kDqAtomic, true>;
         hipLaunchKernelGGL(kern, dim3(BHkv * KT), dim3(S::THREADS), 0, a.stream,
                            (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v,
                            (const uint16_t *)a.dout, a.lse2, a.delta, a.dq, a.dk, a.dv, a.Hq,
                            a.Hkv, a.N, BHkv, KT, a.scale, scale_log2,
                            a.window > 0 ? a.window : kNoWindow,
-                           a.mode == kBwdOrdered ? a.sync : nullptr, a.slopes, a.linear_map);
+                           a.mode == kBwdOrdered || pairs ? a.sync : nullptr, a.slopes, a.linear_map,
+                           pairs ? a.xring : nullptr, pairs ? a.pair_slots : 0);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

@@ -24,8 +24,10 @@ struct FwdArgs {
 };
 
 // How the backward sums dQ: fp32 atomics from the dK/dV kernel; a separate
-// pass that owns each dQ row; or the dK/dV kernel's atomics in a fixed order.
-constexpr int kBwdAtomic = 0, kBwdSeparate = 1, kBwdOrdered = 2;
+// pass that owns each dQ row; the dK/dV kernel's atomics in a fixed order; or
+// its atomics with pairs of key blocks sharing one set (the values of
+// FA_BWD_ATOMIC .. FA_BWD_ATOMIC_PAIRED).
+constexpr int kBwdAtomic = 0, kBwdSeparate = 1, kBwdOrdered = 2, kBwdAtomicPaired = 3;
 
 // Ordered mode's int32 workspace block: the ticket counter, the count of
 // timed-out waits, then (from word kSyncHead on) the turn counters, four per
@@ -33,21 +35,47 @@ constexpr int kBwdAtomic = 0, kBwdSeparate = 1, kBwdOrdered = 2;
 constexpr int kSyncTicket = 0, kSyncTimeouts = 1, kSyncHead = 64;
 inline size_t bwd_sync_words(int BH, int N) { return kSyncHead + (size_t)BH * (((N + 63) & ~63) / 16); }
 
+// Paired atomic mode: key blocks 2p and 2p + 1 (128 keys each) of
+// one kv head hand one block's partial dQ tile to the other, which adds the
+// sum, so each pair issues one set of dQ atomics instead of two.  Int32 block
+// (zeroed by the preprocess): the header (word kSyncTimeouts counts timed-out
+// waits), then one exchange word per (pair, query head of the group, 64-row
+// tile, B wave), then one slot counter per (pair, ring slot, B wave).  The
+// ring itself (not zeroed) holds pairs x slots x 4 B waves partial tiles of
+// 64 x d / 4 fp32.
+constexpr int kPairSlots = 2;
+inline size_t bwd_key_pairs(int N) { return (size_t)((N + 127) / 128 + 1) / 2; }
+inline size_t bwd_pair_xwords(int B, int Hq, int N)
+{
+    return (size_t)B * Hq * bwd_key_pairs(N) * (size_t)((N + 63) / 64) * 4;
+}
+inline size_t bwd_pair_words(int B, int Hq, int Hkv, int N, int slots)
+{
+    return kSyncHead + bwd_pair_xwords(B, Hq, N) + (size_t)B * Hkv * bwd_key_pairs(N) * slots * 4;
+}
+inline size_t bwd_pair_ring_bytes(int B, int Hkv, int N, int d, int slots)
+{
+    return (size_t)B * Hkv * bwd_key_pairs(N) * slots * 4 * (size_t)(64 * d);  // 64 x d / 4 fp32
+}
+
 struct BwdArgs {
     const void *q, *k, *v, *dout;
     const float *o, *lse;
     float *dq, *dk, *dv;
     float *delta;  // workspace: D_i = sum_c dO_ic O_ic, [B, Hq, N]
     float *lse2;   // workspace: LSE_i * log2(e), [B, Hq, N]
-    int *sync;     // workspace, ordered mode only: ticket, timeouts, turn counters
+    int *sync;     // workspace: ordered mode's ticket, timeouts and turn counters, or the
+                   // paired atomic mode's pair block (null in the other two modes)
     int B, Hq, Hkv, N, d;
     float scale;
     bool causal;
-    int mode;      // kBwdAtomic, kBwdSeparate or kBwdOrdered
+    int mode;      // kBwdAtomic, kBwdSeparate, kBwdOrdered or kBwdAtomicPaired
     int window;    // causal sliding window in keys (0: none)
     hipStream_t stream;
     const float *slopes = nullptr;  // linear position bias: slope per query head, [Hq] fp32
     int linear_map = 0;             // 1: workgroups in plain order (measurement switch)
+    float *xring = nullptr;         // paired atomic mode: the partial-tile ring
+    int pair_slots = 0;             // ... and its slots per pair (kPairSlots)
 };
 
 hipError_t launch_fwd(const FwdArgs &a);

@@ -143,9 +143,9 @@ size_t fa_fwd_splitkv_workspace_bytes(int B, int Hq, int Hkv, int N, int d, int 
 
 /*
  * dQ modes of fa_bwd (its `deterministic` argument).
- *   FA_BWD_ATOMIC:   the dK/dV kernel adds each key block's dS K into dq with
- *                    fp32 atomic adds in whatever order they land (bits may
- *                    differ from run to run).
+ *   FA_BWD_ATOMIC:   the dK/dV kernel adds each key block's dS K into dq
+ *                    with fp32 atomic adds in whatever order they land
+ *                    (bits may differ from run to run).
  *   FA_BWD_SEPARATE: a separate pass owns each dq row and sums it in
  *                    registers, no atomics (bitwise identical run to run).
  *   FA_BWD_ORDERED:  the same atomic adds, made in ascending key-block order
@@ -153,10 +153,20 @@ size_t fa_fwd_splitkv_workspace_bytes(int B, int Hq, int Hkv, int N, int d, int 
  *                    workspace (bitwise identical run to run): the
  *                    semaphore-ordered reduction the page "FlashAttention-4"
  *                    names under "Limitations" for its deterministic mode.
+ *   FA_BWD_ATOMIC_PAIRED: as FA_BWD_ATOMIC with half the atomic adds (the
+ *                    restructured dQ of the page "FlashAttention-4", Key
+ *                    Contributions item 3): key blocks 2p and 2p + 1 (128
+ *                    keys each) of a kv head are paired, and for every query
+ *                    tile both see one block hands its partial dQ tile to
+ *                    the other through the workspace, which adds the sum.
+ *                    On MI355X the hand-over's round trips through memory
+ *                    cost more time than the atomics it saves, so
+ *                    FA_BWD_ATOMIC is the faster of the two.
  */
 #define FA_BWD_ATOMIC 0
 #define FA_BWD_SEPARATE 1
 #define FA_BWD_ORDERED 2
+#define FA_BWD_ATOMIC_PAIRED 3
 
 /*
  * Bytes of device workspace fa_bwd needs for this shape and dQ mode: the
@@ -168,6 +178,12 @@ size_t fa_fwd_splitkv_workspace_bytes(int B, int Hq, int Hkv, int N, int d, int 
  * that block counts the waits for a turn that gave up after about 2 s; it is
  * 0 after every call whose dq is bitwise reproducible (a non-zero count
  * leaves dq the correct sum, added in an unspecified order).
+ * FA_BWD_ATOMIC_PAIRED adds, at the same offset, the pairing block: int32
+ * words, 64 + 4 * B * Hq * P * ceil(N / 64) + 8 * B * Hkv * P of them with
+ * P = ceil(ceil(N / 128) / 2) key-block pairs per kv head, rounded up to 256
+ * bytes, then the hand-over ring, 2 * 4 * B * Hkv * P tiles of 64 * d bytes.
+ * Word 1 of the block counts hand-overs whose wait gave up after about 2 s;
+ * it is 0 after every call whose dq holds every key block's contribution.
  * Returns 0 for an invalid shape or mode.
  */
 size_t fa_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d, int deterministic);
@@ -179,9 +195,10 @@ size_t fa_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d, int determin
  *   dout      bf16 [B, Hq, N, d], the gradient of the loss w.r.t. o (read)
  *   dq        fp32 [B, Hq,  N, d]  (written)
  *   dk, dv    fp32 [B, Hkv, N, d]  (written; summed over each group's heads)
- *   deterministic: the dQ mode, FA_BWD_ATOMIC (0), FA_BWD_SEPARATE (1)
- *     or FA_BWD_ORDERED (2), above; any other value is FA_ERR_SHAPE.  The
- *     reproducible modes repeat bit for bit on the same device and shape.
+ *   deterministic: the dQ mode, FA_BWD_ATOMIC (0), FA_BWD_SEPARATE (1),
+ *     FA_BWD_ORDERED (2) or FA_BWD_ATOMIC_PAIRED (3), above; any other
+ *     value is FA_ERR_SHAPE.  The reproducible modes repeat bit for bit on
+ *     the same device and shape.
  *   workspace / workspace_bytes: device scratch of at least
  *     fa_bwd_workspace_bytes(...) bytes, 16-byte aligned, owned by the
  *     caller; its contents on entry are ignored.

@@ -169,14 +169,32 @@ def test_bwd_rejects(kw, status):
     assert bwd(**kw) == status
 
 
+def r256(x):
+    return (x + 255) // 256 * 256
+
+
+def atomic_pair_bytes(B, Hq, Hkv, N, d):
+    """The paired atomic mode's pairing block and hand-over ring, as fa.h lays them out."""
+    P = (-(-N // 128) + 1) // 2
+    words = 64 + 4 * B * Hq * P * (-(-N // 64)) + 8 * B * Hkv * P
+    return r256(4 * words) + 2 * 4 * B * Hkv * P * 64 * d
+
+
 def test_workspace_bytes():
     rows = 2 * 16 * 8192
-    per = (rows * 4 + 255) // 256 * 256
+    per = r256(rows * 4)
     for det in (0, 1):
         assert fa.fa_bwd_workspace_bytes(2, 16, 16, 8192, 128, det) == 2 * per
+    assert fa.fa_bwd_workspace_bytes(2, 16, 16, 8192, 128, 3) == \
+        2 * per + atomic_pair_bytes(2, 16, 16, 8192, 128)
     # rows are padded to a multiple of 64 per head: N = 3 -> 64 rows per head
     assert fa.fa_bwd_workspace_bytes(1, 2, 2, 3, 64, 0) == 2 * 512
+    assert fa.fa_bwd_workspace_bytes(1, 2, 2, 3, 64, 3) == 2 * 512 + atomic_pair_bytes(1, 2, 2, 3, 64)
     assert fa.fa_bwd_workspace_bytes(1, 1, 1, 65, 64, 1) == 2 * 512
+    # grouped heads: exchange words per query head, ring per kv head
+    assert fa.fa_bwd_workspace_bytes(1, 32, 8, 32768, 128, 3) == \
+        2 * r256(32 * 32768 * 4) + atomic_pair_bytes(1, 32, 8, 32768, 128)
+    assert fa.fa_bwd_workspace_bytes(1, 2, 2, 3, 64, 4) == 0
     assert fa.fa_bwd_workspace_bytes(0, 2, 2, 3, 64, 0) == 0
     assert fa.fa_bwd_workspace_bytes(1, 2, 2, 3, 48, 0) == 0
     # exactly the required size passes validation far enough to reach the other checks
@@ -205,7 +223,7 @@ def test_single_hip_runtime_in_process():
     assert out == "1"
 
 
-@pytest.mark.parametrize("mode", [-1, 3, 1 << 20])
+@pytest.mark.parametrize("mode", [-1, 4, 1 << 20])
 def test_bwd_rejects_unknown_dq_mode(mode):
     assert fa.fa_bwd_workspace_bytes(1, 2, 2, 128, 64, mode) == 0
     assert bwd(deterministic=mode) == 2
@@ -224,10 +242,13 @@ def test_bwd_ordered_workspace_bytes():
         sync = ((64 + 4 * B * Hq * npad // 64) * 4 + 255) // 256 * 256
         assert fa.fa_bwd_workspace_bytes(B, Hq, Hkv, N, d, fa.BWD_SEPARATE) == 2 * rows
         assert fa.fa_bwd_workspace_bytes(B, Hq, Hkv, N, d, fa.BWD_ATOMIC) == 2 * rows
+        assert fa.fa_bwd_workspace_bytes(B, Hq, Hkv, N, d, fa.BWD_ATOMIC_PAIRED) == \
+            2 * rows + atomic_pair_bytes(B, Hq, Hkv, N, d)
         assert fa.fa_bwd_workspace_bytes(B, Hq, Hkv, N, d, fa.BWD_ORDERED) == 2 * rows + sync
-    need = fa.fa_bwd_workspace_bytes(1, 2, 2, 128, 64, fa.BWD_ORDERED)
-    assert bwd(deterministic=fa.BWD_ORDERED, workspace_bytes=need - 1) == 5
-    assert bwd(deterministic=fa.BWD_ORDERED, workspace_bytes=need, dq=MIS) == 4
+    for mode in (fa.BWD_ORDERED, fa.BWD_ATOMIC_PAIRED):
+        need = fa.fa_bwd_workspace_bytes(1, 2, 2, 128, 64, mode)
+        assert bwd(deterministic=mode, workspace_bytes=need - 1) == 5
+        assert bwd(deterministic=mode, workspace_bytes=need, dq=MIS) == 4
 
 
 def test_alibi_validates():
@@ -247,7 +268,7 @@ def test_alibi_validates():
     assert fa.fa_bwd_alibi(**dict(bargs, slopes=None)) == 1
     assert fa.fa_bwd_alibi(**dict(bargs, slopes=A + 1)) == 4
     assert fa.fa_bwd_alibi(**dict(bargs, dk=None)) == 1
-    assert fa.fa_bwd_alibi(**dict(bargs, deterministic=3)) == 2
+    assert fa.fa_bwd_alibi(**dict(bargs, deterministic=4)) == 2
     assert fa.fa_bwd_alibi(**dict(bargs, workspace_bytes=16)) == 5
     assert fa.fa_bwd_alibi(**dict(bargs, dv=MIS)) == 4
 
@@ -262,7 +283,7 @@ def test_noalloc_checks_arguments_before_the_device():
     assert fa.fa_bwd_noalloc(**base) == 5
     assert fa.fa_bwd_noalloc(**{**base, "dq": None}) == 1
     assert fa.fa_bwd_noalloc(**{**base, "dk": MIS}) == 4
-    assert fa.fa_bwd_noalloc(**{**base, "deterministic": 3}) == 2
+    assert fa.fa_bwd_noalloc(**{**base, "deterministic": 4}) == 2
     assert fa.fa_bwd_noalloc(**{**base, "d": 96}) == 3
     src = open(os.path.join(ROOT, "include", "fa.h")).read()
     assert "#define FA_NOALLOC_MAX_WORKSPACE ((size_t)32 << 20)" in src

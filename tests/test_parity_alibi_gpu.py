@@ -118,7 +118,7 @@ def alibi_bwd_case(N, d, causal):
     return q, k, v, do, sweep_slopes(Hq, N + 7), 1 / math.sqrt(d)
 
 
-@pytest.mark.parametrize("mode", [0, 1, 2])
+@pytest.mark.parametrize("mode", [0, 1, 2, 3])
 @pytest.mark.parametrize("N,d,causal", BWD_SWEEP)
 def test_alibi_bwd_small(fa, N, d, causal, mode):
     """End to end: fa_fwd_alibi, then fa_bwd_alibi on its O and LSE."""
@@ -132,7 +132,7 @@ def test_alibi_bwd_small(fa, N, d, causal, mode):
     check_alibi_grads(got, ref, bars, floors, MEAN_ABS_FEW_TERMS if N < 64 else MEAN_ABS)
 
 
-@pytest.mark.parametrize("mode", [0, 1, 2])
+@pytest.mark.parametrize("mode", [0, 1, 2, 3])
 @pytest.mark.parametrize("N,d,causal", BWD_SWEEP)
 def test_alibi_bwd_small_isolated(fa, N, d, causal, mode):
     """The backward alone: fa_bwd_alibi on the oracle's O and LSE (fp32)."""
@@ -166,7 +166,7 @@ def test_alibi_long_causal(fa):
     tail = oracle.bwd_groups_tail(q, k, v, do, scale, row0, groups, slopes=a)
     head = oracle.bwd_groups_head(q, k, v, do, scale, True, 256, groups, slopes=a)
     grp = Hq // Hkv
-    for mode in (0, 1, 2):
+    for mode in (0, 1, 2, 3):
         note(f"  dQ mode {mode}")
         dq, dk, dv = gpu_bwd_alibi(fa, q, k, v, do, o, lse, st, scale, True, mode)
         dq, dk, dv = dq.reshape(Hkv, grp, N, d), dk.reshape(Hkv, N, d), dv.reshape(Hkv, N, d)

@@ -12,6 +12,7 @@ zones: afterwards the guards must still be NaN (nothing written out of bounds)
 and the output must hold no NaN (every element written).
 """
 import math
+import os
 from dataclasses import replace
 import sys
 
@@ -117,6 +118,50 @@ def check_ordered_counters(fa, ws, B, Hq, Hkv, N, d, causal, window):
     assert (turns == want[None, :, None]).all(), "turn counters"
 
 
+def check_pair_words(fa, ws, B, Hq, Hkv, N, d, causal, window):
+    """After an atomic-mode call with key-block pairing: no hand-over wait
+    timed out; the exchange word of every (pair, query head, 64-row tile both
+    blocks of the pair see, B wave) ends at 6 (partial handed over: two
+    arrivals + 4) or 10 (both added their own: two arrivals + 8), every
+    other word at 0; and
+    each ring-slot counter equals the number of exchanges that used its slot
+    (exchange e uses slot e % 2).  Returns the fraction handed over."""
+    torch.cuda.synchronize()
+    off = fa.fa_bwd_workspace_bytes(B, Hq, Hkv, N, d, fa.BWD_SEPARATE)
+    words = ws[off:].cpu().numpy().view(np.int32)
+    assert words[1] == 0, f"{words[1]} hand-over waits timed out"
+    KT, QT, grp, R = (N + 127) // 128, (N + 63) // 64, Hq // Hkv, 2
+    P = (KT + 1) // 2
+    W = window if window else 1 << 40
+
+    def sees(kt, qt):
+        r0, r1 = 64 * qt, min(N, 64 * qt + 64) - 1
+        k0, k1 = 128 * kt, min(N, 128 * kt + 128) - 1
+        return (not causal) or (k0 <= r1 and r0 - k1 < W)
+
+    xw = words[64:64 + B * Hkv * P * grp * QT * 4].reshape(B * Hkv, P, grp * QT, 4)
+    slots = words[64 + xw.size:64 + xw.size + B * Hkv * P * R * 4].reshape(B * Hkv, P, R, 4)
+    want_x = np.zeros_like(xw, dtype=bool)
+    want_s = np.zeros_like(slots)
+    for p in range(P):
+        if 2 * p + 1 >= KT:
+            continue
+        common = [qt for qt in range(QT) if sees(2 * p, qt) and sees(2 * p + 1, qt)]
+        n_common = grp * len(common)
+        want_x[:, p, :n_common, :] = True
+        for e in range(n_common):
+            want_s[:, p, e % R, :] += 1
+    assert (xw[~want_x] == 0).all(), "exchange words outside the common tiles"
+    got = xw[want_x]
+    assert np.isin(got, (6, 10)).all(), f"exchange words {np.unique(got)}"
+    assert (slots == want_s).all(), f"ring-slot counters {slots.tolist()} != {want_s.tolist()}; words {xw.tolist()}"
+    LAST_HANDOVER[0] = float((got == 6).mean()) if got.size else 0.0
+    return LAST_HANDOVER[0]
+
+
+LAST_HANDOVER = [0.0]  # hand-over fraction of the last paired atomic call
+
+
 def gpu_bwd(fa, q, k, v, dout, o, lse, scale, causal, deterministic):
     B, Hq, N, d = q.shape
     Hkv = k.shape[1]
@@ -129,6 +174,8 @@ def gpu_bwd(fa, q, k, v, dout, o, lse, scale, causal, deterministic):
     assert st == 0, fa.fa_status_string(st)
     if deterministic == fa.BWD_ORDERED:
         check_ordered_counters(fa, ws, B, Hq, Hkv, N, d, causal, 0)
+    if deterministic == fa.BWD_ATOMIC_PAIRED:
+        check_pair_words(fa, ws, B, Hq, Hkv, N, d, causal, 0)
     return dq.result("dq"), dk.result("dk"), dv.result("dv")
 
 
@@ -154,7 +201,7 @@ def test_fwd_small(fa, N, d, causal):
     compare_lse(lse, lse_ref)
 
 
-MODES = [0, 1, 2]  # dQ modes: atomic, separate pass, ordered atomics
+MODES = [0, 1, 2, 3]  # dQ modes: atomic, separate pass, ordered atomics, paired atomics
 
 
 @pytest.mark.parametrize("N,d,causal", SWEEP)
@@ -381,6 +428,8 @@ def test_workload_backward_both_modes(fa):
     for det in MODES:
         note(f"  deterministic={det}")
         dq, dk, dv = gpu_bwd(fa, x["q"], x["k"], x["v"], x["dout"], o, lse, w.scale, w.causal, det)
+        if det == 3:
+            note(f"  dQ partials handed over: {LAST_HANDOVER[0]:.3f} of the pairs' exchanges")
         results[det] = (dq, dk, dv)
         compare("dq", dq, ref["dq"])
         compare("dk", dk, ref["dk"])
@@ -399,12 +448,50 @@ def test_workload_backward_both_modes(fa):
         again = gpu_bwd(fa, x["q"], x["k"], x["v"], x["dout"], o, lse, w.scale, w.causal, det)
         for a, b_ in zip(again, results[det]):
             assert np.array_equal(a.view(np.uint32), b_.view(np.uint32))
-    for a, b_ in zip(results[0], results[1]):
-        assert float(np.abs(a - b_).max()) <= 5e-3
-    # dK and dV do not depend on the dQ mode: the same kernel computes them
-    for m in (0, 2):
-        for a, b_ in zip(results[m][1:], results[1][1:]):
-            assert np.array_equal(a.view(np.uint32), b_.view(np.uint32))
+    for m in (0, 3):
+        for a, b_ in zip(results[m], results[1]):
+            assert float(np.abs(a - b_).max()) <= 5e-3
+    # dK and dV do not depend on the dQ mode: the same kernel computes them,
+    # in the same order of query tiles except where the atomic mode pairs key
+    # blocks (the tiles both blocks of a pair see come first).
+    for a, b_ in zip(results[2][1:], results[1][1:]):
+        assert np.array_equal(a.view(np.uint32), b_.view(np.uint32))
+    for a, b_ in zip(results[0][1:], results[1][1:]):
+        assert np.array_equal(a.view(np.uint32), b_.view(np.uint32))
+    for a, b_ in zip(results[3][1:], results[1][1:]):
+        assert float(np.abs(a - b_).max()) <= 1e-4
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_atomic_paired_mode(fa, causal):
+    """The paired atomic mode on a GQA input with a ragged key tail (an odd
+    number of 128-key blocks, so one block has no partner): partials are
+    handed over, and it meets the oracle's bars like the plain atomic mode;
+    dK and dV are the same sums (the same bits when every query tile is
+    shared, i.e. without the causal mask)."""
+    B, Hq, Hkv, N, d = 1, 8, 2, 1400, 128
+    note(f"atomic paired B={B} Hq={Hq} Hkv={Hkv} N={N} d={d} causal={causal}")
+    q, k, v = (random_bf16((B, Hq, N, d), 41), random_bf16((B, Hkv, N, d), 42),
+               random_bf16((B, Hkv, N, d), 43))
+    dout = random_bf16((B, Hq, N, d), 44)
+    scale = 1 / math.sqrt(d)
+    o, lse = gpu_fwd(fa, q, k, v, scale, causal)
+    ref = oracle.bwd(q, k, v, dout, scale, causal)
+    from bf16_floor import backward_bars
+    bars, _ = backward_bars(q, k, v, dout, scale, causal, ref)
+    paired = gpu_bwd(fa, q, k, v, dout, o, lse, scale, causal, fa.BWD_ATOMIC_PAIRED)
+    note(f"  handed over: {LAST_HANDOVER[0]:.3f}")
+    assert LAST_HANDOVER[0] > 0.0
+    plain = gpu_bwd(fa, q, k, v, dout, o, lse, scale, causal, fa.BWD_ATOMIC)
+    for got in (paired, plain):
+        for name, a in zip(("dq", "dk", "dv"), got):
+            compare(name, a, ref[name], MEAN_ABS, max_bar=bars[name])
+    for a, b_ in zip(paired[1:], plain[1:]):
+        if causal:
+            assert float(np.abs(a - b_).max()) <= 1e-4
+        else:
+            assert np.array_equal(a.view(np.uint32), b_.view(np.uint32)), "dK, dV"
+    assert float(np.abs(paired[0] - plain[0]).max()) <= 1e-4
 
 
 @pytest.mark.parametrize("causal", [False, True])
@@ -603,6 +690,8 @@ def gpu_bwd_window(fa, q, k, v, dout, o, lse, scale, window, deterministic):
     assert st == 0, fa.fa_status_string(st)
     if deterministic == fa.BWD_ORDERED:
         check_ordered_counters(fa, ws, B, Hq, Hkv, N, d, True, window)
+    if deterministic == fa.BWD_ATOMIC_PAIRED:
+        check_pair_words(fa, ws, B, Hq, Hkv, N, d, True, window)
     return dq.result("dq"), dk.result("dk"), dv.result("dv")
 
 
@@ -793,7 +882,7 @@ def test_graph_capture_replays(fa, mode):
         torch.cuda.synchronize()
         for name, t, e in zip(("o", "lse", "dq", "dk", "dv"), outs, eager):
             assert not torch.isnan(t).any(), f"replay {rep}: {name} not written"
-            if name == "dq" and mode == 0:
+            if name == "dq" and mode in (0, 3):
                 assert float((t - e).abs().max()) <= 1e-5, f"replay {rep}: dq"
             else:
                 assert torch.equal(t.view(torch.int32), e.view(torch.int32)), f"replay {rep}: {name}"
