@@ -211,9 +211,12 @@ __device__ __forceinline__ int wait_count(const int *count, int want, int *sync,
     return c;
 }
 
-// Cache-policy bits of a buffer load or store: sc1, device scope (the
-// access is coherent for every XCD of the device).
-constexpr int kSc1 = 16;
+// Number of the XCD (accelerator complex die) this wave runs on: the
+// hardware register XCC_ID, bits 3:0.
+__device__ __forceinline__ int xcd_id()
+{
+    return __builtin_amdgcn_s_getreg((31 << 11) | 20) & 15;  // hwreg(HW_REG_XCC_ID)
+}
 
 // Paired atomic mode: waits (the whole wave) until the exchange word has
 // bit 2 or 3 set (value 4 or 8) and returns it; 0 after kTurnTimeout ticks (counted in
@@ -306,6 +309,28 @@ __global__ __launch_bounds__(512) void bwd_dkdv_split_kernel(
         }
         kt = hw / BHkv;
         bg = hw % BHkv;
+    } else if (DQ == kDqPaired && pair_slots > 0) {
+        // Workgroups hw and hw + 8 (same hw % 8, so the same XCD under the
+        // round-robin dispatch) are the two key blocks of one pair:
+        // hw = 16 a + 8 m + x gives pair 8 a + x, member m.  With B Hkv a
+        // multiple of 8 each XCD works through whole heads (their Q and dO
+        // stay in its L2).  The grid is rounded up to 16: ids past the last
+        // pair, and the missing partner of an odd block count, exit here.
+        const int P = (KT + 1) / 2;
+        const int hw = blockIdx.x;
+        const int pid = (hw >> 4) * 8 + (hw & 7), m = (hw >> 3) & 1;
+        if (pid >= BHkv * P) return;
+        int p;
+        if (!linear_map && BHkv % kNumXcd == 0) {
+            const int per = BHkv / kNumXcd, a = pid / kNumXcd, x = pid % kNumXcd;
+            bg = x * per + a / P;
+            p = a % P;
+        } else {
+            bg = pid / P;
+            p = pid % P;
+        }
+        kt = 2 * p + m;
+        if (kt >= KT) return;
     } else {
         xcd_tile_map(blockIdx.x, BHkv, KT, false, linear_map, bg, kt);
     }
@@ -491,12 +516,23 @@ __global__ __launch_bounds__(512) void bwd_dkdv_split_kernel(
     //    (exchange e - pair_slots), which then completes without anything
     //    further from this wave; otherwise it raises the counter itself,
     //    adds 8 instead, and both add their own partials.
+    //  - The hand-over goes through the L2 of one XCD: the first arrival
+    //    stores with plain stores (they reach the XCD's L2) and adds 4 once
+    //    they have completed; the second invalidates its compute unit's L1
+    //    (buffer_inv sc0) and loads.  It is taken only when the partner
+    //    workgroup has published the same XCD number as this one (each
+    //    workgroup publishes its number at its start); otherwise the first
+    //    arrival takes the "add 8" path and both add their own partials.
     // Every wait is bounded and waits for a wave that has started and needs
-    // nothing from the waiting one, so no dispatch order can deadlock.  The
-    // ring is written and read with device-scope (sc1) stores and loads,
-    // visible across XCDs without an L2 write-back or invalidate.
+    // nothing from the waiting one, so no dispatch order can deadlock.
     const size_t pair_id = (size_t)bg * ((KT + 1) / 2) + (kt >> 1);
     const size_t xwords = (size_t)BHkv * ((KT + 1) / 2) * grp * (NP / S::BM) * 4;
+    // This workgroup's XCD number + 1 and the partner's published one.
+    int *const xcd_words = sync + kSyncHead + xwords + (size_t)BHkv * ((KT + 1) / 2) * pair_slots * 4;
+    const int my_xcd = xcd_id() + 1;
+    if (DQ == kDqPaired && paired && tid == 0)
+        __hip_atomic_store(xcd_words + pair_id * 2 + (kt & 1), my_xcd, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
     // Returns 0 (partial handed over: no atomics), 1 (add c) or 2 (add c,
     // which now holds both partials, then raise *freec).
     auto word_of = [&](int st) {
@@ -508,11 +544,13 @@ __global__ __launch_bounds__(512) void bwd_dkdv_split_kernel(
     // The arrival at exchange st (and a first read of its slot counter) is
     // made at the end of step st, once dS is known, so that both values are
     // back by the time the exchange runs at the start of step st + 1.
-    int arr_t = 0, arr_fv = 0;  // lane 0: returned word, slot counter
+    int arr_t = 0, arr_fv = 0, arr_px = 0;  // lane 0: returned word, slot counter, partner's XCD
     auto arrive = [&](int st) {
         if (lane == 0) {
             arr_t = __hip_atomic_fetch_add(word_of(st), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             arr_fv = __hip_atomic_load(freec_of(st), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            arr_px = __hip_atomic_load(xcd_words + pair_id * 2 + ((kt & 1) ^ 1), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
         }
     };
     auto exchange = [&](int st, f32x16 (&c)[NT], int *&freec) __attribute__((always_inline)) {
@@ -523,8 +561,9 @@ __global__ __launch_bounds__(512) void bwd_dkdv_split_kernel(
             xring + ((pair_id * pair_slots + slot) * 4 + slice) * (16 * D), 0, 16 * D * 4, 0x00020000);
         const int t = __builtin_amdgcn_readfirstlane(arr_t);
         int fv = __builtin_amdgcn_readfirstlane(arr_fv);
+        const bool same_xcd = __builtin_amdgcn_readfirstlane(arr_px) == my_xcd;
         if (!(t & 1)) {
-            if (fv != st / pair_slots) {
+            if (same_xcd && fv != st / pair_slots) {
                 int prev = 0;
                 if (lane == 0)
                     prev = __hip_atomic_load(word - 4 * pair_slots, __ATOMIC_RELAXED,
@@ -532,14 +571,14 @@ __global__ __launch_bounds__(512) void bwd_dkdv_split_kernel(
                 prev = __builtin_amdgcn_readfirstlane(prev);
                 if ((prev & 3) == 2) fv = wait_count(freec, st / pair_slots, sync, lane);
             }
-            if (fv == st / pair_slots) {
+            if (same_xcd && fv == st / pair_slots) {
 #pragma unroll
                 for (int i = 0; i < NT; i++)
 #pragma unroll
                     for (int j = 0; j < 4; j++) {
                         const f32x4 v4 = {c[i][4 * j], c[i][4 * j + 1], c[i][4 * j + 2], c[i][4 * j + 3]};
                         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v4), rs,
-                                                               ((i * 4 + j) * 64 + lane) * 16, 0, kSc1);
+                                                               ((i * 4 + j) * 64 + lane) * 16, 0, 0);
                     }
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
                 if (lane == 0) __hip_atomic_fetch_add(word, 4, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -553,12 +592,16 @@ __global__ __launch_bounds__(512) void bwd_dkdv_split_kernel(
         }
         const int w = (t & 12) ? t : wait_flag(word, sync, lane);
         if (w & 4) {
+            // The partner ran on this XCD and its stores are in this L2;
+            // drop any copy of the ring slot this compute unit's L1 holds
+            // from an earlier exchange.
+            asm volatile("buffer_inv sc0" ::: "memory");
 #pragma unroll
             for (int i = 0; i < NT; i++)
 #pragma unroll
                 for (int j = 0; j < 4; j++) {
                     const f32x4 v4 = __builtin_bit_cast(
-                        f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, ((i * 4 + j) * 64 + lane) * 16, 0, kSc1));
+                        f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, ((i * 4 + j) * 64 + lane) * 16, 0, 0));
 #pragma unroll
                     for (int r = 0; r < 4; r++) c[i][4 * j + r] += v4[r];
                 }
@@ -623,6 +666,11 @@ __global__ __launch_bounds__(512) void bwd_dkdv_split_kernel(
         const char *ql = P == 0 ? q_lds0 : P == 1 ? q_lds1 : q_lds2;
         const char *dol = P == 0 ? do_lds0 : P == 1 ? do_lds1 : do_lds2;
         const char *rows = P == 0 ? rows0 : P == 1 ? rows1 : rows2;
+        // This lane's byte offset into the row stage (its rows are 4 h + 8 j
+        // + ...); laundered each step so that the compiler does not keep one
+        // hoisted offset register per row group, which costs spills.
+        uint32_t hoff = 16 * h;
+        asm volatile("" : "+v"(hoff));
         // Ordered mode: step st - 2's adds completed at the last end-of-step
         // wait; publish them before this step's copies are in flight (the
         // release waits for every outstanding memory operation of the wave).
@@ -677,7 +725,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_split_kernel(
 #pragma unroll
                     for (int gq = 0; gq < 4; gq++) {
                         const int qr = 32 * qb + 8 * gq + 4 * h;
-                        const f32x4 l2 = lds_read_f32x4(rows, qr * 4);
+                        const f32x4 l2 = lds_read_f32x4(rows, hoff + (32 * qb + 8 * gq) * 4);
 #pragma unroll
                         for (int i = 0; i < 4; i++) {
                             float xs = x[qb][4 * gq + i];
@@ -714,8 +762,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_split_kernel(
             for (int qb = 0; qb < 2; qb++) {
 #pragma unroll
                 for (int gq = 0; gq < 4; gq++) {
-                    const int qr = 32 * qb + 8 * gq + 4 * h;
-                    const f32x4 dl = lds_read_f32x4(rows, (S::BM + qr) * 4);
+                    const f32x4 dl = lds_read_f32x4(rows, hoff + (S::BM + 32 * qb + 8 * gq) * 4);
                     const f32x4 pv = *reinterpret_cast<const f32x4 *>(xchg + (qb * 4 + gq) * 1024);
 #pragma unroll
                     for (int i = 0; i < 4; i++) x[qb][4 * gq + i] = pv[i] * (x[qb][4 * gq + i] - dl[i]);
@@ -1089,7 +1136,11 @@ static hipError_t launch_bwd_t(const BwdArgs &a)
                  : a.mode == kBwdOrdered ? bwd_dkdv_split_kernel<D, CAUSAL, kDqOrdered, true>
                  : pairs                 ? bwd_dkdv_split_kernel<D, CAUSAL, kDqPaired, true>
                                          : bwd_dkdv_split_kernel<D, CAUSAL, kDqAtomic, true>;
-        hipLaunchKernelGGL(kern, dim3(BHkv * KT), dim3(S::THREADS), 0, a.stream,
+        // Paired atomic mode: two workgroups per key-block pair, rounded up to
+        // 16 (see the kernel's pair map).
+        const unsigned grid =
+            pairs ? (unsigned)((2 * BHkv * ((KT + 1) / 2) + 15) / 16 * 16) : (unsigned)(BHkv * KT);
+        hipLaunchKernelGGL(kern, dim3(grid), dim3(S::THREADS), 0, a.stream,
                            (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v,
                            (const uint16_t *)a.dout, a.lse2, a.delta, a.dq, a.dk, a.dv, a.Hq,
                            a.Hkv, a.N, BHkv, KT, a.scale, scale_log2,

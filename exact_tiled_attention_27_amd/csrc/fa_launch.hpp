@@ -37,12 +37,15 @@ inline size_t bwd_sync_words(int BH, int N) { return kSyncHead + (size_t)BH * ((
 
 // Paired atomic mode: key blocks 2p and 2p + 1 (128 keys each) of
 // one kv head hand one block's partial dQ tile to the other, which adds the
-// sum, so each pair issues one set of dQ atomics instead of two.  Int32 block
-// (zeroed by the preprocess): the header (word kSyncTimeouts counts timed-out
-// waits), then one exchange word per (pair, query head of the group, 64-row
-// tile, B wave), then one slot counter per (pair, ring slot, B wave).  The
-// ring itself (not zeroed) holds pairs x slots x 4 B waves partial tiles of
-// 64 x d / 4 fp32.
+// sum, so each pair issues one set of dQ atomics instead of two.  The
+// hand-over goes through the L2 the two workgroups share when they run on
+// the same XCD; otherwise both add their own.  Int32 block (zeroed by the
+// preprocess): the header (word kSyncTimeouts counts timed-out waits), then
+// one exchange word per (pair, query head of the group, 64-row tile, B wave),
+// then one slot counter per (pair, ring slot, B wave), then the XCD number
+// + 1 of each workgroup of each pair (two words per pair).  The ring itself
+// (not zeroed) holds pairs x slots x 4 B waves partial tiles of 64 x d / 4
+// fp32.
 constexpr int kPairSlots = 2;
 inline size_t bwd_key_pairs(int N) { return (size_t)((N + 127) / 128 + 1) / 2; }
 inline size_t bwd_pair_xwords(int B, int Hq, int N)
@@ -51,7 +54,7 @@ inline size_t bwd_pair_xwords(int B, int Hq, int N)
 }
 inline size_t bwd_pair_words(int B, int Hq, int Hkv, int N, int slots)
 {
-    return kSyncHead + bwd_pair_xwords(B, Hq, N) + (size_t)B * Hkv * bwd_key_pairs(N) * slots * 4;
+    return kSyncHead + bwd_pair_xwords(B, Hq, N) + (size_t)B * Hkv * bwd_key_pairs(N) * (slots * 4 + 2);
 }
 inline size_t bwd_pair_ring_bytes(int B, int Hkv, int N, int d, int slots)
 {

@@ -43,7 +43,12 @@
  *     moves forward exponentials from the transcendental unit to a cubic
  *     polynomial on the FMA units (page "FlashAttention-4", Key Contributions
  *     item 2): "1" all of them, "4" one in four; unset or any other value,
- *     none (the default, and the faster choice on this chip).
+ *     none (the default, and the faster choice on this chip).  The
+ *     polynomial's relative error is at most 7.5e-5 (a minimax fit below
+ *     bf16's half ulp), and it clamps its argument at -127: masked scores
+ *     (-inf) and scores more than 127 below the row's reference contribute
+ *     2^-127 each instead of 0, which is below fp32 rounding of a row sum
+ *     that is at least 1.
  *   - The environment variable FA_RESCALE_TAU, read on every forward call,
  *     replaces the rescale threshold 8 by another finite value >= 0 (0:
  *     rescale whenever the running maximum grows); the result is the same
@@ -159,9 +164,10 @@ size_t fa_fwd_splitkv_workspace_bytes(int B, int Hq, int Hkv, int N, int d, int 
  *                    keys each) of a kv head are paired, and for every query
  *                    tile both see one block hands its partial dQ tile to
  *                    the other through the workspace, which adds the sum.
- *                    On MI355X the hand-over's round trips through memory
- *                    cost more time than the atomics it saves, so
- *                    FA_BWD_ATOMIC is the faster of the two.
+ *                    The hand-over goes through the L2 of the XCD both
+ *                    workgroups run on; a pair whose workgroups run on
+ *                    different XCDs adds both partials with atomics (the
+ *                    result is the same sum either way).
  */
 #define FA_BWD_ATOMIC 0
 #define FA_BWD_SEPARATE 1
@@ -179,7 +185,7 @@ size_t fa_fwd_splitkv_workspace_bytes(int B, int Hq, int Hkv, int N, int d, int 
  * 0 after every call whose dq is bitwise reproducible (a non-zero count
  * leaves dq the correct sum, added in an unspecified order).
  * FA_BWD_ATOMIC_PAIRED adds, at the same offset, the pairing block: int32
- * words, 64 + 4 * B * Hq * P * ceil(N / 64) + 8 * B * Hkv * P of them with
+ * words, 64 + 4 * B * Hq * P * ceil(N / 64) + 10 * B * Hkv * P of them with
  * P = ceil(ceil(N / 128) / 2) key-block pairs per kv head, rounded up to 256
  * bytes, then the hand-over ring, 2 * 4 * B * Hkv * P tiles of 64 * d bytes.
  * Word 1 of the block counts hand-overs whose wait gave up after about 2 s;

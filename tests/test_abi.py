@@ -176,7 +176,7 @@ def r256(x):
 def atomic_pair_bytes(B, Hq, Hkv, N, d):
     """The paired atomic mode's pairing block and hand-over ring, as fa.h lays them out."""
     P = (-(-N // 128) + 1) // 2
-    words = 64 + 4 * B * Hq * P * (-(-N // 64)) + 8 * B * Hkv * P
+    words = 64 + 4 * B * Hq * P * (-(-N // 64)) + 10 * B * Hkv * P
     return r256(4 * words) + 2 * 4 * B * Hkv * P * 64 * d
 
 

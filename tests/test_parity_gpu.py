@@ -123,9 +123,10 @@ def check_pair_words(fa, ws, B, Hq, Hkv, N, d, causal, window):
     timed out; the exchange word of every (pair, query head, 64-row tile both
     blocks of the pair see, B wave) ends at 6 (partial handed over: two
     arrivals + 4) or 10 (both added their own: two arrivals + 8), every
-    other word at 0; and
-    each ring-slot counter equals the number of exchanges that used its slot
-    (exchange e uses slot e % 2).  Returns the fraction handed over."""
+    other word at 0; each ring-slot counter equals the number of exchanges
+    that used its slot (exchange e uses slot e % 2); and every paired
+    workgroup published an XCD number + 1 in 1..8.  Returns the fraction
+    handed over."""
     torch.cuda.synchronize()
     off = fa.fa_bwd_workspace_bytes(B, Hq, Hkv, N, d, fa.BWD_SEPARATE)
     words = ws[off:].cpu().numpy().view(np.int32)
@@ -141,6 +142,13 @@ def check_pair_words(fa, ws, B, Hq, Hkv, N, d, causal, window):
 
     xw = words[64:64 + B * Hkv * P * grp * QT * 4].reshape(B * Hkv, P, grp * QT, 4)
     slots = words[64 + xw.size:64 + xw.size + B * Hkv * P * R * 4].reshape(B * Hkv, P, R, 4)
+    xcd = words[64 + xw.size + slots.size:64 + xw.size + slots.size + B * Hkv * P * 2].reshape(
+        B * Hkv, P, 2)
+    for p in range(P):
+        # Blocks with a partner publish their XCD number + 1; the last,
+        # unpaired block of an odd count publishes nothing.
+        want = (1, 8) if 2 * p + 1 < KT else (0, 0)
+        assert ((xcd[:, p, :] >= want[0]) & (xcd[:, p, :] <= want[1])).all(), f"XCD words {xcd[:, p, :]}"
     want_x = np.zeros_like(xw, dtype=bool)
     want_s = np.zeros_like(slots)
     for p in range(P):
