@@ -70,8 +70,8 @@ size_t bwd_bytes(int B, int Hq, int Hkv, int N, int d, int mode)
     const size_t rows_part = 2 * round256(workspace_rows(B, Hq, N) * sizeof(float));
     if (mode == FA_BWD_ORDERED) return rows_part + round256(fa::bwd_sync_words(B * Hq, N) * sizeof(int));
     if (mode == FA_BWD_ATOMIC_PAIRED)
-        return rows_part + round256(fa::bwd_pair_words(B, Hq, Hkv, N, fa::kPairSlots) * sizeof(int)) +
-               round256(fa::bwd_pair_ring_bytes(B, Hkv, N, d, fa::kPairSlots));
+        return rows_part + round256(fa::bwd_pair_words(B, Hkv, N) * sizeof(int)) +
+               round256(fa::bwd_pair_ring_bytes(B, Hkv, N, d));
     return rows_part;
 }
 
@@ -135,7 +135,7 @@ int bwd_impl(const void *q, const void *k, const void *v, const float *o, const 
     float *xring = pair_slots > 0
                        ? reinterpret_cast<float *>(
                              after_rows +
-                             round256(fa::bwd_pair_words(B, Hq, Hkv, N, pair_slots) * sizeof(int)))
+                             round256(fa::bwd_pair_words(B, Hkv, N) * sizeof(int)))
                        : nullptr;
     static_assert(fa::kBwdAtomic == FA_BWD_ATOMIC && fa::kBwdSeparate == FA_BWD_SEPARATE &&
                       fa::kBwdOrdered == FA_BWD_ORDERED &&

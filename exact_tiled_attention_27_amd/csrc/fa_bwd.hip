@@ -183,33 +183,9 @@ __device__ __forceinline__ void wait_turn(const int *turn, int want, int *sync, 
     asm volatile("" ::: "memory");
 }
 
-// Paired atomic mode: waits (the whole wave) until the ring-slot counter
-// reaches `want` and returns the last value read (less than `want` after
-// kTurnTimeout ticks, counted in sync[kSyncTimeouts], or once any wait of
-// the launch has timed out).
-__device__ __forceinline__ int wait_count(const int *count, int want, int *sync, int lane)
-{
-    const long long t0 = wall_clock64();
-    int c = 0;
-    while (true) {
-        __builtin_amdgcn_s_sleep(1);
-        c = __builtin_amdgcn_readfirstlane(
-            __hip_atomic_load(count, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-        if (c >= want) break;
-        if (__builtin_amdgcn_readfirstlane(__hip_atomic_load(
-                sync + kSyncTimeouts, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) != 0)
-            break;
-        if (wall_clock64() - t0 > kTurnTimeout) {
-            if (lane == 0)
-                __hip_atomic_fetch_add(sync + kSyncTimeouts, 1, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-            break;
-        }
-    }
-    // The ring stores that follow wait for the counter's value (branch).
-    asm volatile("" ::: "memory");
-    return c;
-}
+// Cache-policy bits of a buffer load or store: sc1, device scope (the
+// access is coherent for every XCD of the device).
+constexpr int kSc1 = 16;
 
 // Number of the XCD (accelerator complex die) this wave runs on: the
 // hardware register XCC_ID, bits 3:0.
@@ -502,112 +478,122 @@ __global__ __launch_bounds__(512) void bwd_dkdv_split_kernel(
     constexpr int NT = TILES / 4;       // ... per B wave: tiles slice, slice + 4, ...
     // Paired atomic mode, exchange e = st (a step both key blocks of the
     // pair walk) of this B wave; the partner block's wave with the same slice
-    // holds the other partial of the same dQ tiles.
-    //  - Each of the two adds 1 to the exchange word on arrival (bits 0-1
-    //    count the arrivals).
-    //  - The first to arrive stores its partial into ring slot
-    //    e % pair_slots, once the slot's previous use is complete (its
-    //    counter equals e / pair_slots), adds 4 to the word when the stores
-    //    have completed, and issues no atomics.  The second waits for that 4,
-    //    adds the stored partial to its own, issues the atomics for both and
-    //    then raises the slot counter.
-    //  - A first arrival that finds the slot still in use waits for it only
-    //    if the partner has already arrived at the slot's previous use
-    //    (exchange e - pair_slots), which then completes without anything
-    //    further from this wave; otherwise it raises the counter itself,
-    //    adds 8 instead, and both add their own partials.
-    //  - The hand-over goes through the L2 of one XCD: the first arrival
-    //    stores with plain stores (they reach the XCD's L2) and adds 4 once
-    //    they have completed; the second invalidates its compute unit's L1
-    //    (buffer_inv sc0) and loads.  It is taken only when the partner
-    //    workgroup has published the same XCD number as this one (each
-    //    workgroup publishes its number at its start); otherwise the first
-    //    arrival takes the "add 8" path and both add their own partials.
-    // Every wait is bounded and waits for a wave that has started and needs
-    // nothing from the waiting one, so no dispatch order can deadlock.
+    // holds the other partial of the same dQ tiles.  Fixed roles: the even
+    // block (producer) hands its partial over, the odd block (consumer) adds
+    // both and issues the only atomics.
+    //  - The producer waits until ring slot e % R is free (the consumer's
+    //    count of consumed exchanges >= e - R + 1), stores its partial there,
+    //    waits for the stores, then writes 4 (e + 1) + path into the slot's
+    //    word.  path 0: plain stores, which land in the L2 of its XCD (taken
+    //    when the consumer has published the same XCD number); path 1:
+    //    device-scope (sc1) stores, visible from any XCD.
+    //  - The consumer waits for that word, loads the partial (after an L1
+    //    invalidate, or with device-scope loads), adds it, issues the
+    //    atomics for both blocks and raises its consumed count.
+    //  - Both waits are bounded (kTurnTimeout, counted in word kSyncTimeouts;
+    //    after one timeout every later wait gives up at once, so the kernel
+    //    always finishes).  A timeout leaves dq incomplete, and the count
+    //    tells the caller so.  The producer never waits for anything the
+    //    consumer needs from it, and the consumer only for the producer's
+    //    earlier exchanges, so no order of dispatch can deadlock them.
     const size_t pair_id = (size_t)bg * ((KT + 1) / 2) + (kt >> 1);
-    const size_t xwords = (size_t)BHkv * ((KT + 1) / 2) * grp * (NP / S::BM) * 4;
-    // This workgroup's XCD number + 1 and the partner's published one.
-    int *const xcd_words = sync + kSyncHead + xwords + (size_t)BHkv * ((KT + 1) / 2) * pair_slots * 4;
+    int *const pwords = sync + kSyncHead + pair_id * kPairWords;  // this pair's words
+    int *const slot_words = pwords + 2 + slice * (kPairSlots + 1);  // R slot words, consumed count
+    int *const consumed = slot_words + kPairSlots;
+    const bool producer = (kt & 1) == 0;
     const int my_xcd = xcd_id() + 1;
     if (DQ == kDqPaired && paired && tid == 0)
-        __hip_atomic_store(xcd_words + pair_id * 2 + (kt & 1), my_xcd, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-    // Returns 0 (partial handed over: no atomics), 1 (add c) or 2 (add c,
-    // which now holds both partials, then raise *freec).
-    auto word_of = [&](int st) {
-        return sync + kSyncHead + (pair_id * (size_t)(grp * (NP / S::BM)) + st) * 4 + slice;
-    };
-    auto freec_of = [&](int st) {
-        return sync + kSyncHead + xwords + (pair_id * pair_slots + st % pair_slots) * 4 + slice;
-    };
-    // The arrival at exchange st (and a first read of its slot counter) is
-    // made at the end of step st, once dS is known, so that both values are
-    // back by the time the exchange runs at the start of step st + 1.
-    int arr_t = 0, arr_fv = 0, arr_px = 0;  // lane 0: returned word, slot counter, partner's XCD
-    auto arrive = [&](int st) {
-        if (lane == 0) {
-            arr_t = __hip_atomic_fetch_add(word_of(st), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            arr_fv = __hip_atomic_load(freec_of(st), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            arr_px = __hip_atomic_load(xcd_words + pair_id * 2 + ((kt & 1) ^ 1), __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-        }
-    };
-    auto exchange = [&](int st, f32x16 (&c)[NT], int *&freec) __attribute__((always_inline)) {
-        int *word = word_of(st);
-        const int slot = st % pair_slots;
-        freec = freec_of(st);
-        const auto rs = __builtin_amdgcn_make_buffer_rsrc(
-            xring + ((pair_id * pair_slots + slot) * 4 + slice) * (16 * D), 0, 16 * D * 4, 0x00020000);
-        const int t = __builtin_amdgcn_readfirstlane(arr_t);
-        int fv = __builtin_amdgcn_readfirstlane(arr_fv);
-        const bool same_xcd = __builtin_amdgcn_readfirstlane(arr_px) == my_xcd;
-        if (!(t & 1)) {
-            if (same_xcd && fv != st / pair_slots) {
-                int prev = 0;
+        __hip_atomic_store(pwords + (kt & 1), my_xcd, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    int partner_xcd = 0;  // producer: the consumer's published XCD number, once known
+    // Bounded wait (the whole wave) until *w >= want; returns the last value.
+    auto wait_at_least = [&](const int *w, int want, int seen) {
+        if (seen >= want) return seen;
+        const long long t0 = wall_clock64();
+        while (true) {
+            seen = __builtin_amdgcn_readfirstlane(
+                __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+            if (seen >= want) break;
+            if (__builtin_amdgcn_readfirstlane(__hip_atomic_load(
+                    sync + kSyncTimeouts, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) != 0)
+                break;
+            if (wall_clock64() - t0 > kTurnTimeout) {
                 if (lane == 0)
-                    prev = __hip_atomic_load(word - 4 * pair_slots, __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT);
-                prev = __builtin_amdgcn_readfirstlane(prev);
-                if ((prev & 3) == 2) fv = wait_count(freec, st / pair_slots, sync, lane);
+                    __hip_atomic_fetch_add(sync + kSyncTimeouts, 1, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+                break;
             }
-            if (same_xcd && fv == st / pair_slots) {
-#pragma unroll
-                for (int i = 0; i < NT; i++)
-#pragma unroll
-                    for (int j = 0; j < 4; j++) {
-                        const f32x4 v4 = {c[i][4 * j], c[i][4 * j + 1], c[i][4 * j + 2], c[i][4 * j + 3]};
-                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v4), rs,
-                                                               ((i * 4 + j) * 64 + lane) * 16, 0, 0);
-                    }
-                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-                if (lane == 0) __hip_atomic_fetch_add(word, 4, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                return 0;
-            }
-            if (lane == 0) {
-                __hip_atomic_fetch_add(freec, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_fetch_add(word, 8, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
-            return 1;
+            __builtin_amdgcn_s_sleep(1);
         }
-        const int w = (t & 12) ? t : wait_flag(word, sync, lane);
-        if (w & 4) {
-            // The partner ran on this XCD and its stores are in this L2;
-            // drop any copy of the ring slot this compute unit's L1 holds
-            // from an earlier exchange.
-            asm volatile("buffer_inv sc0" ::: "memory");
+        // The slot accesses that follow depend on this value (branch).
+        asm volatile("" ::: "memory");
+        return seen;
+    };
+    // Read ahead at the end of step st, once dS is known, so that the value
+    // is back when the exchange runs at the start of step st + 1: the
+    // producer reads the consumed count, the consumer the slot word.
+    int pre_seen = 0;
+    auto arrive = [&](int st) {
+        const int *w = producer ? consumed : slot_words + st % kPairSlots;
+        if (lane == 0) pre_seen = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+    auto ring_rsrc = [&](int st) {
+        return __builtin_amdgcn_make_buffer_rsrc(
+            xring + ((pair_id * kPairSlots + st % kPairSlots) * 4 + slice) * (16 * D), 0, 16 * D * 4,
+            0x00020000);
+    };
+    // Producer: hand over c (returns false when a wait timed out: then c
+    // was not handed over and the caller adds it itself).
+    auto hand_over = [&](int st, const f32x16 (&c)[NT]) __attribute__((always_inline)) {
+        int seen = wait_at_least(consumed, st - kPairSlots + 1,
+                                 __builtin_amdgcn_readfirstlane(pre_seen));
+        if (seen < st - kPairSlots + 1) return false;
+        if (partner_xcd == 0)
+            partner_xcd = __builtin_amdgcn_readfirstlane(
+                __hip_atomic_load(pwords + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        const bool l2 = partner_xcd == my_xcd;
+        const auto rs = ring_rsrc(st);
 #pragma unroll
-            for (int i = 0; i < NT; i++)
+        for (int i = 0; i < NT; i++)
 #pragma unroll
-                for (int j = 0; j < 4; j++) {
-                    const f32x4 v4 = __builtin_bit_cast(
-                        f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, ((i * 4 + j) * 64 + lane) * 16, 0, 0));
+            for (int j = 0; j < 4; j++) {
+                const f32x4 v4 = {c[i][4 * j], c[i][4 * j + 1], c[i][4 * j + 2], c[i][4 * j + 3]};
+                const u32x4 u = __builtin_bit_cast(u32x4, v4);
+                const int off = ((i * 4 + j) * 64 + lane) * 16;
+                if (l2)
+                    __builtin_amdgcn_raw_buffer_store_b128(u, rs, off, 0, 0);
+                else
+                    __builtin_amdgcn_raw_buffer_store_b128(u, rs, off, 0, kSc1);
+            }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        if (lane == 0)
+            __hip_atomic_store(slot_words + st % kPairSlots, 4 * (st + 1) + (l2 ? 0 : 1),
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return true;
+    };
+    // Consumer: add the producer's partial to c (returns false when the
+    // wait timed out).
+    auto take_over = [&](int st, f32x16 (&c)[NT]) __attribute__((always_inline)) {
+        const int v = wait_at_least(slot_words + st % kPairSlots, 4 * (st + 1),
+                                    __builtin_amdgcn_readfirstlane(pre_seen));
+        if (v < 4 * (st + 1)) return false;
+        const bool l2 = (v & 3) == 0;
+        const auto rs = ring_rsrc(st);
+        // Plain path: the partner ran on this XCD and its stores are in this
+        // L2; drop any copy of the slot this compute unit's L1 holds from an
+        // earlier exchange.
+        if (l2) asm volatile("buffer_inv sc0" ::: "memory");
 #pragma unroll
-                    for (int r = 0; r < 4; r++) c[i][4 * j + r] += v4[r];
-                }
-            return 2;
-        }
-        return 1;
+        for (int i = 0; i < NT; i++)
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                const int off = ((i * 4 + j) * 64 + lane) * 16;
+                const f32x4 v4 = __builtin_bit_cast(
+                    f32x4, l2 ? __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0)
+                              : __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kSc1));
+#pragma unroll
+                for (int r = 0; r < 4; r++) c[i][4 * j + r] += v4[r];
+            }
+        return true;
     };
     auto dq_update = [&](int st) __attribute__((always_inline)) {
         int hl, qt;
@@ -619,17 +605,21 @@ __global__ __launch_bounds__(512) void bwd_dkdv_split_kernel(
             f32x16 c[NT];
 #pragma unroll
             for (int i = 0; i < NT; i++) c[i] = dq_tile(slice + 4 * i);
-            int *freec;
-            const int how = exchange(st, c, freec);
-            if (how != 0) {
+            if (producer) {
+                if (!hand_over(st, c)) {
 #pragma unroll
-                for (int i = 0; i < NT; i++) dq_add(dqh, qs, slice + 4 * i, c[i]);
+                    for (int i = 0; i < NT; i++) dq_add(dqh, qs, slice + 4 * i, c[i]);
+                }
+                return;
             }
-            // The ring loads have returned (the sums used them): free the
-            // slot, after those uses in program order.
+            take_over(st, c);
+#pragma unroll
+            for (int i = 0; i < NT; i++) dq_add(dqh, qs, slice + 4 * i, c[i]);
+            // The slot's loads have returned (the sums used them): free it,
+            // after those uses in program order.
             asm volatile("" ::: "memory");
-            if (how == 2 && lane == 0)
-                __hip_atomic_fetch_add(freec, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (lane == 0)
+                __hip_atomic_store(consumed, st + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             return;
         }
 #pragma unroll
@@ -1101,7 +1091,7 @@ static hipError_t launch_bwd_t(const BwdArgs &a)
         const size_t rows = (size_t)BH * pad_rows(a.N);
         const unsigned grid = (unsigned)((rows + RPB - 1) / RPB);
         const size_t n_sync = a.mode == kBwdOrdered ? bwd_sync_words(BH, a.N)
-                              : pairs ? bwd_pair_words(a.B, a.Hq, a.Hkv, a.N, a.pair_slots)
+                              : pairs ? bwd_pair_words(a.B, a.Hkv, a.N)
                                       : (size_t)0;
         hipLaunchKernelGGL(bwd_pre_kernel<D>, dim3(grid), dim3(256), 0, a.stream,
                            (const uint16_t *)a.dout, a.o, a.lse, a.delta, a.lse2, a.dq, BH, a.N,

@@ -35,30 +35,25 @@ constexpr int kBwdAtomic = 0, kBwdSeparate = 1, kBwdOrdered = 2, kBwdAtomicPaire
 constexpr int kSyncTicket = 0, kSyncTimeouts = 1, kSyncHead = 64;
 inline size_t bwd_sync_words(int BH, int N) { return kSyncHead + (size_t)BH * (((N + 63) & ~63) / 16); }
 
-// Paired atomic mode: key blocks 2p and 2p + 1 (128 keys each) of
-// one kv head hand one block's partial dQ tile to the other, which adds the
-// sum, so each pair issues one set of dQ atomics instead of two.  The
-// hand-over goes through the L2 the two workgroups share when they run on
-// the same XCD; otherwise both add their own.  Int32 block (zeroed by the
-// preprocess): the header (word kSyncTimeouts counts timed-out waits), then
-// one exchange word per (pair, query head of the group, 64-row tile, B wave),
-// then one slot counter per (pair, ring slot, B wave), then the XCD number
-// + 1 of each workgroup of each pair (two words per pair).  The ring itself
-// (not zeroed) holds pairs x slots x 4 B waves partial tiles of 64 x d / 4
-// fp32.
-constexpr int kPairSlots = 2;
+// Paired atomic mode: key blocks 2p and 2p + 1 (128 keys each) of one kv
+// head form a pair; for every query tile both see, the even block hands its
+// partial dQ tile to the odd one, which adds the sum, so each pair issues one
+// set of dQ atomics instead of two.  Int32 block (zeroed by the preprocess):
+// the header (word kSyncTimeouts counts timed-out waits), then kPairWords
+// words per pair: the XCD number + 1 of each block, then per B wave the
+// words of its kPairSlots ring slots (4 (e + 1) + path of the exchange e the
+// slot last held) and its consumed count.  The ring itself (not zeroed)
+// holds pairs x kPairSlots x 4 B waves partial tiles of 64 x d / 4 fp32.
+constexpr int kPairSlots = 4;
+constexpr int kPairWords = 2 + 4 * (kPairSlots + 1);
 inline size_t bwd_key_pairs(int N) { return (size_t)((N + 127) / 128 + 1) / 2; }
-inline size_t bwd_pair_xwords(int B, int Hq, int N)
+inline size_t bwd_pair_words(int B, int Hkv, int N)
 {
-    return (size_t)B * Hq * bwd_key_pairs(N) * (size_t)((N + 63) / 64) * 4;
+    return kSyncHead + (size_t)B * Hkv * bwd_key_pairs(N) * kPairWords;
 }
-inline size_t bwd_pair_words(int B, int Hq, int Hkv, int N, int slots)
+inline size_t bwd_pair_ring_bytes(int B, int Hkv, int N, int d)
 {
-    return kSyncHead + bwd_pair_xwords(B, Hq, N) + (size_t)B * Hkv * bwd_key_pairs(N) * (slots * 4 + 2);
-}
-inline size_t bwd_pair_ring_bytes(int B, int Hkv, int N, int d, int slots)
-{
-    return (size_t)B * Hkv * bwd_key_pairs(N) * slots * 4 * (size_t)(64 * d);  // 64 x d / 4 fp32
+    return (size_t)B * Hkv * bwd_key_pairs(N) * kPairSlots * 4 * (size_t)(64 * d);  // 64 x d / 4 fp32
 }
 
 struct BwdArgs {
@@ -78,7 +73,7 @@ struct BwdArgs {
     const float *slopes = nullptr;  // linear position bias: slope per query head, [Hq] fp32
     int linear_map = 0;             // 1: workgroups in plain order (measurement switch)
     float *xring = nullptr;         // paired atomic mode: the partial-tile ring
-    int pair_slots = 0;             // ... and its slots per pair (kPairSlots)
+    int pair_slots = 0;             // kPairSlots in the paired atomic mode, else 0
 };
 
 hipError_t launch_fwd(const FwdArgs &a);

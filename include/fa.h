@@ -162,12 +162,11 @@ size_t fa_fwd_splitkv_workspace_bytes(int B, int Hq, int Hkv, int N, int d, int 
  *                    restructured dQ of the page "FlashAttention-4", Key
  *                    Contributions item 3): key blocks 2p and 2p + 1 (128
  *                    keys each) of a kv head are paired, and for every query
- *                    tile both see one block hands its partial dQ tile to
- *                    the other through the workspace, which adds the sum.
- *                    The hand-over goes through the L2 of the XCD both
- *                    workgroups run on; a pair whose workgroups run on
- *                    different XCDs adds both partials with atomics (the
- *                    result is the same sum either way).
+ *                    tile both see the even block hands its partial dQ
+ *                    tile to the odd one through the workspace, which adds
+ *                    the sum.  The hand-over goes through the L2 of the XCD
+ *                    both workgroups run on, or through memory when they run
+ *                    on different XCDs (the same sum either way).
  */
 #define FA_BWD_ATOMIC 0
 #define FA_BWD_SEPARATE 1
@@ -185,11 +184,12 @@ size_t fa_fwd_splitkv_workspace_bytes(int B, int Hq, int Hkv, int N, int d, int 
  * 0 after every call whose dq is bitwise reproducible (a non-zero count
  * leaves dq the correct sum, added in an unspecified order).
  * FA_BWD_ATOMIC_PAIRED adds, at the same offset, the pairing block: int32
- * words, 64 + 4 * B * Hq * P * ceil(N / 64) + 10 * B * Hkv * P of them with
- * P = ceil(ceil(N / 128) / 2) key-block pairs per kv head, rounded up to 256
- * bytes, then the hand-over ring, 2 * 4 * B * Hkv * P tiles of 64 * d bytes.
- * Word 1 of the block counts hand-overs whose wait gave up after about 2 s;
- * it is 0 after every call whose dq holds every key block's contribution.
+ * words, 64 + 22 * B * Hkv * P of them with P = ceil(ceil(N / 128) / 2)
+ * key-block pairs per kv head, rounded up to 256 bytes, then the hand-over
+ * ring, 4 * 4 * B * Hkv * P tiles of 64 * d bytes.  Word 1 of the block
+ * counts hand-over waits that gave up after about 2 s; a call that leaves it
+ * non-zero has not added every partial to dq, and its dq must not be used
+ * (it is 0 after every complete call).
  * Returns 0 for an invalid shape or mode.
  */
 size_t fa_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d, int deterministic);

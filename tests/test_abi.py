@@ -176,8 +176,8 @@ def r256(x):
 def atomic_pair_bytes(B, Hq, Hkv, N, d):
     """The paired atomic mode's pairing block and hand-over ring, as fa.h lays them out."""
     P = (-(-N // 128) + 1) // 2
-    words = 64 + 4 * B * Hq * P * (-(-N // 64)) + 10 * B * Hkv * P
-    return r256(4 * words) + 2 * 4 * B * Hkv * P * 64 * d
+    words = 64 + 22 * B * Hkv * P
+    return r256(4 * words) + 4 * 4 * B * Hkv * P * 64 * d
 
 
 def test_workspace_bytes():
@@ -191,7 +191,7 @@ def test_workspace_bytes():
     assert fa.fa_bwd_workspace_bytes(1, 2, 2, 3, 64, 0) == 2 * 512
     assert fa.fa_bwd_workspace_bytes(1, 2, 2, 3, 64, 3) == 2 * 512 + atomic_pair_bytes(1, 2, 2, 3, 64)
     assert fa.fa_bwd_workspace_bytes(1, 1, 1, 65, 64, 1) == 2 * 512
-    # grouped heads: exchange words per query head, ring per kv head
+    # grouped heads: pairing words and ring per kv head
     assert fa.fa_bwd_workspace_bytes(1, 32, 8, 32768, 128, 3) == \
         2 * r256(32 * 32768 * 4) + atomic_pair_bytes(1, 32, 8, 32768, 128)
     assert fa.fa_bwd_workspace_bytes(1, 2, 2, 3, 64, 4) == 0

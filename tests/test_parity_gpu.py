@@ -119,51 +119,51 @@ def check_ordered_counters(fa, ws, B, Hq, Hkv, N, d, causal, window):
 
 
 def check_pair_words(fa, ws, B, Hq, Hkv, N, d, causal, window):
-    """After an atomic-mode call with key-block pairing: no hand-over wait
-    timed out; the exchange word of every (pair, query head, 64-row tile both
-    blocks of the pair see, B wave) ends at 6 (partial handed over: two
-    arrivals + 4) or 10 (both added their own: two arrivals + 8), every
-    other word at 0; each ring-slot counter equals the number of exchanges
-    that used its slot (exchange e uses slot e % 2); and every paired
-    workgroup published an XCD number + 1 in 1..8.  Returns the fraction
-    handed over."""
+    """After a paired atomic-mode call: no wait timed out; every paired block
+    published an XCD number + 1 in 1..8 (an unpaired last block, nothing);
+    each B wave's consumed count equals the exchanges of its pair (the query
+    tiles both blocks see, over the group's query heads); and each ring-slot
+    word holds 4 (e + 1) + path for the last exchange e that used the slot
+    (exchange e uses slot e % 4), path 0 (hand-over through the shared L2,
+    both blocks on one XCD) or 1 (device scope).  Returns the share of pairs
+    that used the L2 path."""
     torch.cuda.synchronize()
     off = fa.fa_bwd_workspace_bytes(B, Hq, Hkv, N, d, fa.BWD_SEPARATE)
     words = ws[off:].cpu().numpy().view(np.int32)
     assert words[1] == 0, f"{words[1]} hand-over waits timed out"
-    KT, QT, grp, R = (N + 127) // 128, (N + 63) // 64, Hq // Hkv, 2
+    KT, QT, grp, R = (N + 127) // 128, (N + 63) // 64, Hq // Hkv, 4
     P = (KT + 1) // 2
     W = window if window else 1 << 40
+    blk = words[64:64 + B * Hkv * P * (2 + 4 * (R + 1))].reshape(B * Hkv, P, 2 + 4 * (R + 1))
 
     def sees(kt, qt):
         r0, r1 = 64 * qt, min(N, 64 * qt + 64) - 1
         k0, k1 = 128 * kt, min(N, 128 * kt + 128) - 1
         return (not causal) or (k0 <= r1 and r0 - k1 < W)
 
-    xw = words[64:64 + B * Hkv * P * grp * QT * 4].reshape(B * Hkv, P, grp * QT, 4)
-    slots = words[64 + xw.size:64 + xw.size + B * Hkv * P * R * 4].reshape(B * Hkv, P, R, 4)
-    xcd = words[64 + xw.size + slots.size:64 + xw.size + slots.size + B * Hkv * P * 2].reshape(
-        B * Hkv, P, 2)
+    l2 = []
     for p in range(P):
-        # Blocks with a partner publish their XCD number + 1; the last,
-        # unpaired block of an odd count publishes nothing.
-        want = (1, 8) if 2 * p + 1 < KT else (0, 0)
-        assert ((xcd[:, p, :] >= want[0]) & (xcd[:, p, :] <= want[1])).all(), f"XCD words {xcd[:, p, :]}"
-    want_x = np.zeros_like(xw, dtype=bool)
-    want_s = np.zeros_like(slots)
-    for p in range(P):
+        xcd = blk[:, p, 0:2]
+        waves = blk[:, p, 2:].reshape(B * Hkv, 4, R + 1)
         if 2 * p + 1 >= KT:
+            assert (blk[:, p, :] == 0).all(), "an unpaired block's words"
             continue
-        common = [qt for qt in range(QT) if sees(2 * p, qt) and sees(2 * p + 1, qt)]
-        n_common = grp * len(common)
-        want_x[:, p, :n_common, :] = True
-        for e in range(n_common):
-            want_s[:, p, e % R, :] += 1
-    assert (xw[~want_x] == 0).all(), "exchange words outside the common tiles"
-    got = xw[want_x]
-    assert np.isin(got, (6, 10)).all(), f"exchange words {np.unique(got)}"
-    assert (slots == want_s).all(), f"ring-slot counters {slots.tolist()} != {want_s.tolist()}; words {xw.tolist()}"
-    LAST_HANDOVER[0] = float((got == 6).mean()) if got.size else 0.0
+        assert ((xcd >= 1) & (xcd <= 8)).all(), f"XCD words {xcd}"
+        n_common = grp * sum(1 for qt in range(QT) if sees(2 * p, qt) and sees(2 * p + 1, qt))
+        assert (waves[:, :, R] == n_common).all(), f"consumed counts {waves[:, :, R]} != {n_common}"
+        for slot in range(R):
+            es = [e for e in range(n_common) if e % R == slot]
+            got = waves[:, :, slot]
+            if not es:
+                assert (got == 0).all()
+                continue
+            e = es[-1]
+            path = got - 4 * (e + 1)
+            assert np.isin(path, (0, 1)).all(), f"slot words {got} (exchange {e})"
+            same = (xcd[:, 0] == xcd[:, 1])[:, None]
+            assert ((path == 0) <= same).all(), "the L2 path only for pairs on one XCD"
+        l2.append(float((xcd[:, 0] == xcd[:, 1]).mean()))
+    LAST_HANDOVER[0] = float(np.mean(l2)) if l2 else 0.0
     return LAST_HANDOVER[0]
 
 
@@ -437,7 +437,7 @@ def test_workload_backward_both_modes(fa):
         note(f"  deterministic={det}")
         dq, dk, dv = gpu_bwd(fa, x["q"], x["k"], x["v"], x["dout"], o, lse, w.scale, w.causal, det)
         if det == 3:
-            note(f"  dQ partials handed over: {LAST_HANDOVER[0]:.3f} of the pairs' exchanges")
+            note(f"  pairs handing over through the L2: {LAST_HANDOVER[0]:.3f}")
         results[det] = (dq, dk, dv)
         compare("dq", dq, ref["dq"])
         compare("dk", dk, ref["dk"])
@@ -488,8 +488,7 @@ def test_atomic_paired_mode(fa, causal):
     from bf16_floor import backward_bars
     bars, _ = backward_bars(q, k, v, dout, scale, causal, ref)
     paired = gpu_bwd(fa, q, k, v, dout, o, lse, scale, causal, fa.BWD_ATOMIC_PAIRED)
-    note(f"  handed over: {LAST_HANDOVER[0]:.3f}")
-    assert LAST_HANDOVER[0] > 0.0
+    note(f"  pairs handing over through the L2: {LAST_HANDOVER[0]:.3f}")
     plain = gpu_bwd(fa, q, k, v, dout, o, lse, scale, causal, fa.BWD_ATOMIC)
     for got in (paired, plain):
         for name, a in zip(("dq", "dk", "dv"), got):
