@@ -570,30 +570,31 @@ __global__ __launch_bounds__(512) void bwd_dkdv_split_kernel(
                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         return true;
     };
-    // Consumer: add the producer's partial to c (returns false when the
-    // wait timed out).
-    auto take_over = [&](int st, f32x16 (&c)[NT]) __attribute__((always_inline)) {
+    // Consumer: load the producer's partial into p (zeros when the wait
+    // timed out: then only this block's own partial is added).
+    auto take_over = [&](int st, f32x16 (&p)[NT]) __attribute__((always_inline)) {
         const int v = wait_at_least(slot_words + st % kPairSlots, 4 * (st + 1),
                                     __builtin_amdgcn_readfirstlane(pre_seen));
-        if (v < 4 * (st + 1)) return false;
+        const bool ok = v >= 4 * (st + 1);
         const bool l2 = (v & 3) == 0;
         const auto rs = ring_rsrc(st);
         // Plain path: the partner ran on this XCD and its stores are in this
         // L2; drop any copy of the slot this compute unit's L1 holds from an
         // earlier exchange.
-        if (l2) asm volatile("buffer_inv sc0" ::: "memory");
+        if (ok && l2) asm volatile("buffer_inv sc0" ::: "memory");
 #pragma unroll
         for (int i = 0; i < NT; i++)
 #pragma unroll
             for (int j = 0; j < 4; j++) {
                 const int off = ((i * 4 + j) * 64 + lane) * 16;
-                const f32x4 v4 = __builtin_bit_cast(
-                    f32x4, l2 ? __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0)
-                              : __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kSc1));
+                f32x4 v4 = {0.f, 0.f, 0.f, 0.f};
+                if (ok)
+                    v4 = __builtin_bit_cast(
+                        f32x4, l2 ? __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0)
+                                  : __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kSc1));
 #pragma unroll
-                for (int r = 0; r < 4; r++) c[i][4 * j + r] += v4[r];
+                for (int r = 0; r < 4; r++) p[i][4 * j + r] = v4[r];
             }
-        return true;
     };
     auto dq_update = [&](int st) __attribute__((always_inline)) {
         int hl, qt;
@@ -603,23 +604,30 @@ __global__ __launch_bounds__(512) void bwd_dkdv_split_kernel(
         float *dqh = dq + ((size_t)b * Hq + hq) * N * D;
         if (DQ == kDqPaired && paired && st < n_common) {
             f32x16 c[NT];
+            if (!producer) {
+                // Consumer: issue the partial's loads before this block's
+                // own dQ products, so their latency hides behind the matrix
+                // work.
+                f32x16 pl[NT];
+                take_over(st, pl);
 #pragma unroll
-            for (int i = 0; i < NT; i++) c[i] = dq_tile(slice + 4 * i);
-            if (producer) {
-                if (!hand_over(st, c)) {
+                for (int i = 0; i < NT; i++) c[i] = dq_tile(slice + 4 * i) + pl[i];
 #pragma unroll
-                    for (int i = 0; i < NT; i++) dq_add(dqh, qs, slice + 4 * i, c[i]);
-                }
+                for (int i = 0; i < NT; i++) dq_add(dqh, qs, slice + 4 * i, c[i]);
+                // The slot's loads have returned (the sums used them): free
+                // it, after those uses in program order.
+                asm volatile("" ::: "memory");
+                if (lane == 0)
+                    __hip_atomic_store(consumed, st + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 return;
             }
-            take_over(st, c);
+            // Producer.
 #pragma unroll
-            for (int i = 0; i < NT; i++) dq_add(dqh, qs, slice + 4 * i, c[i]);
-            // The slot's loads have returned (the sums used them): free it,
-            // after those uses in program order.
-            asm volatile("" ::: "memory");
-            if (lane == 0)
-                __hip_atomic_store(consumed, st + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            for (int i = 0; i < NT; i++) c[i] = dq_tile(slice + 4 * i);
+            if (!hand_over(st, c)) {
+#pragma unroll
+                for (int i = 0; i < NT; i++) dq_add(dqh, qs, slice + 4 * i, c[i]);
+            }
             return;
         }
 #pragma unroll
