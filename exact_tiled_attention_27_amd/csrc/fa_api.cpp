@@ -61,6 +61,17 @@ int linear_map()
     return (e && std::strcmp(e, "linear") == 0) ? 1 : 0;
 }
 
+// FA_PAIR_PATH=memory makes the paired atomic mode hand its partials over
+// with device-scope stores and loads even when both blocks of a pair run on
+// one XCD (the path taken otherwise only for pairs split across XCDs): a
+// switch for testing that path and measuring what the L2 path gains.  Read
+// on every call.
+int pair_memory()
+{
+    const char *e = std::getenv("FA_PAIR_PATH");
+    return (e && std::strcmp(e, "memory") == 0) ? 1 : 0;
+}
+
 bool valid_bwd_mode(int mode) { return mode >= FA_BWD_ATOMIC && mode <= FA_BWD_ATOMIC_PAIRED; }
 
 // Backward workspace bytes for dQ mode `mode`: the D and LSE2 rows, then the
@@ -143,7 +154,8 @@ int bwd_impl(const void *q, const void *k, const void *v, const float *o, const 
                   "dQ mode values");
     fa::BwdArgs a{q, k, v, dout, o, lse, dq, dk, dv, delta, lse2, sync, B, Hq, Hkv, N, d, scale,
                   causal != 0, deterministic, window < N ? window : 0,
-                  reinterpret_cast<hipStream_t>(stream), slopes, linear_map(), xring, pair_slots};
+                  reinterpret_cast<hipStream_t>(stream), slopes, linear_map(), xring, pair_slots,
+                  pair_memory()};
     return hip_status(fa::launch_bwd(a));
 }
 

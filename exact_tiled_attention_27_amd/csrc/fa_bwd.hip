@@ -235,7 +235,8 @@ __global__ __launch_bounds__(512) void bwd_dkdv_split_kernel(
     const float *__restrict__ lse2, const float *__restrict__ delta, float *__restrict__ dq,
     float *__restrict__ dk, float *__restrict__ dv, int Hq, int Hkv, int N, int BHkv, int KT,
     float scale, float scale_log2, int window, int *__restrict__ sync,
-    const float *__restrict__ slopes, int linear_map, float *__restrict__ xring, int pair_slots)
+    const float *__restrict__ slopes, int linear_map, float *__restrict__ xring, int pair_slots,
+    int pair_memory)
 {
     using S = DkdvSplitShape<D>;
     constexpr bool ATOMIC_DQ = DQ != kDqNone;
@@ -485,8 +486,9 @@ __global__ __launch_bounds__(512) void bwd_dkdv_split_kernel(
     //    count of consumed exchanges >= e - R + 1), stores its partial there,
     //    waits for the stores, then writes 4 (e + 1) + path into the slot's
     //    word.  path 0: plain stores, which land in the L2 of its XCD (taken
-    //    when the consumer has published the same XCD number); path 1:
-    //    device-scope (sc1) stores, visible from any XCD.
+    //    when the consumer has published the same XCD number, unless
+    //    pair_memory asks for path 1 throughout); path 1: device-scope (sc1)
+    //    stores, visible from any XCD.
     //  - The consumer waits for that word, loads the partial (after an L1
     //    invalidate, or with device-scope loads), adds it, issues the
     //    atomics for both blocks and raises its consumed count.
@@ -550,7 +552,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_split_kernel(
         if (partner_xcd == 0)
             partner_xcd = __builtin_amdgcn_readfirstlane(
                 __hip_atomic_load(pwords + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-        const bool l2 = partner_xcd == my_xcd;
+        const bool l2 = partner_xcd == my_xcd && !pair_memory;
         const auto rs = ring_rsrc(st);
 #pragma unroll
         for (int i = 0; i < NT; i++)
@@ -1144,7 +1146,8 @@ static hipError_t launch_bwd_t(const BwdArgs &a)
                            a.Hkv, a.N, BHkv, KT, a.scale, scale_log2,
                            a.window > 0 ? a.window : kNoWindow,
                            a.mode == kBwdOrdered || pairs ? a.sync : nullptr, a.slopes, a.linear_map,
-                           pairs ? a.xring : nullptr, pairs ? a.pair_slots : 0);
+                           pairs ? a.xring : nullptr, pairs ? a.pair_slots : 0,
+                           pairs ? a.pair_memory : 0);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

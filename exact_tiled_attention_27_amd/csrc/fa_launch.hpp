@@ -74,6 +74,7 @@ struct BwdArgs {
     int linear_map = 0;             // 1: workgroups in plain order (measurement switch)
     float *xring = nullptr;         // paired atomic mode: the partial-tile ring
     int pair_slots = 0;             // kPairSlots in the paired atomic mode, else 0
+    int pair_memory = 0;            // 1: paired hand-over through memory even within one XCD
 };
 
 hipError_t launch_fwd(const FwdArgs &a);

@@ -60,6 +60,11 @@
  *     default order gains.  Every workgroup computes the same values either
  *     way, so the outputs are the same bits (apart from dQ in FA_BWD_ATOMIC
  *     mode, whose order of additions is unspecified in any case).
+ *   - The environment variable FA_PAIR_PATH, read on every backward call,
+ *     set to "memory" makes FA_BWD_ATOMIC_PAIRED hand its partial dQ tiles
+ *     over through memory (device-scope stores and loads) for every pair,
+ *     not only for pairs whose workgroups run on different XCDs: the same
+ *     sums, for testing that path and measuring what the L2 path gains.
  *   - Supported: d in {64, 128}; B, Hq, Hkv, N >= 1; Hq % Hkv == 0;
  *     scale > 0 and finite; every pointer 16-byte aligned; N need not be a
  *     multiple of any tile size; one head's bf16 rows, N * d * 2 bytes, must

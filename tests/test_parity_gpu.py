@@ -118,7 +118,7 @@ def check_ordered_counters(fa, ws, B, Hq, Hkv, N, d, causal, window):
     assert (turns == want[None, :, None]).all(), "turn counters"
 
 
-def check_pair_words(fa, ws, B, Hq, Hkv, N, d, causal, window):
+def check_pair_words(fa, ws, B, Hq, Hkv, N, d, causal, window, path=None):
     """After a paired atomic-mode call: no wait timed out; every paired block
     published an XCD number + 1 in 1..8 (an unpaired last block, nothing);
     each B wave's consumed count equals the exchanges of its pair (the query
@@ -158,10 +158,12 @@ def check_pair_words(fa, ws, B, Hq, Hkv, N, d, causal, window):
                 assert (got == 0).all()
                 continue
             e = es[-1]
-            path = got - 4 * (e + 1)
-            assert np.isin(path, (0, 1)).all(), f"slot words {got} (exchange {e})"
+            path_used = got - 4 * (e + 1)
+            assert np.isin(path_used, (0, 1)).all(), f"slot words {got} (exchange {e})"
+            if path is not None:
+                assert (path_used == path).all(), f"slot words {got}: not all on path {path}"
             same = (xcd[:, 0] == xcd[:, 1])[:, None]
-            assert ((path == 0) <= same).all(), "the L2 path only for pairs on one XCD"
+            assert ((path_used == 0) <= same).all(), "the L2 path only for pairs on one XCD"
         l2.append(float((xcd[:, 0] == xcd[:, 1]).mean()))
     LAST_HANDOVER[0] = float(np.mean(l2)) if l2 else 0.0
     return LAST_HANDOVER[0]
@@ -170,7 +172,7 @@ def check_pair_words(fa, ws, B, Hq, Hkv, N, d, causal, window):
 LAST_HANDOVER = [0.0]  # hand-over fraction of the last paired atomic call
 
 
-def gpu_bwd(fa, q, k, v, dout, o, lse, scale, causal, deterministic):
+def gpu_bwd(fa, q, k, v, dout, o, lse, scale, causal, deterministic, pair_path=None):
     B, Hq, N, d = q.shape
     Hkv = k.shape[1]
     dq, dk, dv = Guarded((B, Hq, N, d)), Guarded((B, Hkv, N, d)), Guarded((B, Hkv, N, d))
@@ -183,7 +185,7 @@ def gpu_bwd(fa, q, k, v, dout, o, lse, scale, causal, deterministic):
     if deterministic == fa.BWD_ORDERED:
         check_ordered_counters(fa, ws, B, Hq, Hkv, N, d, causal, 0)
     if deterministic == fa.BWD_ATOMIC_PAIRED:
-        check_pair_words(fa, ws, B, Hq, Hkv, N, d, causal, 0)
+        check_pair_words(fa, ws, B, Hq, Hkv, N, d, causal, 0, pair_path)
     return dq.result("dq"), dk.result("dk"), dv.result("dv")
 
 
@@ -499,6 +501,31 @@ def test_atomic_paired_mode(fa, causal):
         else:
             assert np.array_equal(a.view(np.uint32), b_.view(np.uint32)), "dK, dV"
     assert float(np.abs(paired[0] - plain[0]).max()) <= 1e-4
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+def test_atomic_paired_memory_path(fa, monkeypatch, causal, d):
+    """FA_PAIR_PATH=memory: every pair hands its partials over with
+    device-scope stores and loads, the path otherwise taken only by pairs
+    whose workgroups run on different XCDs (which the default map avoids).
+    The slot words must all record that path, and the gradients meet the
+    oracle's bars.  GQA with a ragged tail and an odd number of key blocks
+    (B1 Hq8 Hkv2 N1400)."""
+    B, Hq, Hkv, N = 1, 8, 2, 1400
+    note(f"atomic paired, memory path B={B} Hq={Hq} Hkv={Hkv} N={N} d={d} causal={causal}")
+    q, k, v = (random_bf16((B, Hq, N, d), 45), random_bf16((B, Hkv, N, d), 46),
+               random_bf16((B, Hkv, N, d), 47))
+    dout = random_bf16((B, Hq, N, d), 48)
+    scale = 1 / math.sqrt(d)
+    o, lse = gpu_fwd(fa, q, k, v, scale, causal)
+    ref = oracle.bwd(q, k, v, dout, scale, causal)
+    from bf16_floor import backward_bars
+    bars, _ = backward_bars(q, k, v, dout, scale, causal, ref)
+    monkeypatch.setenv("FA_PAIR_PATH", "memory")
+    got = gpu_bwd(fa, q, k, v, dout, o, lse, scale, causal, fa.BWD_ATOMIC_PAIRED, pair_path=1)
+    for name, a in zip(("dq", "dk", "dv"), got):
+        compare(name, a, ref[name], MEAN_ABS, max_bar=bars[name])
 
 
 @pytest.mark.parametrize("causal", [False, True])
