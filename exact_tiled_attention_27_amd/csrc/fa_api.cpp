@@ -72,6 +72,20 @@ int pair_memory()
     return (e && std::strcmp(e, "memory") == 0) ? 1 : 0;
 }
 
+// FA_WAIT_TICKS replaces the longest wait of the ordered and paired modes
+// for another workgroup (100 MHz wall-clock ticks, an integer >= 0; 0: any
+// wait whose condition is not met at once gives up), so that tests can
+// exercise the timeout path; unset or invalid: 2 s.  Read on every call.
+long long wait_ticks()
+{
+    const char *e = std::getenv("FA_WAIT_TICKS");
+    if (!e) return fa::kWaitTicks;
+    char *end = nullptr;
+    const long long t = std::strtoll(e, &end, 10);
+    if (end == e || *end != '\0' || t < 0) return fa::kWaitTicks;
+    return t;
+}
+
 bool valid_bwd_mode(int mode) { return mode >= FA_BWD_ATOMIC && mode <= FA_BWD_ATOMIC_PAIRED; }
 
 // Backward workspace bytes for dQ mode `mode`: the D and LSE2 rows, then the
@@ -155,7 +169,7 @@ int bwd_impl(const void *q, const void *k, const void *v, const float *o, const 
     fa::BwdArgs a{q, k, v, dout, o, lse, dq, dk, dv, delta, lse2, sync, B, Hq, Hkv, N, d, scale,
                   causal != 0, deterministic, window < N ? window : 0,
                   reinterpret_cast<hipStream_t>(stream), slopes, linear_map(), xring, pair_slots,
-                  pair_memory()};
+                  pair_memory(), wait_ticks()};
     return hip_status(fa::launch_bwd(a));
 }
 

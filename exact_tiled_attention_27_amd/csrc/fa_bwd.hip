@@ -132,7 +132,8 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t *__restrict
 //     counts the key blocks that have added; key block kt adds when the
 //     counter equals its rank among the tile's key blocks, and raises it one
 //     step later, once the end-of-step wait has seen its atomics complete.
-//   - Every wait is bounded (kTurnTimeout ticks of the wall clock).  A wait
+//   - Every wait is bounded (wait_ticks of the 100 MHz wall clock, 2 s by
+//     default).  A wait
 //     that times out is counted in the workspace, makes every later wait of
 //     the launch give up at once, and the adds still happen: dQ is then the
 //     correct sum in an unspecified order, and the kernel always finishes.
@@ -151,11 +152,10 @@ struct DkdvSplitShape {
 
 constexpr int kDqNone = 0, kDqAtomic = 1, kDqOrdered = 2, kDqPaired = 3;
 
-// Longest wait for a turn: 2 s at the 100 MHz wall clock.
-constexpr long long kTurnTimeout = 200000000LL;
-
-// Waits (the whole wave) until *turn == want, bounded as described above.
-__device__ __forceinline__ void wait_turn(const int *turn, int want, int *sync, int lane)
+// Waits (the whole wave) until *turn == want, bounded as described above
+// (ticks: the longest wait, in 100 MHz wall-clock ticks).
+__device__ __forceinline__ void wait_turn(const int *turn, int want, int *sync, int lane,
+                                          long long ticks)
 {
     int seen = __builtin_amdgcn_readfirstlane(
         __hip_atomic_load(turn, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
@@ -169,7 +169,7 @@ __device__ __forceinline__ void wait_turn(const int *turn, int want, int *sync, 
             if (__builtin_amdgcn_readfirstlane(__hip_atomic_load(
                     sync + kSyncTimeouts, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) != 0)
                 break;
-            if (wall_clock64() - t0 > kTurnTimeout) {
+            if (wall_clock64() - t0 > ticks) {
                 if (lane == 0)
                     __hip_atomic_fetch_add(sync + kSyncTimeouts, 1, __ATOMIC_RELAXED,
                                            __HIP_MEMORY_SCOPE_AGENT);
@@ -194,38 +194,6 @@ __device__ __forceinline__ int xcd_id()
     return __builtin_amdgcn_s_getreg((31 << 11) | 20) & 15;  // hwreg(HW_REG_XCC_ID)
 }
 
-// Paired atomic mode: waits (the whole wave) until the exchange word has
-// bit 2 or 3 set (value 4 or 8) and returns it; 0 after kTurnTimeout ticks (counted in
-// sync[kSyncTimeouts]), and at once once any wait of the launch has timed
-// out, so that the kernel always finishes quickly.
-__device__ __forceinline__ int wait_flag(const int *word, int *sync, int lane)
-{
-    const long long t0 = wall_clock64();
-    int w = 0;
-    while (true) {
-        __builtin_amdgcn_s_sleep(1);
-        w = __builtin_amdgcn_readfirstlane(
-            __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-        if (w & 12) break;
-        if (__builtin_amdgcn_readfirstlane(__hip_atomic_load(
-                sync + kSyncTimeouts, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) != 0) {
-            w = 0;
-            break;
-        }
-        if (wall_clock64() - t0 > kTurnTimeout) {
-            if (lane == 0)
-                __hip_atomic_fetch_add(sync + kSyncTimeouts, 1, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-            w = 0;
-            break;
-        }
-    }
-    // The ring loads that follow wait for the word's value (branch): keep
-    // the compiler from moving them above the wait.
-    asm volatile("" ::: "memory");
-    return w;
-}
-
 // BIAS: the linear position bias, slopes[hq] * (key - query), enters P's
 // recomputation (added to the raw score as slope / scale * (key - query)).
 template <int D, bool CAUSAL, int DQ, bool BIAS = false>
@@ -236,7 +204,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_split_kernel(
     float *__restrict__ dk, float *__restrict__ dv, int Hq, int Hkv, int N, int BHkv, int KT,
     float scale, float scale_log2, int window, int *__restrict__ sync,
     const float *__restrict__ slopes, int linear_map, float *__restrict__ xring, int pair_slots,
-    int pair_memory)
+    int pair_memory, long long wait_ticks)
 {
     using S = DkdvSplitShape<D>;
     constexpr bool ATOMIC_DQ = DQ != kDqNone;
@@ -492,7 +460,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_split_kernel(
     //  - The consumer waits for that word, loads the partial (after an L1
     //    invalidate, or with device-scope loads), adds it, issues the
     //    atomics for both blocks and raises its consumed count.
-    //  - Both waits are bounded (kTurnTimeout, counted in word kSyncTimeouts;
+    //  - Both waits are bounded (wait_ticks, counted in word kSyncTimeouts;
     //    after one timeout every later wait gives up at once, so the kernel
     //    always finishes).  A timeout leaves dq incomplete, and the count
     //    tells the caller so.  The producer never waits for anything the
@@ -518,7 +486,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_split_kernel(
             if (__builtin_amdgcn_readfirstlane(__hip_atomic_load(
                     sync + kSyncTimeouts, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) != 0)
                 break;
-            if (wall_clock64() - t0 > kTurnTimeout) {
+            if (wall_clock64() - t0 > wait_ticks) {
                 if (lane == 0)
                     __hip_atomic_fetch_add(sync + kSyncTimeouts, 1, __ATOMIC_RELAXED,
                                            __HIP_MEMORY_SCOPE_AGENT);
@@ -635,7 +603,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_split_kernel(
 #pragma unroll
         for (int tt = slice; tt < TILES; tt += 4) {
             const f32x16 c = dq_tile(tt);
-            if (ORDERED && tt == slice) wait_turn(turn_of(st), rank_of(st), sync, lane);
+            if (ORDERED && tt == slice) wait_turn(turn_of(st), rank_of(st), sync, lane, wait_ticks);
             dq_add(dqh, qs, tt, c);
         }
     };
@@ -1147,7 +1115,7 @@ static hipError_t launch_bwd_t(const BwdArgs &a)
                            a.window > 0 ? a.window : kNoWindow,
                            a.mode == kBwdOrdered || pairs ? a.sync : nullptr, a.slopes, a.linear_map,
                            pairs ? a.xring : nullptr, pairs ? a.pair_slots : 0,
-                           pairs ? a.pair_memory : 0);
+                           pairs ? a.pair_memory : 0, a.wait_ticks);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

@@ -44,6 +44,10 @@ inline size_t bwd_sync_words(int BH, int N) { return kSyncHead + (size_t)BH * ((
 // words of its kPairSlots ring slots (4 (e + 1) + path of the exchange e the
 // slot last held) and its consumed count.  The ring itself (not zeroed)
 // holds pairs x kPairSlots x 4 B waves partial tiles of 64 x d / 4 fp32.
+// Longest wait of the ordered and paired modes for another workgroup: 2 s
+// at the 100 MHz wall clock.
+constexpr long long kWaitTicks = 200000000LL;
+
 constexpr int kPairSlots = 4;
 constexpr int kPairWords = 2 + 4 * (kPairSlots + 1);
 inline size_t bwd_key_pairs(int N) { return (size_t)((N + 127) / 128 + 1) / 2; }
@@ -75,6 +79,7 @@ struct BwdArgs {
     float *xring = nullptr;         // paired atomic mode: the partial-tile ring
     int pair_slots = 0;             // kPairSlots in the paired atomic mode, else 0
     int pair_memory = 0;            // 1: paired hand-over through memory even within one XCD
+    long long wait_ticks = kWaitTicks;  // longest inter-workgroup wait (ordered, paired modes)
 };
 
 hipError_t launch_fwd(const FwdArgs &a);

@@ -65,6 +65,12 @@
  *     over through memory (device-scope stores and loads) for every pair,
  *     not only for pairs whose workgroups run on different XCDs: the same
  *     sums, for testing that path and measuring what the L2 path gains.
+ *   - The environment variable FA_WAIT_TICKS, read on every backward call,
+ *     replaces the longest wait of FA_BWD_ORDERED and FA_BWD_ATOMIC_PAIRED
+ *     for another workgroup (2 s) by that many ticks of the 100 MHz wall
+ *     clock (an integer >= 0; 0: a wait whose condition is not met at once
+ *     gives up): for testing the timeout path described at
+ *     fa_bwd_workspace_bytes.
  *   - Supported: d in {64, 128}; B, Hq, Hkv, N >= 1; Hq % Hkv == 0;
  *     scale > 0 and finite; every pointer 16-byte aligned; N need not be a
  *     multiple of any tile size; one head's bf16 rows, N * d * 2 bytes, must

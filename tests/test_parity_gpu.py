@@ -528,6 +528,45 @@ def test_atomic_paired_memory_path(fa, monkeypatch, causal, d):
         compare(name, a, ref[name], MEAN_ABS, max_bar=bars[name])
 
 
+@pytest.mark.parametrize("mode", ["ordered", "paired"])
+def test_bounded_waits_give_up(fa, monkeypatch, mode):
+    """FA_WAIT_TICKS=0: every wait of the ordered or the paired mode whose
+    condition is not met at once gives up, is counted in word 1 of the
+    mode's workspace block, and makes every later wait of the launch give up
+    at once, so the launch finishes.  The count is non-zero; dK and dV, which
+    no wait guards, still meet the oracle's bars; the ordered mode's dQ is
+    still the whole sum (added in an unspecified order) and meets them too;
+    the paired mode's dQ may lack partials (the count marks it invalid) but
+    holds finite values.  B1 Hq4 Hkv2 N4096 d128, causal."""
+    B, Hq, Hkv, N, d, causal = 1, 4, 2, 4096, 128, True
+    m = fa.BWD_ORDERED if mode == "ordered" else fa.BWD_ATOMIC_PAIRED
+    note(f"bounded waits give up: {mode} B={B} Hq={Hq} Hkv={Hkv} N={N} d={d} causal")
+    q, k, v = (random_bf16((B, Hq, N, d), 81), random_bf16((B, Hkv, N, d), 82),
+               random_bf16((B, Hkv, N, d), 83))
+    dout = random_bf16((B, Hq, N, d), 84)
+    scale = 1 / math.sqrt(d)
+    o, lse = gpu_fwd(fa, q, k, v, scale, causal)
+    ref = oracle.bwd(q, k, v, dout, scale, causal)
+    from bf16_floor import backward_bars
+    bars, _ = backward_bars(q, k, v, dout, scale, causal, ref)
+    monkeypatch.setenv("FA_WAIT_TICKS", "0")
+    dq, dk, dv = Guarded((B, Hq, N, d)), Guarded((B, Hkv, N, d)), Guarded((B, Hkv, N, d))
+    need = fa.fa_bwd_workspace_bytes(B, Hq, Hkv, N, d, m)
+    ws = torch.full((need,), 255, dtype=torch.uint8, device="cuda")
+    st = fa.fa_bwd(dev(q), dev(k), dev(v), torch.from_numpy(o).cuda(), torch.from_numpy(lse).cuda(),
+                   dev(dout), dq.t, dk.t, dv.t, B, Hq, Hkv, N, d, scale, causal, m, ws, need)
+    assert st == 0, fa.fa_status_string(st)
+    torch.cuda.synchronize()
+    off = fa.fa_bwd_workspace_bytes(B, Hq, Hkv, N, d, fa.BWD_SEPARATE)
+    gave_up = int(ws[off:off + 8].cpu().numpy().view(np.int32)[1])
+    note(f"  waits given up: {gave_up}")
+    assert gave_up > 0
+    got = {"dq": dq.result("dq"), "dk": dk.result("dk"), "dv": dv.result("dv")}
+    for name in ("dk", "dv") + (("dq",) if mode == "ordered" else ()):
+        compare(name, got[name], ref[name], MEAN_ABS, max_bar=bars[name])
+    assert np.isfinite(got["dq"]).all()
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_ordered_mode_repeats_across_xcds(fa, causal):
     """One key/value head (B1 Hq2 Hkv1 N4096 d128): its 32 key blocks run at
