@@ -237,8 +237,10 @@ int fa_bwd(const void *q, const void *k, const void *v, const float *o, const fl
  * device looks the array's address up (hipGetSymbolAddress).
  *   Limit: fa_bwd_workspace_bytes(B, Hq, Hkv, N, d, deterministic) must not
  *     exceed FA_NOALLOC_MAX_WORKSPACE (about 4 million rows B * Hq * N,
- *     e.g. B = 1, Hq = 32, N = 131072); otherwise FA_ERR_WORKSPACE, before
- *     anything is enqueued.
+ *     e.g. B = 1, Hq = 32, N = 131072; in FA_BWD_ATOMIC_PAIRED the hand-over
+ *     ring, 128 KiB per pair of 128-key blocks at d = 128, counts too, so
+ *     that about 250 such pairs fit, e.g. B = 1, Hkv = 8, N = 4096);
+ *     otherwise FA_ERR_WORKSPACE, before anything is enqueued.
  *   Every call on one device shares that device's array: calls that overlap
  *   in time on one device (different streams, or different host threads
  *   without ordering) race and give wrong results.  Calls ordered on one

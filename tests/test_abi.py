@@ -285,6 +285,12 @@ def test_noalloc_checks_arguments_before_the_device():
     assert fa.fa_bwd_noalloc(**{**base, "dk": MIS}) == 4
     assert fa.fa_bwd_noalloc(**{**base, "deterministic": 4}) == 2
     assert fa.fa_bwd_noalloc(**{**base, "d": 96}) == 3
+    # The paired mode's hand-over ring counts against the limit: B1 Hq8 Hkv8
+    # N8192 d128 fits in the other modes but not in the paired one.
+    small = {**base, "Hq": 8, "Hkv": 8, "N": 8192}
+    assert fa.fa_bwd_workspace_bytes(1, 8, 8, 8192, 128, 0) <= fa.NOALLOC_MAX_WORKSPACE
+    assert fa.fa_bwd_workspace_bytes(1, 8, 8, 8192, 128, 3) > fa.NOALLOC_MAX_WORKSPACE
+    assert fa.fa_bwd_noalloc(**{**small, "deterministic": 3}) == 5
     src = open(os.path.join(ROOT, "include", "fa.h")).read()
     assert "#define FA_NOALLOC_MAX_WORKSPACE ((size_t)32 << 20)" in src
     assert fa.NOALLOC_MAX_WORKSPACE == 32 << 20
