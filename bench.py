@@ -76,8 +76,12 @@ def measured_traffic(kernels, workload):
         return None
     if t.get("workload") != workload or t.get("source_sha256") != source_sha256():
         return None
+    # A backward preprocess is stored under the kernel dispatched after it
+    # (the dQ zeroing of the atomic modes makes its bytes mode-dependent).
+    keys = [f"{k} (before {kernels[i + 1]})" if "bwd_pre_kernel" in k and i + 1 < len(kernels) else k
+            for i, k in enumerate(kernels)]
     try:
-        return sum(t["kernels"][k]["read_bytes"] + t["kernels"][k]["write_bytes"] for k in kernels)
+        return sum(t["kernels"][k]["read_bytes"] + t["kernels"][k]["write_bytes"] for k in keys)
     except KeyError:
         return None
 

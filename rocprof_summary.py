@@ -161,9 +161,35 @@ def source_sha256():
     return bench.source_sha256()
 
 
+def dispatch_rows(d):
+    """{(kernel, counter): [value per dispatch]} like counter_rows, with each
+    backward preprocess dispatch (`bwd_pre_kernel`) named after the kernel
+    dispatched right after it: the preprocess zeroes dQ only ahead of the
+    atomic modes, so its bytes depend on the mode it serves."""
+    rows = []
+    with open(one_csv(d, "_counter_collection.csv")) as f:
+        for r in csv.DictReader(f):
+            if wanted(r["Kernel_Name"]):
+                rows.append((int(r["Dispatch_Id"]), short_name(r["Kernel_Name"]), r["Counter_Name"],
+                             float(r["Counter_Value"])))
+    rows.sort()
+    order = []  # kernel name per dispatch, in dispatch order
+    for disp, k, _, _ in rows:
+        if not order or order[-1][0] != disp:
+            order.append((disp, k))
+    label = {}
+    for i, (disp, k) in enumerate(order):
+        nxt = order[i + 1][1] if i + 1 < len(order) else None
+        label[disp] = f"{k} (before {nxt})" if "bwd_pre_kernel" in k and nxt else k
+    vals = collections.defaultdict(list)
+    for disp, _, c, v in rows:
+        vals[(label[disp], c)].append(v)
+    return vals
+
+
 def cmd_traffic(a):
-    fv, _ = counter_rows(a.fetch_dir)
-    wv, _ = counter_rows(a.write_dir)
+    fv = dispatch_rows(a.fetch_dir)
+    wv = dispatch_rows(a.write_dir)
     f_copy = mean(fv[(COPY_KERNEL, "FETCH_SIZE")])
     w_copy = mean(wv[(COPY_KERNEL, "WRITE_SIZE")])
     ff = COPY_BYTES / (f_copy * 1024.0)

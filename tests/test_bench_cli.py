@@ -72,8 +72,15 @@ def test_roofline_kernels_are_in_the_stored_traffic():
         assert pat in src, pat
     if stored["workload"] != "fwdbwd_causal_n8192":
         pytest.skip("stored counters are for another workload")
-    for name in ("fa::fwd_kernel<128, true, 0, false, false>", "fa::bwd_pre_kernel<128>",
-                 "fa::bwd_dkdv_split_kernel<128, true, 0, false>",
-                 "fa::bwd_dkdv_split_kernel<128, true, 1, false>",
-                 "fa::bwd_dq_kernel<128, true, false, false>"):
+    dkdv0 = "fa::bwd_dkdv_split_kernel<128, true, 0, false>"
+    dkdv1 = "fa::bwd_dkdv_split_kernel<128, true, 1, false>"
+    # The preprocess is stored per mode, under the kernel dispatched after it.
+    for name in ("fa::fwd_kernel<128, true, 0, false, false>", dkdv0, dkdv1,
+                 "fa::bwd_dq_kernel<128, true, false, false>",
+                 f"fa::bwd_pre_kernel<128> (before {dkdv0})",
+                 f"fa::bwd_pre_kernel<128> (before {dkdv1})"):
         assert name in stored["kernels"], name
+    pre_det = stored["kernels"][f"fa::bwd_pre_kernel<128> (before {dkdv0})"]["write_bytes"]
+    pre_atomic = stored["kernels"][f"fa::bwd_pre_kernel<128> (before {dkdv1})"]["write_bytes"]
+    # Only the atomic modes' preprocess zeroes dQ (B2 Hq16 N8192 d128 fp32: 128 MiB).
+    assert pre_atomic - pre_det > 120 * 2**20
